@@ -1,0 +1,195 @@
+/*
+ * pa.h - paged attention on AMD Instinct MI355X (gfx950): C ABI.
+ *
+ * The KV cache is cut into fixed-size physical blocks of 16 or 32 tokens and a
+ * per-sequence block table maps each logical token position to the physical
+ * block that holds it (How vLLM gets real throughput on H100s, "PagedAttention
+ * borrows from operating systems"; vLLM architecture, memory and benchmarks
+ * deep dive, "PagedAttention: a 1960s idea for modern GPUs"). The attention
+ * kernels walk that table at run time and gather K/V from the scattered blocks
+ * (Dissecting vLLM, "PagedAttention: Virtual Memory for KV Cache").
+ *
+ * Layouts (all row-major, contiguous, element type given by pa_dtype_t):
+ *   key_cache, value_cache  [num_blocks, num_kv_heads, block_size, head_dim]
+ *       one (block, head) tile of block_size rows of head_dim elements is
+ *       contiguous; token slot s lives in block s / block_size, row
+ *       s % block_size.
+ *   block_tables            int32 [num_seqs, max_blocks_per_seq]; entry j is
+ *       the physical block of logical tokens j*block_size .. (j+1)*block_size-1.
+ *       Several sequences may name the same physical block (copy-on-write
+ *       sharing of a prompt: How vLLM gets real throughput on H100s,
+ *       "PagedAttention borrows from operating systems").
+ *   context_lens            int32 [num_seqs]; tokens attended, new token
+ *       included (it is written by pa_reshape_and_cache first).
+ *   query                   [num_seqs, num_q_heads, head_dim] (decode) or
+ *                           [total_q, num_q_heads, head_dim] (prefill chunk)
+ *   out                     float32, same leading shape as query.
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads) (grouped-query
+ * attention, as in the pages' example of 4 KV heads of dimension 256).
+ *
+ * Ownership and threading: every pointer argument except `stream` is a device
+ * pointer owned by the caller. The library allocates no device memory, keeps
+ * no pointer after a call returns, and never synchronizes: each call enqueues
+ * its kernels on `stream` (a hipStream_t; NULL means the null stream) and
+ * returns. The caller keeps every buffer alive until the stream has drained.
+ * Calls are reentrant; concurrent calls must not share output or workspace
+ * buffers.
+ *
+ * Errors: a negative count is PA_ERR_SHAPE and a zero count of tokens /
+ * sequences / rows is a successful no-op; both are decided first. The other
+ * host-visible arguments are then checked before any HIP call, in this order,
+ * and the first failure is returned:
+ *   PA_ERR_NULL         a required pointer is NULL
+ *   PA_ERR_SHAPE        a size is negative or zero where it must be positive,
+ *                       or num_q_heads is not a multiple of num_kv_heads
+ *   PA_ERR_UNSUPPORTED  block_size not 16/32, head_dim not 64/128/256, query
+ *                       group size not 1/2/4/8, or a dtype the entry point
+ *                       does not take
+ *   PA_ERR_ALIGN        a tensor or workspace pointer is not 16-byte aligned,
+ *                       or an index array is not aligned to its element size
+ *   PA_ERR_WORKSPACE    the workspace is smaller than the size query returns
+ *   PA_ERR_HIP          a kernel launch failed (hipGetLastError after launch)
+ * Device-resident values (table entries, lengths, slots) are not checked on
+ * the host, since that would need a synchronization. The kernels never read or
+ * write outside the buffers the sizes describe: a table entry outside
+ * [0, num_blocks) makes its tokens contribute nothing, a length above
+ * max_blocks_per_seq * block_size (or above max_context_len) is clamped, and a
+ * slot outside [0, num_blocks * block_size) is skipped; the results for such
+ * rows are then unspecified. Duplicate non-negative slots in one scatter call
+ * leave either token's bits in that slot.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_DTYPE_F32 = 0,   /* IEEE binary32 */
+  PA_DTYPE_BF16 = 1   /* bfloat16: the top 16 bits of a binary32 */
+} pa_dtype_t;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,
+  PA_ERR_SHAPE = 2,
+  PA_ERR_UNSUPPORTED = 3,
+  PA_ERR_ALIGN = 4,
+  PA_ERR_WORKSPACE = 5,
+  PA_ERR_HIP = 6
+} pa_status_t;
+
+/*
+ * Cache-write scatter. Blocks fill as tokens are generated (How vLLM gets real
+ * throughput on H100s, "PagedAttention borrows from operating systems"): for
+ * every token t with s = slot_mapping[t] in [0, num_blocks*block_size),
+ *   key_cache  [s / block_size, h, s % block_size, :] = key  [t, h, :]
+ *   value_cache[s / block_size, h, s % block_size, :] = value[t, h, :]
+ * for all h. A bit copy: no conversion, no rounding. A negative slot skips the
+ * token.
+ *   key, value      [num_tokens, num_kv_heads, head_dim], element type dtype
+ *   slot_mapping    int64 [num_tokens]
+ * dtype: PA_DTYPE_F32 or PA_DTYPE_BF16 (the cache's own type).
+ */
+pa_status_t pa_reshape_and_cache(const void* key, const void* value,
+                                 void* key_cache, void* value_cache,
+                                 const int64_t* slot_mapping,
+                                 int32_t num_tokens, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size,
+                                 int64_t num_blocks, pa_dtype_t dtype,
+                                 void* stream);
+
+/*
+ * Bytes of device workspace pa_decode needs for these sizes (split-context
+ * partial results). Depends only on the arguments; 0 never occurs for
+ * positive sizes. Returns 0 for arguments pa_decode would reject.
+ */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim,
+                                int32_t block_size, int32_t max_context_len);
+
+/*
+ * Decode attention: one new query per sequence over its whole paged context
+ * (decode re-reads the KV cache at every step and is bound by memory
+ * bandwidth: How vLLM gets real throughput on H100s, "Decode is a memory
+ * problem, not a math problem"). For sequence b with n = context_lens[b] and
+ * query head h of KV group g = h / G:
+ *   out[b,h,:] = sum_{j<n} softmax_j(scale * q[b,h,:] . k_j) v_j
+ * where k_j, v_j are KV head g's rows at logical position j, found through
+ * block_tables[b, j / block_size]. n == 0 gives a zero row. Accumulation is
+ * float32; out is float32 and fully overwritten (never read).
+ *   query           [num_seqs, num_q_heads, head_dim], element type dtype
+ *   workspace       device buffer of at least pa_decode_workspace_size(...)
+ *                   bytes (pass NULL only if that size is 0); contents on
+ *                   entry are ignored.
+ *   max_context_len upper bound of context_lens (sizes the launch grid).
+ * dtype: PA_DTYPE_F32 or PA_DTYPE_BF16 for query and both caches.
+ */
+pa_status_t pa_decode(float* out, const void* query,
+                      const void* key_cache, const void* value_cache,
+                      const int32_t* block_tables, const int32_t* context_lens,
+                      int32_t num_seqs, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int32_t max_blocks_per_seq,
+                      int64_t num_blocks, int32_t max_context_len,
+                      float scale, pa_dtype_t dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of device workspace pa_prefill_chunk needs for these sizes; may be 0.
+ */
+size_t pa_prefill_chunk_workspace_size(int32_t num_seqs, int32_t total_q,
+                                       int32_t max_q_len, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t block_size,
+                                       int32_t max_context_len);
+
+/*
+ * Causal chunk of a prompt against the paged cache. Prefill is a dense
+ * matrix product (How vLLM gets real throughput on H100s, "Decode is a memory
+ * problem, not a math problem") and chunked prefill cuts a long prompt into
+ * pieces interleaved with decode tokens (vLLM architecture, memory and
+ * benchmarks deep dive, "Hardware-level optimizations"). Rows
+ * cu_q_lens[b] .. cu_q_lens[b+1]-1 of query are sequence b's chunk of
+ * L = cu_q_lens[b+1] - cu_q_lens[b] rows; its K/V are already in the cache and
+ * n = context_lens[b] counts prefix plus chunk, so row i sits at position
+ * n - L + i and attends keys 0 .. n - L + i:
+ *   out[r,h,:] = sum_{j <= n-L+i} softmax_j(scale * q[r,h,:] . k_j) v_j
+ * QK^T and PV run on the matrix cores in BF16 with float32 accumulation; the
+ * softmax weights are rounded to BF16 before the PV product.
+ *   query      BF16 [total_q, num_q_heads, head_dim]
+ *   cu_q_lens  int32 [num_seqs + 1], device, non-decreasing, cu[0] = 0,
+ *              cu[num_seqs] = total_q; each chunk length <= max_q_len and
+ *              <= its context length.
+ *   workspace  at least pa_prefill_chunk_workspace_size(...) bytes.
+ * dtype: PA_DTYPE_BF16 only.
+ */
+pa_status_t pa_prefill_chunk(float* out, const void* query,
+                             const void* key_cache, const void* value_cache,
+                             const int32_t* block_tables,
+                             const int32_t* context_lens,
+                             const int32_t* cu_q_lens,
+                             int32_t num_seqs, int32_t total_q,
+                             int32_t max_q_len, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, int32_t max_blocks_per_seq,
+                             int64_t num_blocks, int32_t max_context_len,
+                             float scale, pa_dtype_t dtype,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* pa_status_string(pa_status_t status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,29 @@
+"""Paged attention for AMD Instinct MI355X (gfx950).
+
+A KV cache cut into fixed-size physical blocks of 16 or 32 tokens, mapped per
+sequence by a block table, with three operations implemented as hand-written
+HIP kernels behind the C ABI in ``include/pa.h``:
+
+* ``pa_reshape_and_cache`` - scatter new K/V rows into their block slots;
+* ``pa_decode``            - one-query-per-sequence attention (GQA) over the
+                             paged context, split over the context with a
+                             separate merge kernel;
+* ``pa_prefill_chunk``     - a causal query chunk against the paged cache on
+                             the matrix cores.
+
+The Python functions below only marshal torch tensors to that ABI.
+"""
+
+from ._lib import (  # noqa: F401
+    LIB_PATH,
+    PA_DTYPE_BF16,
+    PA_DTYPE_F32,
+    SIGNATURES,
+    PaError,
+    lib,
+    pa_decode,
+    pa_decode_workspace_size,
+    pa_prefill_chunk,
+    pa_prefill_chunk_workspace_size,
+    pa_reshape_and_cache,
+)

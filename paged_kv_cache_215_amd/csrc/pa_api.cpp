@@ -1,0 +1,256 @@
+// C ABI of the paged-attention library: argument validation (before any HIP
+// call), launch geometry, workspace carving. Declarations and the contract of
+// every entry point are in include/pa.h.
+
+#include "pa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+
+#include "pa_internal.hpp"
+
+namespace pa {
+
+int decode_target_workgroups() {
+  // Workgroups the decode launch aims for (a few times the CU count). The
+  // environment override exists for tuning sweeps only.
+  static const int target = [] {
+    const char* s = std::getenv("PA_DECODE_TARGET_WGS");
+    const int v = s ? std::atoi(s) : 0;
+    return v > 0 ? v : 1024;
+  }();
+  return target;
+}
+
+}  // namespace pa
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool supported_block(int32_t bs) { return bs == 16 || bs == 32; }
+bool supported_dim(int32_t d) { return d == 64 || d == 128 || d == 256; }
+bool supported_group(int32_t hq, int32_t hkv) {
+  const int32_t g = hq / hkv;
+  return g == 1 || g == 2 || g == 4 || g == 8;
+}
+int log2_exact(int32_t v) {
+  int r = 0;
+  while ((1 << r) < v) ++r;
+  return r;
+}
+int elem_bytes(pa_dtype_t t) { return t == PA_DTYPE_BF16 ? 2 : 4; }
+
+int32_t ctx_limit(int32_t max_ctx, int32_t max_blocks, int32_t bs) {
+  const int64_t cap = (int64_t)max_blocks * bs;
+  return (int32_t)(cap < max_ctx ? cap : max_ctx);
+}
+
+struct DecodeGeometry {
+  int part_tokens;
+  int max_parts;
+  size_t part_o_bytes;
+  size_t bytes;
+};
+
+DecodeGeometry decode_geometry(int32_t num_seqs, int32_t hq, int32_t hkv, int32_t d, int32_t bs,
+                               int32_t max_ctx) {
+  DecodeGeometry g;
+  g.part_tokens = pa::decode_part_tokens(num_seqs, hkv, bs, max_ctx);
+  g.max_parts = (max_ctx + g.part_tokens - 1) / g.part_tokens;
+  const size_t rows = (size_t)num_seqs * hq * (g.max_parts > 0 ? g.max_parts : 1);
+  g.part_o_bytes = rows * d * sizeof(float);
+  g.bytes = g.part_o_bytes + rows * 2 * sizeof(float);
+  return g;
+}
+
+pa_status_t from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+pa_status_t pa_reshape_and_cache(const void* key, const void* value, void* key_cache,
+                                 void* value_cache, const int64_t* slot_mapping,
+                                 int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int64_t num_blocks, pa_dtype_t dtype,
+                                 void* stream) {
+  if (num_tokens < 0) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping) return PA_ERR_NULL;
+  if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return PA_ERR_SHAPE;
+  if (!supported_block(block_size) || !supported_dim(head_dim) ||
+      (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16))
+    return PA_ERR_UNSUPPORTED;
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(key_cache, 16) ||
+      !aligned(value_cache, 16) || !aligned(slot_mapping, 8))
+    return PA_ERR_ALIGN;
+  pa::ScatterArgs a;
+  a.key = key;
+  a.value = value;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.slot_mapping = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.num_kv_heads = num_kv_heads;
+  a.row_chunks = head_dim * elem_bytes(dtype) / 16;
+  a.block_size = block_size;
+  a.num_slots = num_blocks * block_size;
+  return from_hip(pa::launch_scatter(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t max_context_len) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0 ||
+      num_q_heads % num_kv_heads || !supported_block(block_size) || !supported_dim(head_dim) ||
+      !supported_group(num_q_heads, num_kv_heads))
+    return 0;
+  return decode_geometry(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                         max_context_len)
+      .bytes;
+}
+
+pa_status_t pa_decode(float* out, const void* query, const void* key_cache,
+                      const void* value_cache, const int32_t* block_tables,
+                      const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                      int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len,
+                      float scale, pa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (num_seqs < 0) return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens ||
+      !workspace)
+    return PA_ERR_NULL;
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      max_blocks_per_seq <= 0 || num_blocks <= 0 || max_context_len < 0 ||
+      num_q_heads % num_kv_heads != 0 || !std::isfinite(scale))
+    return PA_ERR_SHAPE;
+  if (!supported_block(block_size) || !supported_dim(head_dim) ||
+      !supported_group(num_q_heads, num_kv_heads) ||
+      (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16))
+    return PA_ERR_UNSUPPORTED;
+  if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) ||
+      !aligned(value_cache, 16) || !aligned(workspace, 16) || !aligned(block_tables, 4) ||
+      !aligned(context_lens, 4))
+    return PA_ERR_ALIGN;
+  const DecodeGeometry geo = decode_geometry(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                             block_size, max_context_len);
+  if (workspace_bytes < geo.bytes) return PA_ERR_WORKSPACE;
+
+  pa::DecodeArgs a;
+  a.out = out;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + geo.part_o_bytes);
+  a.query = query;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size_log2 = log2_exact(block_size);
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.ctx_limit = ctx_limit(max_context_len, max_blocks_per_seq, block_size);
+  a.part_tokens = geo.part_tokens;
+  a.max_parts = geo.max_parts;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return from_hip(pa::launch_decode(a, dtype == PA_DTYPE_BF16, static_cast<hipStream_t>(stream)));
+}
+
+size_t pa_prefill_chunk_workspace_size(int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                                       int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t block_size,
+                                       int32_t max_context_len) {
+  if (num_seqs <= 0 || total_q <= 0 || max_q_len <= 0 || num_q_heads <= 0 ||
+      num_kv_heads <= 0 || num_q_heads % num_kv_heads || max_context_len < 0 ||
+      !supported_block(block_size) || !supported_dim(head_dim) ||
+      !supported_group(num_q_heads, num_kv_heads))
+    return 0;
+  const int splits = pa::prefill_kv_splits(num_seqs, max_q_len, num_kv_heads, max_context_len);
+  if (splits <= 1) return 0;
+  const size_t rows = (size_t)total_q * num_q_heads * splits;
+  return rows * head_dim * sizeof(float) + rows * 2 * sizeof(float);
+}
+
+pa_status_t pa_prefill_chunk(float* out, const void* query, const void* key_cache,
+                             const void* value_cache, const int32_t* block_tables,
+                             const int32_t* context_lens, const int32_t* cu_q_lens,
+                             int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, int32_t max_blocks_per_seq,
+                             int64_t num_blocks, int32_t max_context_len, float scale,
+                             pa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (num_seqs < 0 || total_q < 0) return PA_ERR_SHAPE;
+  if (num_seqs == 0 || total_q == 0) return PA_OK;
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens ||
+      !cu_q_lens)
+    return PA_ERR_NULL;
+  if (max_q_len <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || max_context_len < 0 ||
+      num_q_heads % num_kv_heads != 0 || !std::isfinite(scale))
+    return PA_ERR_SHAPE;
+  if (!supported_block(block_size) || !supported_dim(head_dim) ||
+      !supported_group(num_q_heads, num_kv_heads) || dtype != PA_DTYPE_BF16)
+    return PA_ERR_UNSUPPORTED;
+  if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) ||
+      !aligned(value_cache, 16) || !aligned(block_tables, 4) || !aligned(context_lens, 4) ||
+      !aligned(cu_q_lens, 4) || (workspace && !aligned(workspace, 16)))
+    return PA_ERR_ALIGN;
+  const size_t need = pa_prefill_chunk_workspace_size(num_seqs, total_q, max_q_len, num_q_heads,
+                                                      num_kv_heads, head_dim, block_size,
+                                                      max_context_len);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+
+  pa::PrefillArgs a;
+  a.out = out;
+  a.kv_splits = pa::prefill_kv_splits(num_seqs, max_q_len, num_kv_heads, max_context_len);
+  if (a.kv_splits < 1) a.kv_splits = 1;
+  const size_t rows = (size_t)total_q * num_q_heads * a.kv_splits;
+  a.part_o = need ? static_cast<float*>(workspace) : nullptr;
+  a.part_ml = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                              rows * head_dim * sizeof(float))
+                   : nullptr;
+  a.query = query;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.cu_q_lens = cu_q_lens;
+  a.num_seqs = num_seqs;
+  a.total_q = total_q;
+  a.max_q_len = max_q_len;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size_log2 = log2_exact(block_size);
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.ctx_limit = ctx_limit(max_context_len, max_blocks_per_seq, block_size);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return from_hip(pa::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+const char* pa_status_string(pa_status_t status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "a required pointer is NULL";
+    case PA_ERR_SHAPE: return "invalid size or shape";
+    case PA_ERR_UNSUPPORTED: return "unsupported block size, head dim, group size or dtype";
+    case PA_ERR_ALIGN: return "misaligned pointer (tensors need 16 bytes, index arrays their element size)";
+    case PA_ERR_WORKSPACE: return "workspace too small";
+    case PA_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t pa_version(void) { return 100; }
+
+}  // extern "C"

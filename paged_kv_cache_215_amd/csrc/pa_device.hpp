@@ -1,0 +1,107 @@
+// Device-side helpers shared by the paged-attention kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kWave = 64;
+
+// Element-type tags. The cache stores either binary32 or bfloat16 (the top
+// half of a binary32); both move through 16-byte vectors.
+struct F32 {
+  static constexpr int kBytes = 4;
+};
+struct BF16 {
+  static constexpr int kBytes = 2;
+};
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Widen the low / high bfloat16 of a packed pair: a bfloat16 is the high half
+// of the binary32 with the same value, so widening is a shift or a mask.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// a.lo*b.lo + a.hi*b.hi + c on packed bfloat16 pairs (v_dot2_f32_bf16): the
+// products of two bfloat16 are exact in binary32 and the sum accumulates in
+// binary32.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Dot product of one 16-byte chunk of K with the matching chunk of q.
+__device__ __forceinline__ float dot_chunk(BF16, const uint4& k, const uint4& q, float c) {
+  c = dot2_bf16(k.x, q.x, c);
+  c = dot2_bf16(k.y, q.y, c);
+  c = dot2_bf16(k.z, q.z, c);
+  c = dot2_bf16(k.w, q.w, c);
+  return c;
+}
+__device__ __forceinline__ float dot_chunk(F32, const uint4& k, const uint4& q, float c) {
+  c = __builtin_fmaf(__uint_as_float(k.x), __uint_as_float(q.x), c);
+  c = __builtin_fmaf(__uint_as_float(k.y), __uint_as_float(q.y), c);
+  c = __builtin_fmaf(__uint_as_float(k.z), __uint_as_float(q.z), c);
+  c = __builtin_fmaf(__uint_as_float(k.w), __uint_as_float(q.w), c);
+  return c;
+}
+
+// Widen one 16-byte chunk to binary32 (8 bfloat16 or 4 binary32 values).
+__device__ __forceinline__ void widen_chunk(BF16, const uint4& v, float* out) {
+  out[0] = bf16_lo(v.x); out[1] = bf16_hi(v.x);
+  out[2] = bf16_lo(v.y); out[3] = bf16_hi(v.y);
+  out[4] = bf16_lo(v.z); out[5] = bf16_hi(v.z);
+  out[6] = bf16_lo(v.w); out[7] = bf16_hi(v.w);
+}
+__device__ __forceinline__ void widen_chunk(F32, const uint4& v, float* out) {
+  out[0] = __uint_as_float(v.x); out[1] = __uint_as_float(v.y);
+  out[2] = __uint_as_float(v.z); out[3] = __uint_as_float(v.w);
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane exchange. xor_lane<M>(x) returns x from lane (lane ^ M).
+//   M = 1, 2 : DPP quad permutation (VALU, no LDS traffic)
+//   M = 8    : DPP row rotate by 8 within a 16-lane row, which is lane ^ 8
+//   M = 4, 16: ds_swizzle in xor mode (within 32 lanes)
+//   M = 32   : ds_bpermute
+template <int M>
+__device__ __forceinline__ float xor_lane(float x) {
+  static_assert(M == 1 || M == 2 || M == 4 || M == 8 || M == 16 || M == 32, "mask");
+  int v = __float_as_int(x);
+  if constexpr (M == 1) {
+    v = __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  } else if constexpr (M == 2) {
+    v = __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  } else if constexpr (M == 8) {
+    v = __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);  // row_ror:8
+  } else if constexpr (M == 4 || M == 16) {
+    v = __builtin_amdgcn_ds_swizzle(v, 0x1F | (M << 10));           // and 0x1F, xor M
+  } else {
+    v = __builtin_amdgcn_ds_bpermute((int)((__lane_id() ^ 32u) << 2), v);
+  }
+  return __int_as_float(v);
+}
+
+// Partner for the transposing reduction at lane bit log2(M): any involution
+// that flips bit log2(M) and keeps every higher bit works there, because the
+// lower bits are resolved afterwards. Bit 2 uses the DPP half-row mirror
+// (lane ^ 7), which stays on the VALU.
+template <int M>
+__device__ __forceinline__ float reduce_partner(float x) {
+  if constexpr (M == 4) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
+  } else {
+    return xor_lane<M>(x);
+  }
+}
+
+__device__ __forceinline__ float readlane_f(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace pa

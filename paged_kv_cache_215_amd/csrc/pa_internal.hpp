@@ -1,0 +1,76 @@
+// Host-side interfaces between the C ABI (pa_api.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct DecodeArgs {
+  float* out;            // [S, Hq, D] float32
+  float* part_o;         // [S, Hq, max_parts, D] normalised partial outputs
+  float* part_ml;        // [S, Hq, max_parts, 2] (max in log2 units, sum)
+  const void* query;     // [S, Hq, D]
+  const void* key_cache;    // [num_blocks, Hkv, bs, D]
+  const void* value_cache;
+  const int32_t* block_tables;  // [S, max_blocks_per_seq]
+  const int32_t* context_lens;  // [S]
+  int num_seqs;
+  int num_q_heads;
+  int num_kv_heads;
+  int head_dim;
+  int block_size_log2;
+  int max_blocks_per_seq;
+  int64_t num_blocks;
+  int ctx_limit;         // min(max_context_len, max_blocks_per_seq * block_size)
+  int part_tokens;       // tokens per context partition (multiple of 64)
+  int max_parts;         // ceil(max_context_len / part_tokens)
+  float scale_log2;      // softmax scale * log2(e)
+};
+
+struct ScatterArgs {
+  const void* key;       // [T, Hkv, D]
+  const void* value;
+  void* key_cache;       // [num_blocks, Hkv, bs, D]
+  void* value_cache;
+  const int64_t* slot_mapping;  // [T]
+  int num_tokens;
+  int num_kv_heads;
+  int row_chunks;        // D * elem_bytes / 16
+  int block_size;
+  int64_t num_slots;     // num_blocks * block_size
+};
+
+struct PrefillArgs {
+  float* out;            // [total_q, Hq, D] float32
+  float* part_o;         // split-context partials (may be unused)
+  float* part_ml;
+  const void* query;     // BF16 [total_q, Hq, D]
+  const void* key_cache;
+  const void* value_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* cu_q_lens;     // [S + 1]
+  int num_seqs;
+  int total_q;
+  int max_q_len;
+  int num_q_heads;
+  int num_kv_heads;
+  int head_dim;
+  int block_size_log2;
+  int max_blocks_per_seq;
+  int64_t num_blocks;
+  int ctx_limit;
+  int kv_splits;         // context splits per row tile (1 = no partials)
+  float scale_log2;
+};
+
+int decode_target_workgroups();
+int decode_part_tokens(int num_seqs, int num_kv_heads, int block_size, int max_context_len);
+hipError_t launch_decode(const DecodeArgs& a, bool bf16, hipStream_t stream);
+hipError_t launch_scatter(const ScatterArgs& a, hipStream_t stream);
+
+int prefill_kv_splits(int num_seqs, int max_q_len, int num_kv_heads, int max_context_len);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+}  // namespace pa
