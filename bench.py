@@ -1,0 +1,312 @@
+"""Benchmark: paged-attention decode on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline] [--profile]
+
+A step is one pass of the hot path over one batch: for the full decode step
+(the default workload, 64 sequences at context 8192, 16 layers, 4 KV / 16
+query heads, head dim 256, block size 32, BF16) every layer runs
+pa_reshape_and_cache for the new token and then pa_decode over the whole
+paged context. Inputs are synthetic (seeded N(0,1), BF16) and resident in HBM
+before the timed region. Prints ONE JSON line.
+
+Roofline: the dominant call is pa_decode (its partition kernel plus the small
+merge kernel). Its algorithmic bytes per call are the K/V rows of every
+attended token, the query, the float32 output and the block-table entries in
+use; the live duration comes from HIP events recorded on the launch stream
+around every pa_decode call of the timed steps.
+
+cpu_baseline: the fp64 CPU oracle, as it stands, on a bounded sample of the
+same workload (one layer's sequences), in worker processes on the host cores.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+DECODE_SOURCES = ["paged_kv_cache_215_amd/csrc/pa_decode.hip",
+                  "paged_kv_cache_215_amd/csrc/pa_device.hpp"]
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_c3_hbm_counters.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def decode_bytes(layout, num_decode, num_q_heads, num_kv_heads, head_dim, elem_bytes,
+                 unique_blocks=False):
+    """Algorithmic bytes of one pa_decode call: K+V rows of every attended
+    token (each distinct physical block once when unique_blocks), q, float32
+    out and the block-table entries in use."""
+    lens = layout.context_lens[:num_decode].astype(np.int64)
+    bs = layout.block_size
+    nblk = -(-lens // bs)
+    if unique_blocks:
+        seen = {}
+        for b in range(num_decode):
+            n = int(lens[b])
+            for j in range(int(nblk[b])):
+                blk = int(layout.block_tables[b, j])
+                rows = min(bs, n - j * bs)
+                seen[blk] = max(seen.get(blk, 0), rows)
+        kv_tokens = sum(seen.values())
+    else:
+        kv_tokens = int(lens.sum())
+    kv = 2 * kv_tokens * num_kv_heads * head_dim * elem_bytes
+    q = num_decode * num_q_heads * head_dim * elem_bytes
+    out = num_decode * num_q_heads * head_dim * 4
+    bt = int(nblk.sum()) * 4
+    return kv + q + out + bt
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(bytes_per_call):
+    """HBM traffic per pa_decode call from the committed rocprofv3 counter
+    summary, only if it was taken on the current decode kernel source."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("source_hash") != source_hash(DECODE_SOURCES):
+        return None
+    return c.get("hbm_bytes_per_call")
+
+
+# ---------------------------------------------------------------- CPU leg ---
+
+_ARR = {}
+
+
+def _cpu_worker_init(folder):
+    _ARR["folder"] = folder
+
+
+def _cpu_arr(name):
+    if name not in _ARR:
+        _ARR[name] = np.load(os.path.join(_ARR["folder"], name + ".npy"), mmap_mode="r")
+    return _ARR[name]
+
+
+def _cpu_worker(args):
+    layer, b, scale = args
+    import oracle  # the oracle is used here only, to time it
+    q = _cpu_arr(f"q{layer}")
+    kc = _cpu_arr(f"kc{layer}")
+    vc = _cpu_arr(f"vc{layer}")
+    bt = _cpu_arr("bt")
+    lens = _cpu_arr("lens")
+    return oracle.decode_ref(q[b:b + 1], kc, vc, bt[b:b + 1], lens[b:b + 1], scale)
+
+
+def cpu_baseline(case, layers, seq_layers_per_step):
+    """Time the oracle on every sequence of the given layers; scale to the
+    seconds of a full step (seq_layers_per_step sequence-layers)."""
+    import shutil
+    import tempfile
+    from multiprocessing import get_context
+    from workloads import to_numpy_bits
+
+    S = case.num_decode_seqs
+    folder = tempfile.mkdtemp(prefix="pa_cpu_baseline_")
+    try:
+        np.save(os.path.join(folder, "bt.npy"), case.layout.block_tables[:S])
+        np.save(os.path.join(folder, "lens.npy"), case.layout.context_lens[:S].astype(np.int64))
+        for layer in layers:
+            np.save(os.path.join(folder, f"q{layer}.npy"), to_numpy_bits(case.queries[layer]))
+            np.save(os.path.join(folder, f"kc{layer}.npy"), to_numpy_bits(case.key_caches[layer]))
+            np.save(os.path.join(folder, f"vc{layer}.npy"), to_numpy_bits(case.value_caches[layer]))
+        try:
+            cores = len(os.sched_getaffinity(0))
+        except AttributeError:
+            cores = os.cpu_count() or 1
+        workers = max(1, min(16, cores))
+        saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
+                                                "MKL_NUM_THREADS")}
+        for k in saved:
+            os.environ[k] = "1"
+        try:
+            ctx = get_context("spawn")
+            with ctx.Pool(workers, initializer=_cpu_worker_init, initargs=(folder,)) as pool:
+                # warm every worker (imports, page cache) outside the timed region
+                pool.map(_cpu_worker, [(layers[0], b % S, case.scale) for b in range(workers)],
+                         chunksize=1)
+                tasks = [(layer, b, case.scale) for layer in layers for b in range(S)]
+                t0 = time.perf_counter()
+                pool.map(_cpu_worker, tasks, chunksize=1)
+                wall = time.perf_counter() - t0
+        finally:
+            for k, v in saved.items():
+                if v is None:
+                    os.environ.pop(k, None)
+                else:
+                    os.environ[k] = v
+    finally:
+        shutil.rmtree(folder, ignore_errors=True)
+    n_tasks = len(layers) * S
+    return {"wall_s": wall, "workers": workers, "tasks": n_tasks,
+            "step_seconds": wall * seq_layers_per_step / n_tasks}
+
+
+# ---------------------------------------------------------------- GPU leg ---
+
+def run(args):
+    import torch
+    import paged_kv_cache_215_amd as pa
+    from workloads import make_config_case
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU (MI355X); none is visible")
+    pa.lib()                                   # fail loudly if the library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] generating {args.workload} ...")
+    case = make_config_case(args.workload, device=dev)
+    torch.cuda.synchronize()
+    L = case.num_layers
+    S = case.num_decode_seqs
+    elem = 2 if case.dtype == torch.bfloat16 else 4
+    outs = [torch.empty((S, case.num_q_heads, case.head_dim), dtype=torch.float32, device=dev)
+            for _ in range(L)]
+    ws_bytes = pa.pa_decode_workspace_size(S, case.num_q_heads, case.num_kv_heads, case.head_dim,
+                                           case.block_size, case.max_context_len)
+    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(events=None):
+        for layer in range(L):
+            if case.slot_mapping is not None:
+                pa.pa_reshape_and_cache(case.new_keys[layer], case.new_values[layer],
+                                        case.key_caches[layer], case.value_caches[layer],
+                                        case.slot_mapping)
+            if events is not None:
+                events.append(torch.cuda.Event(enable_timing=True))
+                events[-1].record(stream)
+            pa.pa_decode(case.queries[layer], case.key_caches[layer], case.value_caches[layer],
+                         case.block_tables, case.context_lens, case.scale, case.max_context_len,
+                         out=outs[layer], workspace=workspace)
+            if events is not None:
+                events.append(torch.cuda.Event(enable_timing=True))
+                events[-1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(events)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    decode_ms = [events[i].elapsed_time(events[i + 1]) for i in range(0, len(events), 2)]
+    avg_decode_s = float(np.mean(decode_ms)) / 1e3
+
+    unique = args.workload == "c4_grpo_cow"
+    bytes_call = decode_bytes(case.layout, S, case.num_q_heads, case.num_kv_heads, case.head_dim,
+                              elem, unique_blocks=unique)
+    achieved_gbs = bytes_call / avg_decode_s / 1e9
+    ms_per_step = elapsed / args.steps * 1e3
+    tokens_per_s = S * args.steps / elapsed
+    log(f"[bench] {args.steps} steps in {elapsed * 1e3:.2f} ms: {ms_per_step:.3f} ms/step, "
+        f"{tokens_per_s:.1f} tok/s; pa_decode avg {avg_decode_s * 1e6:.1f} us "
+        f"(min {min(decode_ms) * 1e3:.1f}, max {max(decode_ms) * 1e3:.1f}), "
+        f"{achieved_gbs:.1f} GB/s = {achieved_gbs / HBM_PEAK_GBS:.3f} of HBM peak")
+    traffic = load_traffic(bytes_call)
+
+    result = {
+        "metric": "paged-attn decode tokens/s & achieved HBM GB/s (% of 8 TB/s), 1 MI355X",
+        "value": round(tokens_per_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if elem == 2 else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "num_seqs": S,
+            "context_len": int(case.max_context_len),
+            "layers": L,
+            "num_q_heads": case.num_q_heads,
+            "num_kv_heads": case.num_kv_heads,
+            "head_dim": case.head_dim,
+            "block_size": case.block_size,
+            "step": "per layer: pa_reshape_and_cache(new token) + pa_decode",
+        },
+        "roofline": {
+            "kernel": "pa_decode (decode_partition_kernel + decode_merge_kernel)",
+            "bound": "hbm",
+            "achieved": round(achieved_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_call": bytes_call,
+            "avg_call_us": round(avg_decode_s * 1e6, 2),
+        },
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        layers = list(range(min(L, args.cpu_sample_layers)))
+        log(f"[bench] cpu baseline: oracle on {S} sequences x layers {layers} ...")
+        cb = cpu_baseline(case, layers, S * L)
+        result["cpu_baseline"] = {
+            "value": round(S / cb["step_seconds"], 4),
+            "unit": "tokens/s",
+            "cores": cb["workers"],
+            "kind": "oracle",
+            "sample": f"fp64 oracle decode_ref on all {S} sequences of {len(layers)} of the {L} "
+                      f"layers ({cb['tasks']} of {S * L} sequence-layers per step; "
+                      f"{cb['wall_s']:.2f} s wall on {cb['workers']} worker processes), "
+                      f"scaled to a full step",
+        }
+        log(f"[bench] cpu baseline {cb['wall_s']:.2f} s for {cb['tasks']} seq-layers on "
+            f"{cb['workers']} workers")
+    print(json.dumps(result), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c3_full_step",
+                    choices=["c2_layer_decode", "c3_full_step", "c4_grpo_cow", "c5_mixed_step"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-layers", type=int, default=2)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+    if "RANK" in os.environ and os.environ.get("WORLD_SIZE", "1") != "1":
+        print("bench.py runs on one GPU only (WORLD_SIZE > 1 given)", file=sys.stderr)
+        sys.exit(2)
+    run(args)
+
+
+if __name__ == "__main__":
+    main()

@@ -43,9 +43,9 @@ constexpr int kThreads = kWaves * kWave;
 
 constexpr int choose_k_lanes(int row_chunks, int group) {
   // Enough lanes per K row that the q chunks held per lane (group * KCH
-  // 16-byte chunks) fit in 64 VGPRs, at least 4 so that a tile holds whole
+  // 16-byte chunks) fit in 32 VGPRs, at least 4 so that a tile holds whole
   // load groups.
-  int need = group * row_chunks / 16;
+  int need = group * row_chunks / 8;
   if (need < 4) need = 4;
   int kl = 4;
   while (kl < need) kl *= 2;
@@ -136,22 +136,25 @@ __device__ __forceinline__ float reduce_neutral(float x) {
   return x;
 }
 
-template <typename Shape, typename T>
-__device__ __forceinline__ void load_tile(const uint4* __restrict__ kbase,
-                                          const uint4* __restrict__ vbase, int lane,
-                                          uint4 (&kb)[Shape::NGK][Shape::KCH],
-                                          uint4 (&vb)[Shape::NGV]) {
-  constexpr int RC = Shape::RC, KL = Shape::KL, RK = Shape::RK, VL = Shape::VL,
-                RV = Shape::RV;
+template <typename Shape>
+__device__ __forceinline__ void load_k(const uint4* __restrict__ kbase, int lane,
+                                       uint4 (&kb)[Shape::NGK][Shape::KCH]) {
+  constexpr int RC = Shape::RC, KL = Shape::KL, RK = Shape::RK;
   const int krow = lane / KL, kc = lane % KL;
 #pragma unroll
   for (int gk = 0; gk < Shape::NGK; ++gk)
 #pragma unroll
     for (int i = 0; i < Shape::KCH; ++i)
-      kb[gk][i] = kbase[(gk * RK + krow) * RC + kc + KL * i];
+      kb[gk][i] = load_stream(kbase + (gk * RK + krow) * RC + kc + KL * i);
+}
+
+template <typename Shape>
+__device__ __forceinline__ void load_v(const uint4* __restrict__ vbase, int lane,
+                                       uint4 (&vb)[Shape::NGV]) {
+  constexpr int RC = Shape::RC, VL = Shape::VL, RV = Shape::RV;
   const int vrow = lane / VL, vc = lane % VL;
 #pragma unroll
-  for (int gv = 0; gv < Shape::NGV; ++gv) vb[gv] = vbase[(gv * RV + vrow) * RC + vc];
+  for (int gv = 0; gv < Shape::NGV; ++gv) vb[gv] = load_stream(vbase + (gv * RV + vrow) * RC + vc);
 }
 
 template <typename T, int D, int G>
@@ -222,15 +225,28 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
   const int ntiles = (end - start + kTile - 1) / kTile;
   float* p_lds = s_p[wave];
 
+  // Offset of tile t's (block, head) rows, or -1 for an invalid table entry.
+  auto tile_offset = [&](int t) -> int64_t {
+    const int blk = __builtin_amdgcn_readlane(my_block, (t * kTile) >> bs_log2);
+    if (blk < 0) return -1;
+    return (int64_t)blk * block_stride + head_off + (int64_t)((start + t * kTile) & (bs - 1)) * RC;
+  };
+
+  // Software pipeline over this wave's tiles t = wave, wave + 4, ...: the K
+  // registers are refilled for the next tile as soon as the scores are done,
+  // the V registers as soon as the PV update is done, so one tile's loads are
+  // always in flight behind the current tile's arithmetic.
+  uint4 kb[NGK][KCH];
+  uint4 vb[NGV];
+  int64_t off = wave < ntiles ? tile_offset(wave) : -1;
+  if (off >= 0) {
+    load_k<S>(kcache + off, lane, kb);
+    load_v<S>(vcache + off, lane, vb);
+  }
   for (int t = wave; t < ntiles; t += kWaves) {
     const int tok0 = start + t * kTile;
-    const int blk = __builtin_amdgcn_readlane(my_block, (t * kTile) >> bs_log2);
-    if (blk < 0) continue;  // invalid table entry: these tokens contribute nothing
-    const int64_t tile_off = (int64_t)blk * block_stride + head_off +
-                             (int64_t)(tok0 & (bs - 1)) * RC;
-    uint4 kb[NGK][KCH];
-    uint4 vb[NGV];
-    load_tile<S, T>(kcache + tile_off, vcache + tile_off, lane, kb, vb);
+    const bool valid = off >= 0;  // invalid table entry: these tokens contribute nothing
+    const int64_t next_off = t + kWaves < ntiles ? tile_offset(t + kWaves) : -1;
 
     // ---- scores: partial dots, then transposing reduction over KL lanes
     float sc[NV];
@@ -243,6 +259,12 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
         for (int i = 0; i < KCH; ++i) c = dot_chunk(T{}, kb[gk][i], q[g][i], c);
         sc[gk * G + g] = c;
       }
+    if (next_off >= 0) load_k<S>(kcache + next_off, lane, kb);
+    if (!valid) {
+      off = next_off;
+      if (off >= 0) load_v<S>(vcache + off, lane, vb);
+      continue;
+    }
     transpose_reduce<NV, KL / 2>(sc);
 
     const bool partial_tile = tok0 + kTile > n;
@@ -324,6 +346,8 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[g][e] = __builtin_fmaf(pw[g], v[e], acc[g][e]);
     }
+    off = next_off;
+    if (off >= 0) load_v<S>(vcache + off, lane, vb);
     __builtin_amdgcn_wave_barrier();
   }
 

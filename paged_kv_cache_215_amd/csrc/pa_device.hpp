@@ -18,6 +18,15 @@ struct BF16 {
 };
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte load marked nontemporal (global_load_dwordx4 ... nt): for data read
+// exactly once per launch, such as the K/V rows of a decode step, so that the
+// stream does not displace reusable lines in L2 and the Infinity Cache.
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // Widen the low / high bfloat16 of a packed pair: a bfloat16 is the high half
 // of the binary32 with the same value, so widening is a shift or a mask.

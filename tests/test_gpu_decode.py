@@ -128,7 +128,7 @@ def test_copy_on_write_shared_vs_private_bit_identical():
     # copies of those blocks: identical outputs.
     case = make_case(name="cow", seed=12, context_lens=[512 + 40, 512 + 300], num_q_heads=16,
                      num_kv_heads=4, head_dim=256, block_size=16, device=DEV,
-                     shared_prefix=(2, 512))
+                     shared_prefix=(2, 512), pool_slack=1.0)
     shared = gpu_decode(case)
     bt = case.block_tables.clone()
     kc = case.key_caches[0].clone()
