@@ -35,6 +35,8 @@
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
 
+#include <type_traits>
+
 namespace pa {
 
 constexpr int kTile = 16;
@@ -180,7 +182,8 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
   const int nparts = (n + a.part_tokens - 1) / a.part_tokens;
 
   const int tid = threadIdx.x;
-  const int wave = tid / kWave;
+  // wave index as a scalar, so that all tile bookkeeping below is uniform
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
 
   // q of the G heads of this KV group, in the K-lane layout.
@@ -225,28 +228,29 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
   const int ntiles = (end - start + kTile - 1) / kTile;
   float* p_lds = s_p[wave];
 
-  // Offset of tile t's (block, head) rows, or -1 for an invalid table entry.
-  auto tile_offset = [&](int t) -> int64_t {
-    const int blk = __builtin_amdgcn_readlane(my_block, (t * kTile) >> bs_log2);
-    if (blk < 0) return -1;
-    return (int64_t)blk * block_stride + head_off + (int64_t)((start + t * kTile) & (bs - 1)) * RC;
+  // Physical block of tile t (a scalar read of the table entry held by lane
+  // t*16/bs); an entry outside the pool reads block 0 and the tile is masked.
+  auto tile_block = [&](int t) -> int {
+    return __builtin_amdgcn_readlane(my_block, (t * kTile) >> bs_log2);
+  };
+  auto tile_offset = [&](int t, int blk) -> int64_t {
+    return (int64_t)(blk < 0 ? 0 : blk) * block_stride + head_off +
+           (int64_t)((start + t * kTile) & (bs - 1)) * RC;
   };
 
   // Software pipeline over this wave's tiles t = wave, wave + 4, ...: the K
   // registers are refilled for the next tile as soon as the scores are done,
   // the V registers as soon as the PV update is done, so one tile's loads are
-  // always in flight behind the current tile's arithmetic.
+  // always in flight behind the current tile's arithmetic. All branches are
+  // wave-uniform; the last tile is peeled so that every pipelined iteration
+  // prefetches unconditionally.
   uint4 kb[NGK][KCH];
   uint4 vb[NGV];
-  int64_t off = wave < ntiles ? tile_offset(wave) : -1;
-  if (off >= 0) {
-    load_k<S>(kcache + off, lane, kb);
-    load_v<S>(vcache + off, lane, vb);
-  }
-  for (int t = wave; t < ntiles; t += kWaves) {
+
+  auto process = [&](int t, int blk, int64_t off_next, auto prefetch) {
+    constexpr bool kPrefetch = decltype(prefetch)::value;
     const int tok0 = start + t * kTile;
-    const bool valid = off >= 0;  // invalid table entry: these tokens contribute nothing
-    const int64_t next_off = t + kWaves < ntiles ? tile_offset(t + kWaves) : -1;
+    const bool valid = blk >= 0;  // invalid table entry: these tokens contribute nothing
 
     // ---- scores: partial dots, then transposing reduction over KL lanes
     float sc[NV];
@@ -259,23 +263,28 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
         for (int i = 0; i < KCH; ++i) c = dot_chunk(T{}, kb[gk][i], q[g][i], c);
         sc[gk * G + g] = c;
       }
-    if (next_off >= 0) load_k<S>(kcache + next_off, lane, kb);
-    if (!valid) {
-      off = next_off;
-      if (off >= 0) load_v<S>(vcache + off, lane, vb);
-      continue;
-    }
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kPrefetch) load_k<S>(kcache + off_next, lane, kb);
+    __builtin_amdgcn_sched_barrier(0);
     transpose_reduce<NV, KL / 2>(sc);
 
-    const bool partial_tile = tok0 + kTile > n;
+    // rows past the context (or of an invalid block) are masked; they may
+    // hold anything, NaN included
+    const bool masked_tile = (tok0 + kTile > n) || !valid;
     float s[NVF];
 #pragma unroll
     for (int j = 0; j < NVF; ++j) {
       s[j] = sc[j] * a.scale_log2;
-      if (partial_tile) {
+      if (masked_tile) {
         const int tok = tok0 + S::slot_token(lane, j);
-        s[j] = tok < n ? s[j] : -INFINITY;
+        s[j] = (valid && tok < n) ? s[j] : -INFINITY;
       }
+    }
+    if (masked_tile) {
+      const int vrow = lane / VL;
+#pragma unroll
+      for (int gv = 0; gv < NGV; ++gv)
+        if (!valid || tok0 + gv * RV + vrow >= n) vb[gv] = make_uint4(0, 0, 0, 0);
     }
 
     // ---- online softmax: tile max per head, rescale on increase
@@ -318,24 +327,25 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
       for (int g = 0; g < G; ++g) m_run[g] = m_new[g];
     }
 
-    // ---- weights: exp2, running sums, hand to the V lanes through LDS
+    // ---- weights: exp2, running sums, hand to the V lanes through LDS. A
+    // head whose every score so far is masked has m = -inf: its weights are 0.
 #pragma unroll
     for (int j = 0; j < NVF; ++j) {
       float mh_j = m_run[0];
 #pragma unroll
       for (int g = 1; g < G; ++g) mh_j = S::slot_head(lane, j) == g ? m_run[g] : mh_j;
+      mh_j = mh_j == -INFINITY ? 0.f : mh_j;
       const float p = fast_exp2(s[j] - mh_j);
       l_slot[j] += p;
       p_lds[S::slot_token(lane, j) * G + S::slot_head(lane, j)] = p;
     }
     __builtin_amdgcn_wave_barrier();
 
-    // ---- PV: zero V rows past the context (they may hold anything)
+    // ---- PV over this lane's head-dim slice, all G heads
     const int vrow = lane / VL;
 #pragma unroll
     for (int gv = 0; gv < NGV; ++gv) {
       const int trow = gv * RV + vrow;
-      if (partial_tile && tok0 + trow >= n) vb[gv] = make_uint4(0, 0, 0, 0);
       float pw[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) pw[g] = p_lds[trow * G + g];
@@ -346,9 +356,23 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[g][e] = __builtin_fmaf(pw[g], v[e], acc[g][e]);
     }
-    off = next_off;
-    if (off >= 0) load_v<S>(vcache + off, lane, vb);
-    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kPrefetch) load_v<S>(vcache + off_next, lane, vb);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  int t = wave;
+  if (t < ntiles) {
+    int blk = tile_block(t);
+    const int64_t off = tile_offset(t, blk);
+    load_k<S>(kcache + off, lane, kb);
+    load_v<S>(vcache + off, lane, vb);
+    for (; t + kWaves < ntiles; t += kWaves) {
+      const int blk_next = tile_block(t + kWaves);
+      process(t, blk, tile_offset(t + kWaves, blk_next), std::true_type{});
+      blk = blk_next;
+    }
+    process(t, blk, 0, std::false_type{});
   }
 
   // ---- wave totals: l per head (each score counted once), m per head
