@@ -159,8 +159,9 @@ size_t pa_prefill_chunk_workspace_size(int32_t num_seqs, int32_t total_q,
  * n = context_lens[b] counts prefix plus chunk, so row i sits at position
  * n - L + i and attends keys 0 .. n - L + i:
  *   out[r,h,:] = sum_{j <= n-L+i} softmax_j(scale * q[r,h,:] . k_j) v_j
- * QK^T and PV run on the matrix cores in BF16 with float32 accumulation; the
- * softmax weights are rounded to BF16 before the PV product.
+ * QK^T and PV run on the matrix cores in BF16 with float32 accumulation; each
+ * softmax weight enters the PV product as the sum of two BF16 values (about
+ * 16 significant bits).
  *   query      BF16 [total_q, num_q_heads, head_dim]
  *   cu_q_lens  int32 [num_seqs + 1], device, non-decreasing, cu[0] = 0,
  *              cu[num_seqs] = total_q; each chunk length <= max_q_len and

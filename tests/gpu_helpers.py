@@ -59,3 +59,35 @@ def oracle_decode(case, layer=0, seqs=None):
 def max_abs_err(got, want):
     got = np.asarray(got, dtype=np.float64)
     return float(np.max(np.abs(got - want))) if got.size else 0.0
+
+
+def gpu_prefill(case, **kw):
+    p = case.prefill
+    return pa.pa_prefill_chunk(p.query, case.key_caches[0], case.value_caches[0], p.block_tables,
+                               p.context_lens, p.cu_q_lens, p.max_q_len, case.scale,
+                               int(max(int(x) for x in p.context_lens.cpu())), **kw)
+
+
+def oracle_prefill_rows(case, seq, rows):
+    """Oracle rows of prefill sequence `seq` (index among the prefill
+    sequences). Row i of a chunk of L rows at context n equals a one-row chunk
+    at context n - L + i + 1 (the oracle's chunking invariance, pinned by its
+    own tests), so sampled rows need only the blocks that row can see."""
+    p = case.prefill
+    b = case.num_decode_seqs + seq
+    n = int(case.layout.context_lens[b])
+    L = p.q_lens[seq]
+    q0 = int(np.sum(p.q_lens[:seq]))
+    bs = case.block_size
+    qh = to_numpy_bits(p.query)
+    out = []
+    for i in rows:
+        visible = n - L + i + 1
+        blocks = [int(x) for x in case.layout.block_tables[b, : -(-visible // bs)]]
+        idx = torch.as_tensor(blocks, dtype=torch.int64, device=case.key_caches[0].device)
+        kc = to_numpy_bits(case.key_caches[0].index_select(0, idx))
+        vc = to_numpy_bits(case.value_caches[0].index_select(0, idx))
+        table = np.arange(len(blocks), dtype=np.int32)[None, :]
+        out.append(oracle.prefill_chunk_ref(qh[q0 + i:q0 + i + 1], kc, vc, table,
+                                            np.array([visible]), np.array([0, 1]), case.scale)[0])
+    return np.stack(out)
