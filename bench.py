@@ -35,6 +35,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense BF16 matrix-core peak, TFLOP/s
 DECODE_SOURCES = ["paged_kv_cache_215_amd/csrc/pa_decode.hip",
                   "paged_kv_cache_215_amd/csrc/pa_device.hpp"]
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_c3_hbm_counters.json")
@@ -78,7 +79,7 @@ def source_hash(paths):
     return h.hexdigest()[:16]
 
 
-def load_traffic(bytes_per_call):
+def load_traffic():
     """HBM traffic per pa_decode call from the committed rocprofv3 counter
     summary, only if it was taken on the current decode kernel source."""
     try:
@@ -191,32 +192,52 @@ def run(args):
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step(events=None):
+    pf = case.prefill
+    if pf is not None:
+        pf_ctx = int(max(int(x) for x in pf.context_lens.cpu()))
+        pf_out = torch.empty((pf.query.shape[0], case.num_q_heads, case.head_dim),
+                             dtype=torch.float32, device=dev)
+        pf_ws = torch.empty(max(16, pa.pa_prefill_chunk_workspace_size(
+            len(pf.q_lens), pf.query.shape[0], pf.max_q_len, case.num_q_heads, case.num_kv_heads,
+            case.head_dim, case.block_size, pf_ctx)), dtype=torch.uint8, device=dev)
+
+    def timed(events, fn):
+        if events is None:
+            fn()
+            return
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        events.append((e0, e1))
+
+    def step(dec_events=None, pf_events=None):
         for layer in range(L):
             if case.slot_mapping is not None:
                 pa.pa_reshape_and_cache(case.new_keys[layer], case.new_values[layer],
                                         case.key_caches[layer], case.value_caches[layer],
                                         case.slot_mapping)
-            if events is not None:
-                events.append(torch.cuda.Event(enable_timing=True))
-                events[-1].record(stream)
-            pa.pa_decode(case.queries[layer], case.key_caches[layer], case.value_caches[layer],
-                         case.block_tables, case.context_lens, case.scale, case.max_context_len,
-                         out=outs[layer], workspace=workspace)
-            if events is not None:
-                events.append(torch.cuda.Event(enable_timing=True))
-                events[-1].record(stream)
+            timed(dec_events, lambda: pa.pa_decode(
+                case.queries[layer], case.key_caches[layer], case.value_caches[layer],
+                case.block_tables, case.context_lens, case.scale, case.max_context_len,
+                out=outs[layer], workspace=workspace))
+            if pf is not None:
+                timed(pf_events, lambda: pa.pa_prefill_chunk(
+                    pf.query, case.key_caches[layer], case.value_caches[layer], pf.block_tables,
+                    pf.context_lens, pf.cu_q_lens, pf.max_q_len, case.scale, pf_ctx,
+                    out=pf_out, workspace=pf_ws))
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = []
+    dec_events, pf_events = [], []
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(events)
+        step(dec_events, pf_events)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    decode_ms = [events[i].elapsed_time(events[i + 1]) for i in range(0, len(events), 2)]
+    decode_ms = [a.elapsed_time(b) for a, b in dec_events]
     avg_decode_s = float(np.mean(decode_ms)) / 1e3
 
     unique = args.workload == "c4_grpo_cow"
@@ -229,7 +250,7 @@ def run(args):
         f"{tokens_per_s:.1f} tok/s; pa_decode avg {avg_decode_s * 1e6:.1f} us "
         f"(min {min(decode_ms) * 1e3:.1f}, max {max(decode_ms) * 1e3:.1f}), "
         f"{achieved_gbs:.1f} GB/s = {achieved_gbs / HBM_PEAK_GBS:.3f} of HBM peak")
-    traffic = load_traffic(bytes_call)
+    traffic = load_traffic() if args.workload == "c3_full_step" else None
 
     result = {
         "metric": "paged-attn decode tokens/s & achieved HBM GB/s (% of 8 TB/s), 1 MI355X",
@@ -268,6 +289,22 @@ def run(args):
         },
         "cpu_baseline": None,
     }
+    if pf is not None:
+        pf_s = float(np.mean([a.elapsed_time(b) for a, b in pf_events])) / 1e3
+        flop = 0
+        for pre, ql in zip(pf.prefix_lens, pf.q_lens):
+            flop += 4 * case.num_q_heads * case.head_dim * sum(pre + i + 1 for i in range(ql))
+        result["prefill"] = {
+            "kernel": "pa_prefill_chunk (prefill_kernel + prefill_merge_kernel)",
+            "bound": "mfma",
+            "avg_call_us": round(pf_s * 1e6, 2),
+            "algorithmic_flop_per_call": flop,
+            "achieved": round(flop / pf_s / 1e12, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(flop / pf_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        }
+        log(f"[bench] pa_prefill_chunk avg {pf_s * 1e6:.1f} us, {flop / pf_s / 1e12:.1f} TFLOP/s")
 
     if not args.no_cpu_baseline:
         layers = list(range(min(L, args.cpu_sample_layers)))
@@ -288,6 +325,142 @@ def run(args):
     print(json.dumps(result), flush=True)
 
 
+def copy_calibration(nbytes=1 << 30, reps=5):
+    """A plain device copy of known size (for scaling the HBM byte counters)."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": nbytes, "bytes_written": nbytes,
+                                           "reps": reps}}), flush=True)
+
+
+# ------------------------------------------------------- profile summaries ---
+
+PROFILE_COMMANDS = {
+    "kt_c3": "cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats --output-format csv "
+             "-d <out>/kt_c3 -o kt -- python3 <repo>/bench.py --steps 5 --warmup 1 --no-cpu-baseline",
+    "kt_c5": "cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats --output-format csv "
+             "-d <out>/kt_c5 -o kt -- python3 <repo>/bench.py --workload c5_mixed_step "
+             "--steps 5 --warmup 1 --no-cpu-baseline",
+    "pmc_fetch_c3": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/pmc_fetch_c3 -o p -- "
+                    "python3 <repo>/bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+    "pmc_write_c3": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/pmc_write_c3 -o p -- "
+                    "python3 <repo>/bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+    "pmc_fetch_copy": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/pmc_fetch_copy -o p -- "
+                      "python3 <repo>/bench.py --copy-calib",
+    "pmc_write_copy": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/pmc_write_copy -o p -- "
+                      "python3 <repo>/bench.py --copy-calib",
+}
+
+
+def _csv(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _find(folder, suffix):
+    for dirpath, _, files in os.walk(folder):
+        for name in files:
+            if name.endswith(suffix):
+                return os.path.join(dirpath, name)
+    raise FileNotFoundError(f"no *{suffix} under {folder}")
+
+
+def _short(name):
+    name = name.replace("(pa::DecodeArgs)", "").replace("(pa::PrefillArgs)", "")
+    name = name.replace("(pa::ScatterArgs)", "").replace("void ", "")
+    return name if len(name) < 70 else name[:67] + "..."
+
+
+def _counter_means(folder, counter):
+    out = {}
+    for r in _csv(_find(folder, "counter_collection.csv")):
+        if r["Counter_Name"] != counter:
+            continue
+        out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: (len(v), sum(v) / len(v)) for k, v in out.items()}
+
+
+def summarize_profiles(src, dst):
+    """Turn rocprofv3 CSV output (folders named as in PROFILE_COMMANDS) into
+    the short text summaries kept under profiles/."""
+    os.makedirs(dst, exist_ok=True)
+    for tag, title in (("kt_c3", "pa kernels, 64 seqs x 8192 ctx x 16 layers (bs 32)"),
+                       ("kt_c5", "pa kernels, mixed step: 255 decode seqs + 512-row prefill chunk")):
+        folder = os.path.join(src, tag)
+        if not os.path.isdir(folder):
+            continue
+        rows = _csv(_find(folder, "kernel_stats.csv"))
+        lines = [f"# rocprofv3 kernel trace: {title}", "",
+                 "Command (run on one MI355X; `<repo>` is the repository root):", "",
+                 f"    {PROFILE_COMMANDS[tag]}", "",
+                 "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+        for r in rows:
+            if "pa::" not in r["Name"]:
+                continue
+            lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+        lines.append("")
+        lines.append("Kernels not listed are torch's input generation (outside the timed steps).")
+        name = "decode_c3_kernel_trace.md" if tag == "kt_c3" else "mixed_c5_kernel_trace.md"
+        with open(os.path.join(dst, name), "w") as f:
+            f.write("\n".join(lines) + "\n")
+        log(f"wrote {name}")
+
+    need = ["pmc_fetch_c3", "pmc_write_c3", "pmc_fetch_copy", "pmc_write_copy"]
+    if not all(os.path.isdir(os.path.join(src, t)) for t in need):
+        return
+    fetch = _counter_means(os.path.join(src, "pmc_fetch_c3"), "FETCH_SIZE")
+    write = _counter_means(os.path.join(src, "pmc_write_c3"), "WRITE_SIZE")
+    cf = _counter_means(os.path.join(src, "pmc_fetch_copy"), "FETCH_SIZE")
+    cw = _counter_means(os.path.join(src, "pmc_write_copy"), "WRITE_SIZE")
+    copy_name = [k for k in cf if "copyBuffer" in k][0]
+    calib = 1 << 30                                   # bench.py --copy-calib moves 1 GiB each way
+    f_factor = calib / (cf[copy_name][1] * 1024)
+    w_factor = calib / (cw[copy_name][1] * 1024)
+    parts = [k for k in fetch if "decode_partition_kernel" in k] + \
+            [k for k in fetch if "decode_merge_kernel" in k]
+    per_call_read = sum(fetch[k][1] for k in parts) * 1024 * f_factor
+    per_call_write = sum(write[k][1] for k in parts) * 1024 * w_factor
+    summary = {
+        "workload": "c3_full_step (64 seqs x 8192 ctx, bs 32, 4 KV / 16 query heads, d 256, BF16)",
+        "source_hash": source_hash(DECODE_SOURCES),
+        "copy_calibration": {"kernel": copy_name, "bytes_each_way": calib,
+                             "fetch_size_kib": cf[copy_name][1], "write_size_kib": cw[copy_name][1],
+                             "fetch_scale": f_factor, "write_scale": w_factor},
+        "per_kernel_kib_per_dispatch": {
+            _short(k): {"FETCH_SIZE": fetch[k][1], "WRITE_SIZE": write.get(k, (0, 0.0))[1],
+                        "dispatches": fetch[k][0]} for k in parts},
+        "hbm_read_bytes_per_call": per_call_read,
+        "hbm_write_bytes_per_call": per_call_write,
+        "hbm_bytes_per_call": per_call_read + per_call_write,
+        "commands": {t: PROFILE_COMMANDS[t] for t in need},
+    }
+    with open(os.path.join(dst, "decode_c3_hbm_counters.json"), "w") as f:
+        json.dump(summary, f, indent=1)
+    lines = ["# HBM traffic of pa_decode, 64 seqs x 8192 ctx (bs 32, BF16)", "",
+             "Per dispatch, averaged over the profiled steps; FETCH_SIZE and WRITE_SIZE are "
+             "in KiB. Each counter ran in a pass of its own.", "",
+             "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB |", "|---|---|---|"]
+    for k in parts:
+        lines.append(f"| `{_short(k)}` | {fetch[k][1]:.1f} | {write.get(k, (0, 0.0))[1]:.1f} |")
+    lines += ["", f"Calibration: a plain 1 GiB device copy (`{_short(copy_name)}`, "
+                  f"`bench.py --copy-calib`) reads as FETCH_SIZE {cf[copy_name][1]:.1f} KiB and "
+                  f"WRITE_SIZE {cw[copy_name][1]:.1f} KiB, so fetch counts are scaled by "
+                  f"{f_factor:.4f} and write counts by {w_factor:.4f}.", "",
+              f"Traffic per pa_decode call: read {per_call_read / 1e9:.4f} GB, write "
+              f"{per_call_write / 1e9:.4f} GB, total {(per_call_read + per_call_write) / 1e9:.4f} GB "
+              f"(algorithmic bytes: 2.1491 GB).", "", "Commands:", ""]
+    lines += [f"    {PROFILE_COMMANDS[t]}" for t in need]
+    with open(os.path.join(dst, "decode_c3_hbm_counters.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    log("wrote decode_c3_hbm_counters.{json,md}")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -296,8 +469,15 @@ def main():
     ap.add_argument("--workload", default="c3_full_step",
                     choices=["c2_layer_decode", "c3_full_step", "c4_grpo_cow", "c5_mixed_step"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-layers", type=int, default=2)
+    ap.add_argument("--cpu-sample-layers", type=int, default=4)
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="run only a plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--summarize-profile", metavar="DIR", default=None,
+                    help="write profiles/ summaries from rocprofv3 CSV output under DIR")
     args = ap.parse_args()
+    if args.summarize_profile:
+        summarize_profiles(args.summarize_profile, os.path.join(ROOT, "profiles"))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
@@ -305,6 +485,9 @@ def main():
     if "RANK" in os.environ and os.environ.get("WORLD_SIZE", "1") != "1":
         print("bench.py runs on one GPU only (WORLD_SIZE > 1 given)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calib:
+        copy_calibration()
+        return
     run(args)
 
 
