@@ -187,9 +187,8 @@ def run(args):
     elem = 2 if case.dtype == torch.bfloat16 else 4
     outs = [torch.empty((S, case.num_q_heads, case.head_dim), dtype=torch.float32, device=dev)
             for _ in range(L)]
-    ws_bytes = pa.pa_decode_workspace_size(S, case.num_q_heads, case.num_kv_heads, case.head_dim,
-                                           case.block_size, case.max_context_len)
-    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    workspace = pa.decode_workspace(S, case.num_q_heads, case.num_kv_heads, case.head_dim,
+                                    case.block_size, case.max_context_len, dev)
     stream = torch.cuda.current_stream(dev)
 
     pf = case.prefill

@@ -21,7 +21,9 @@ from ._lib import (  # noqa: F401
     SIGNATURES,
     PaError,
     lib,
+    decode_workspace,
     pa_decode,
+    pa_decode_workspace_init,
     pa_decode_workspace_size,
     pa_prefill_chunk,
     pa_prefill_chunk_workspace_size,

@@ -29,6 +29,7 @@ _i32, _i64, _sz, _vp, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ct
 SIGNATURES = {
     "pa_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i32, _vp]),
     "pa_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_workspace_init": (_i32, [_vp, _sz, _vp]),
     "pa_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
                          _i32, _f32, _i32, _vp, _sz, _vp]),
     "pa_prefill_chunk_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
@@ -123,6 +124,23 @@ def pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, bloc
                                               block_size, max_context_len))
 
 
+def pa_decode_workspace_init(workspace):
+    """Zero-fill a decode workspace on the current stream (needed once)."""
+    dev = _dev(workspace)
+    _check("pa_decode_workspace_init", lib().pa_decode_workspace_init(
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev)))
+
+
+def decode_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                     max_context_len, device):
+    """A zero-filled decode workspace for these sizes, reusable across calls."""
+    need = pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                    max_context_len)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    pa_decode_workspace_init(ws)
+    return ws
+
+
 def pa_decode(query, key_cache, value_cache, block_tables, context_lens, scale,
               max_context_len, out=None, workspace=None):
     """Decode attention over the paged cache; returns float32 [S, Hq, d]."""
@@ -133,10 +151,9 @@ def pa_decode(query, key_cache, value_cache, block_tables, context_lens, scale,
     num_blocks, num_kv_heads, block_size, _ = key_cache.shape
     if out is None:
         out = torch.empty((num_seqs, num_q_heads, head_dim), dtype=torch.float32, device=dev)
-    need = pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                                    max_context_len)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        workspace = decode_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                     max_context_len, dev)
     _dev(out, workspace)
     _check("pa_decode", lib().pa_decode(
         _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),

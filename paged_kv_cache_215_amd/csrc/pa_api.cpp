@@ -24,6 +24,15 @@ int decode_target_workgroups() {
   return target;
 }
 
+int decode_waves_per_workgroup() {
+  static const int waves = [] {
+    const char* s = std::getenv("PA_DECODE_WAVES");
+    const int v = s ? std::atoi(s) : 0;
+    return v == 4 ? 4 : 8;
+  }();
+  return waves;
+}
+
 }  // namespace pa
 
 namespace {
@@ -49,20 +58,25 @@ int32_t ctx_limit(int32_t max_ctx, int32_t max_blocks, int32_t bs) {
 }
 
 struct DecodeGeometry {
-  int part_tokens;
-  int max_parts;
-  size_t part_o_bytes;
+  pa::DecodeLaunch launch;
+  size_t part_o_off;
+  size_t part_ml_off;
   size_t bytes;
 };
 
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Workspace: plan summary | partial outputs | partial (m, l). Launches of at
+// most 4096 sequences each reuse it in stream order.
 DecodeGeometry decode_geometry(int32_t num_seqs, int32_t hq, int32_t hkv, int32_t d, int32_t bs,
                                int32_t max_ctx) {
   DecodeGeometry g;
-  g.part_tokens = pa::decode_part_tokens(num_seqs, hkv, bs, max_ctx);
-  g.max_parts = (max_ctx + g.part_tokens - 1) / g.part_tokens;
-  const size_t rows = (size_t)num_seqs * hq * (g.max_parts > 0 ? g.max_parts : 1);
-  g.part_o_bytes = rows * d * sizeof(float);
-  g.bytes = g.part_o_bytes + rows * 2 * sizeof(float);
+  g.launch = pa::decode_launch_shape(num_seqs, hkv, bs, max_ctx);
+  const size_t seqs = num_seqs < 4096 ? (size_t)num_seqs : 4096;
+  const size_t rows = seqs * hq * g.launch.max_parts;
+  g.part_o_off = 256;
+  g.part_ml_off = round_up(g.part_o_off + rows * d * sizeof(float), 256);
+  g.bytes = round_up(g.part_ml_off + rows * 2 * sizeof(float), 256);
   return g;
 }
 
@@ -113,6 +127,14 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
       .bytes;
 }
 
+pa_status_t pa_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (workspace_bytes == 0) return PA_OK;
+  if (!workspace) return PA_ERR_NULL;
+  if (!aligned(workspace, 16)) return PA_ERR_ALIGN;
+  return from_hip(pa::launch_zero_fill(workspace, workspace_bytes & ~(size_t)15,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 pa_status_t pa_decode(float* out, const void* query, const void* key_cache,
                       const void* value_cache, const int32_t* block_tables,
                       const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
@@ -142,9 +164,13 @@ pa_status_t pa_decode(float* out, const void* query, const void* key_cache,
   if (workspace_bytes < geo.bytes) return PA_ERR_WORKSPACE;
 
   pa::DecodeArgs a;
+  char* ws = static_cast<char*>(workspace);
   a.out = out;
-  a.part_o = static_cast<float*>(workspace);
-  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + geo.part_o_bytes);
+  a.plan = reinterpret_cast<pa::DecodePlan*>(ws);
+  a.plan_cus = 0;
+  a.plan_units_per_cu = 0;
+  a.part_o = reinterpret_cast<float*>(ws + geo.part_o_off);
+  a.part_ml = reinterpret_cast<float*>(ws + geo.part_ml_off);
   a.query = query;
   a.key_cache = key_cache;
   a.value_cache = value_cache;
@@ -158,8 +184,10 @@ pa_status_t pa_decode(float* out, const void* query, const void* key_cache,
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_blocks = num_blocks;
   a.ctx_limit = ctx_limit(max_context_len, max_blocks_per_seq, block_size);
-  a.part_tokens = geo.part_tokens;
-  a.max_parts = geo.max_parts;
+  a.part_floor = geo.launch.part_floor;
+  a.part_cap = geo.launch.part_cap;
+  a.waves = geo.launch.waves;
+  a.max_parts = geo.launch.max_parts;
   a.scale_log2 = scale * 1.4426950408889634f;
   return from_hip(pa::launch_decode(a, dtype == PA_DTYPE_BF16, static_cast<hipStream_t>(stream)));
 }

@@ -35,13 +35,13 @@
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
 
+#include <cstdlib>
 #include <type_traits>
 
 namespace pa {
 
 constexpr int kTile = 16;
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * kWave;
+constexpr int kMaxPartBlocks = 512;  // table entries staged per partition
 
 constexpr int choose_k_lanes(int row_chunks, int group) {
   // Enough lanes per K row that the q chunks held per lane (group * KCH
@@ -159,29 +159,186 @@ __device__ __forceinline__ void load_v(const uint4* __restrict__ vbase, int lane
   for (int gv = 0; gv < Shape::NGV; ++gv) vb[gv] = load_stream(vbase + (gv * RV + vrow) * RC + vc);
 }
 
-template <typename T, int D, int G>
-__global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a) {
+// ---------------------------------------------------------------------------
+// Plan of one decode call. Every partition workgroup derives the same plan
+// from the context lengths: the partition size is one partition per sequence
+// for a batch of equal lengths (when that alone gives every CU a unit),
+// otherwise about units_per_cu units per CU; units are every full partition
+// first, then each sequence's last (shorter) one, and a single unit for an
+// empty context (its zero row). A launch covers at most kPlanSeqs sequences.
+constexpr int kPlanSeqs = 4096;
+
+__device__ __forceinline__ long long wave_sum_ll(long long x) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) x += __shfl_xor(x, m);
+  return x;
+}
+__device__ __forceinline__ int wave_min(int x) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) x = min(x, __shfl_xor(x, m));
+  return x;
+}
+__device__ __forceinline__ int wave_max(int x) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) x = max(x, __shfl_xor(x, m));
+  return x;
+}
+// inclusive prefix sum across the wave
+__device__ __forceinline__ int wave_scan(int x) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) {
+    const int y = __shfl_up(x, m);
+    if (lane >= m) x += y;
+  }
+  return x;
+}
+
+struct PlanLds {
+  int lens[kPlanSeqs];        // clamped context lengths
+  int full_pre[kPlanSeqs];    // exclusive prefix of full-partition counts
+  long long red_sum[16];
+  int red_a[16], red_b[16];
+  int part_tokens, full_total, max_nparts;
+  int ticket;                 // this workgroup's current unit
+};
+
+// Fills the plan for the whole workgroup (NW waves); ends with a barrier.
+template <int NW>
+__device__ void build_plan(const DecodeArgs& a, PlanLds& pl) {
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int S = a.num_seqs;
+  constexpr int kT = NW * kWave;
+  const int chunk = (S + kT - 1) / kT;
+  const int b0 = min(S, tid * chunk), b1 = min(S, b0 + chunk);
+  long long sum = 0;
+  int mn = 0x7fffffff, mx = 0;
+  for (int b = b0; b < b1; ++b) {
+    int n = a.context_lens[b];
+    n = n < 0 ? 0 : n;
+    n = n > a.ctx_limit ? a.ctx_limit : n;
+    pl.lens[b] = n;
+    sum += n;
+    mn = min(mn, n);
+    mx = max(mx, n);
+  }
+  sum = wave_sum_ll(sum);
+  mn = wave_min(mn);
+  mx = wave_max(mx);
+  if (lane == 0) {
+    pl.red_sum[wave] = sum;
+    pl.red_a[wave] = mn;
+    pl.red_b[wave] = mx;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    sum = lane < NW ? pl.red_sum[lane] : 0;
+    mn = lane < NW ? pl.red_a[lane] : 0x7fffffff;
+    mx = lane < NW ? pl.red_b[lane] : 0;
+    sum = wave_sum_ll(sum);
+    mn = wave_min(mn);
+    mx = wave_max(mx);
+    if (lane == 0) {
+      int P = a.part_floor;
+      if (mx > 0 && mn == mx) {
+        for (int p = a.part_floor; p <= a.part_cap; p *= 2)
+          if ((long long)S * a.num_kv_heads * ((mx + p - 1) / p) >= a.plan_cus) P = p;
+      } else if (mx > 0) {
+        const long long budget =
+            sum * a.num_kv_heads / ((long long)a.plan_cus * a.plan_units_per_cu);
+        for (int p = a.part_floor; p <= a.part_cap; p *= 2)
+          if (p <= budget) P = p;
+      }
+      pl.part_tokens = P;
+    }
+  }
+  __syncthreads();
+  const int P = pl.part_tokens;
+  int full = 0, most = 0;
+  for (int b = b0; b < b1; ++b) {
+    const int np = max(1, (pl.lens[b] + P - 1) / P);
+    full += np - 1;
+    most = max(most, np);
+  }
+  const int incl = wave_scan(full);
+  most = wave_max(most);
+  __syncthreads();  // the reduction slots are reused below
+  if (lane == kWave - 1) pl.red_a[wave] = incl;
+  if (lane == 0) pl.red_b[wave] = most;
+  __syncthreads();
+  if (wave == 0) {
+    const int c = lane < NW ? pl.red_a[lane] : 0;
+    const int ci = wave_scan(c);
+    const int mp = wave_max(lane < NW ? pl.red_b[lane] : 0);
+    if (lane < NW) pl.red_a[lane] = ci - c;
+    if (lane == kWave - 1) {
+      pl.full_total = ci;
+      pl.max_nparts = mp;
+    }
+  }
+  __syncthreads();
+  int run = pl.red_a[wave] + incl - full;
+  for (int b = b0; b < b1; ++b) {
+    pl.full_pre[b] = run;
+    run += max(1, (pl.lens[b] + P - 1) / P) - 1;
+  }
+  __syncthreads();
+}
+
+// Unit e of the plan -> (sequence, partition).
+__device__ __forceinline__ int2 plan_unit(const PlanLds& pl, int S, int e) {
+  if (e >= pl.full_total) {
+    const int b = e - pl.full_total;
+    const int P = pl.part_tokens;
+    return make_int2(b, max(1, (pl.lens[b] + P - 1) / P) - 1);
+  }
+  int lo = 0, hi = S - 1;  // last b with full_pre[b] <= e
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pl.full_pre[mid] <= e) lo = mid; else hi = mid - 1;
+  }
+  return make_int2(lo, e - pl.full_pre[lo]);
+}
+
+template <typename T, int D, int G, int NW>
+__global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(DecodeArgs a) {
   using S = DecodeShape<T, D, G>;
+  constexpr int kWaves = NW;
+  constexpr int kThreads = NW * kWave;
   constexpr int RC = S::RC, KL = S::KL, KCH = S::KCH, NGK = S::NGK, NV = S::NV,
                 NVF = S::NVF, NGV = S::NGV, VL = S::VL, RV = S::RV, E = S::E;
 
+  __shared__ PlanLds s_plan;
+  __shared__ int s_bt[kMaxPartBlocks];
   __shared__ float s_p[kWaves][kTile * G];
   __shared__ float s_m[kWaves][G];
   __shared__ float s_l[kWaves][G];
-  __shared__ float4 s_acc[kWaves][RV][G][D / 4];
+  __shared__ float4 s_acc[kWaves][G][D / 4];
 
-  const int part = blockIdx.x, kvh = blockIdx.y, seq = blockIdx.z;
   const int bs_log2 = a.block_size_log2;
   const int bs = 1 << bs_log2;
-  int n = a.context_lens[seq];
-  n = n < 0 ? 0 : n;
-  n = n > a.ctx_limit ? a.ctx_limit : n;
-  const int start = part * a.part_tokens;
-  if (start >= n) return;
-  const int end = min(start + a.part_tokens, n);
-  const int nparts = (n + a.part_tokens - 1) / a.part_tokens;
-
   const int tid = threadIdx.x;
+  build_plan<NW>(a, s_plan);
+  const int P = s_plan.part_tokens;
+  if (blockIdx.x == 0 && tid == 0) {  // for the merge kernel
+    a.plan->part_tokens = P;
+    a.plan->max_nparts = s_plan.max_nparts;
+  }
+
+  // One work unit: (sequence, KV head, partition) of the plan.
+  auto unit = [&](const int seq, const int kvh, const int part) {
+  const int n = s_plan.lens[seq];
+  const int start = part * P;
+  if (n == 0) {  // empty context: a zero row
+    for (int idx = tid; idx < G * D / 4; idx += kThreads)
+      reinterpret_cast<float4*>(a.out)[((int64_t)seq * a.num_q_heads + (int64_t)kvh * G) * (D / 4) + idx] =
+          make_float4(0.f, 0.f, 0.f, 0.f);
+    return;
+  }
+  if (start >= n) return;
+  const int end = min(start + P, n);
+  const int nparts = (n + P - 1) / P;
+
   // wave index as a scalar, so that all tile bookkeeping below is uniform
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
@@ -198,15 +355,16 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
       for (int i = 0; i < KCH; ++i) q[g][i] = qb[g * RC + kc + KL * i];
   }
 
-  // Block-table entries of this partition: lane i holds entry blk0 + i
-  // (at most 64 blocks per partition by construction of part_tokens).
+  // Block-table entries of this partition, staged in LDS (at most
+  // kMaxPartBlocks by construction of part_tokens); -1 marks an entry outside
+  // the pool.
   const int blk0 = start >> bs_log2;
   const int nblk = ((end - start) + bs - 1) >> bs_log2;
-  int my_block = -1;
-  if (lane < nblk) {
-    const int e = a.block_tables[(int64_t)seq * a.max_blocks_per_seq + blk0 + lane];
-    my_block = (e >= 0 && (int64_t)e < a.num_blocks) ? e : -1;
+  for (int i = tid; i < nblk; i += kThreads) {
+    const int e = a.block_tables[(int64_t)seq * a.max_blocks_per_seq + blk0 + i];
+    s_bt[i] = (e >= 0 && (int64_t)e < a.num_blocks) ? e : -1;
   }
+  __syncthreads();
 
   const uint4* kcache = reinterpret_cast<const uint4*>(a.key_cache);
   const uint4* vcache = reinterpret_cast<const uint4*>(a.value_cache);
@@ -228,10 +386,10 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
   const int ntiles = (end - start + kTile - 1) / kTile;
   float* p_lds = s_p[wave];
 
-  // Physical block of tile t (a scalar read of the table entry held by lane
-  // t*16/bs); an entry outside the pool reads block 0 and the tile is masked.
+  // Physical block of tile t (one broadcast LDS read, made scalar); an entry
+  // outside the pool reads block 0 and the tile is masked.
   auto tile_block = [&](int t) -> int {
-    return __builtin_amdgcn_readlane(my_block, (t * kTile) >> bs_log2);
+    return __builtin_amdgcn_readfirstlane(s_bt[(t * kTile) >> bs_log2]);
   };
   auto tile_offset = [&](int t, int blk) -> int64_t {
     return (int64_t)(blk < 0 ? 0 : blk) * block_stride + head_off +
@@ -397,13 +555,26 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
     }
   }
   {
-    const int r = lane / VL, c = lane % VL;
+    // sum the RV row groups of the wave (lanes l, l + VL, ...) in registers
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int e4 = 0; e4 < E / 4; ++e4)
-        s_acc[wave][r][g][c * (E / 4) + e4] =
-            make_float4(acc[g][4 * e4], acc[g][4 * e4 + 1], acc[g][4 * e4 + 2], acc[g][4 * e4 + 3]);
+      for (int e = 0; e < E; ++e) {
+        float x = acc[g][e];
+        if constexpr (VL <= 32 && RV > 1) x += xor_lane<(VL <= 32 ? 32 : 1)>(x);
+        if constexpr (VL <= 16 && RV > 2) x += xor_lane<(VL <= 16 ? 16 : 1)>(x);
+        if constexpr (VL <= 8 && RV > 4) x += xor_lane<(VL <= 8 ? 8 : 1)>(x);
+        acc[g][e] = x;
+      }
+    if (lane < VL) {
+      const int c = lane;
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e4 = 0; e4 < E / 4; ++e4)
+          s_acc[wave][g][c * (E / 4) + e4] =
+              make_float4(acc[g][4 * e4], acc[g][4 * e4 + 1], acc[g][4 * e4 + 2], acc[g][4 * e4 + 3]);
+    }
   }
   __syncthreads();
 
@@ -419,11 +590,8 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
     for (int w = 0; w < kWaves; ++w) {
       const float sw = fast_exp2(s_m[w][g] - M);
       L += sw * s_l[w][g];
-#pragma unroll
-      for (int r = 0; r < RV; ++r) {
-        const float4 x = s_acc[w][r][g][d4];
-        o.x += sw * x.x; o.y += sw * x.y; o.z += sw * x.z; o.w += sw * x.w;
-      }
+      const float4 x = s_acc[w][g][d4];
+      o.x += sw * x.x; o.y += sw * x.y; o.z += sw * x.z; o.w += sw * x.w;
     }
     const float inv = 1.f / L;
     o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
@@ -439,28 +607,59 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
       }
     }
   }
+  };  // unit
+
+  // Persistent loop. Full partitions (all of one size) go round-robin, so the
+  // grid walks them in lockstep rounds: sequences that share prompt blocks
+  // (copy-on-write rollouts are consecutive) read those blocks at about the
+  // same time. The last partitions, whose sizes are ragged, are then taken
+  // from the ticket counter in the workspace head so they balance across CUs;
+  // the merge kernel, which follows in stream order, resets the counter.
+  const int n_full = s_plan.full_total * a.num_kv_heads;
+  const int n_units = (s_plan.full_total + a.num_seqs) * a.num_kv_heads;
+  for (int u = blockIdx.x; u < n_full; u += gridDim.x) {
+    const int2 e = plan_unit(s_plan, a.num_seqs, u / a.num_kv_heads);
+    unit(e.x, u % a.num_kv_heads, e.y);
+    __syncthreads();  // LDS is reused by the next unit
+  }
+  for (;;) {
+    if (tid == 0) s_plan.ticket = atomicAdd(&a.plan->ticket, 1);
+    __syncthreads();
+    const int u = n_full + s_plan.ticket;
+    __syncthreads();  // every thread has read the ticket before it is reused
+    if (u < n_full || u >= n_units) break;  // (below n_full: workspace never zero-filled)
+    const int2 e = plan_unit(s_plan, a.num_seqs, u / a.num_kv_heads);
+    unit(e.x, u % a.num_kv_heads, e.y);
+    __syncthreads();
+  }
 }
 
 // Merge of the per-partition partials of one (sequence, query head):
 // out = sum_p w_p o_p / sum_p w_p with w_p = l_p * 2^(m_p - max_p m_p).
+// Persistent over rows; when the plan gave every sequence one partition the
+// partition kernel already wrote every row and the launch ends at once. It
+// also resets the partition kernel's ticket counter for the next call.
 template <int D>
 __global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeArgs a) {
   constexpr int PER = D / kWave;  // 1, 2 or 4 floats per lane
-  const int h = blockIdx.x, seq = blockIdx.y;
-  int n = a.context_lens[seq];
-  n = n < 0 ? 0 : n;
-  n = n > a.ctx_limit ? a.ctx_limit : n;
-  const int nparts = (n + a.part_tokens - 1) / a.part_tokens;
-  const int64_t head = (int64_t)seq * a.num_q_heads + h;
-  float* out = a.out + head * D + threadIdx.x * PER;
-  if (nparts == 1) return;  // the partition kernel wrote this row
-  float o[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) o[e] = 0.f;
-  if (nparts > 1) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) a.plan->ticket = 0;  // ready for the next call
+  const int P = a.plan->part_tokens;
+  if (a.plan->max_nparts <= 1) return;
+  const int rows = a.num_seqs * a.num_q_heads;
+  for (int row = blockIdx.x; row < rows; row += gridDim.x) {
+    const int seq = row / a.num_q_heads;
+    int n = a.context_lens[seq];
+    n = n < 0 ? 0 : n;
+    n = n > a.ctx_limit ? a.ctx_limit : n;
+    const int nparts = (n + P - 1) / P;
+    if (nparts <= 1) continue;  // written by the partition kernel (zeros if empty)
+    const int64_t head = row;
     const float* ml = a.part_ml + 2 * head * a.max_parts;
     float M = -INFINITY;
     for (int p = 0; p < nparts; ++p) M = fmaxf(M, ml[2 * p]);
+    float o[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) o[e] = 0.f;
     float L = 0.f;
     const float* po = a.part_o + head * a.max_parts * D + threadIdx.x * PER;
     for (int p = 0; p < nparts; ++p) {
@@ -470,49 +669,131 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeArgs a) {
       for (int e = 0; e < PER; ++e) o[e] = __builtin_fmaf(w, po[(int64_t)p * D + e], o[e]);
     }
     const float inv = 1.f / L;
+    float* out = a.out + head * D + threadIdx.x * PER;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) o[e] *= inv;
+    for (int e = 0; e < PER; ++e) out[e] = o[e] * inv;
   }
-#pragma unroll
-  for (int e = 0; e < PER; ++e) out[e] = o[e];
+}
+
+// Zero fill of a decode workspace (a kernel rather than a memset, so that it
+// can be captured in a graph).
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint4* p, int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16;
+       i += (int64_t)gridDim.x * 256)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t stream) {
+  const int64_t n16 = (int64_t)(bytes / 16);
+  if (n16 == 0) return hipSuccess;
+  int64_t blocks = (n16 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     static_cast<uint4*>(p), n16);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
 // Host side.
 
-int decode_part_tokens(int num_seqs, int num_kv_heads, int block_size, int max_context_len) {
-  // Largest partition (a multiple of 64 tokens, at most 64 blocks) that still
-  // gives the launch enough workgroups to fill 256 CUs several times over.
-  const int target = decode_target_workgroups();
-  int best = 64;
-  const int cap = 64 * block_size;
-  for (int p = 64; p <= cap; p *= 2) {
-    const int64_t parts = (max_context_len + p - 1) / p;
-    if ((int64_t)num_seqs * num_kv_heads * parts >= target) best = p;
+DecodeLaunch decode_launch_shape(int num_seqs, int num_kv_heads, int block_size,
+                                 int max_context_len) {
+  // The plan kernel picks the partition size per call between part_floor and
+  // part_cap; the workspace is laid out for part_floor (the most partitions).
+  DecodeLaunch r;
+  r.waves = decode_waves_per_workgroup();
+  r.part_floor = 256;                                   // a multiple of 16 * 8 waves
+  r.part_cap = kMaxPartBlocks * block_size < 8192 ? kMaxPartBlocks * block_size : 8192;
+  r.max_parts = (max_context_len + r.part_floor - 1) / r.part_floor;
+  if (r.max_parts < 1) r.max_parts = 1;
+  return r;
+}
+
+namespace {
+
+int device_cus() {
+  static int cus[64] = {0};  // per device, filled on first use
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int v = 0;
+    cus[dev] = (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) ==
+                    hipSuccess && v > 0)
+                   ? v
+                   : 256;
   }
-  return best;
+  return cus[dev];
+}
+
+int units_per_cu() {
+  static const int v = [] {
+    const char* s = std::getenv("PA_DECODE_UNITS_PER_CU");
+    const int x = s ? std::atoi(s) : 0;
+    return x > 0 ? x : 4;
+  }();
+  return v;
+}
+
+template <typename Kernel>
+int resident_per_cu(Kernel k, int threads) {
+  int blocks = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k, threads, 0) != hipSuccess ||
+      blocks < 1)
+    blocks = 1;
+  return blocks;
+}
+
+}  // namespace
+
+template <typename T, int D, int G, int NW>
+static hipError_t launch_nw(const DecodeArgs& a, hipStream_t stream) {
+  static const int per_cu = resident_per_cu(decode_partition_kernel<T, D, G, NW>, NW * kWave);
+  const int cus = device_cus();
+  // Batches above kPlanSeqs sequences run as consecutive launches of at most
+  // kPlanSeqs sequences each, sharing the workspace in stream order.
+  for (int s0 = 0; s0 < a.num_seqs; s0 += kPlanSeqs) {
+    DecodeArgs c = a;
+    c.num_seqs = a.num_seqs - s0 < kPlanSeqs ? a.num_seqs - s0 : kPlanSeqs;
+    c.out = a.out + (int64_t)s0 * a.num_q_heads * D;
+    c.query = static_cast<const char*>(a.query) + (int64_t)s0 * a.num_q_heads * D * T::kBytes;
+    c.block_tables = a.block_tables + (int64_t)s0 * a.max_blocks_per_seq;
+    c.context_lens = a.context_lens + s0;
+    c.plan_cus = cus;
+    c.plan_units_per_cu = units_per_cu();
+    const int64_t most_units = (int64_t)c.num_seqs * c.num_kv_heads * c.max_parts;
+    const int64_t slots = (int64_t)cus * per_cu;
+    const int64_t grid = most_units < slots ? most_units : slots;
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, G, NW>), dim3((unsigned)grid),
+                       dim3(NW * kWave), 0, stream, c);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int64_t rows = (int64_t)c.num_seqs * c.num_q_heads;
+    const int64_t mgrid = rows < (int64_t)cus ? rows : (int64_t)cus;
+    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)mgrid), dim3(kWave), 0, stream, c);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
 }
 
 template <typename T, int D, int G>
-static hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  if (a.max_parts > 0) {  // every context empty: only the merge kernel runs (zero rows)
-    dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
-    hipLaunchKernelGGL((decode_partition_kernel<T, D, G>), grid, dim3(kThreads), 0, stream, a);
-    const hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+static hipError_t launch_t(const DecodeArgs& a, int waves, hipStream_t stream) {
+  // 8-wave workgroups are limited to 256 VGPRs per lane; the d = 256 shapes
+  // with 8 query heads per KV head or float32 data need more and use 4 waves.
+  constexpr bool kFits8 = !(D == 256 && (G == 8 || T::kBytes == 4));
+  if constexpr (kFits8) {
+    if (waves == 8) return launch_nw<T, D, G, 8>(a, stream);
   }
-  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.num_q_heads, a.num_seqs), dim3(kWave), 0,
-                     stream, a);
-  return hipGetLastError();
+  return launch_nw<T, D, G, 4>(a, stream);
 }
 
 template <typename T, int D>
 static hipError_t launch_g(const DecodeArgs& a, int group, hipStream_t stream) {
   switch (group) {
-    case 1: return launch_t<T, D, 1>(a, stream);
-    case 2: return launch_t<T, D, 2>(a, stream);
-    case 4: return launch_t<T, D, 4>(a, stream);
-    case 8: return launch_t<T, D, 8>(a, stream);
+    case 1: return launch_t<T, D, 1>(a, a.waves, stream);
+    case 2: return launch_t<T, D, 2>(a, a.waves, stream);
+    case 4: return launch_t<T, D, 4>(a, a.waves, stream);
+    case 8: return launch_t<T, D, 8>(a, a.waves, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -6,6 +6,15 @@
 
 namespace pa {
 
+// Plan summary of one decode launch, written by the partition kernel into the
+// head of the workspace for the merge kernel.
+struct DecodePlan {
+  int part_tokens;   // tokens per partition chosen for this batch
+  int max_nparts;    // largest partition count of any sequence
+  int ticket;        // next unit to take; 0 between calls
+  int pad;
+};
+
 struct DecodeArgs {
   float* out;            // [S, Hq, D] float32
   float* part_o;         // [S, Hq, max_parts, D] normalised partial outputs
@@ -23,8 +32,13 @@ struct DecodeArgs {
   int max_blocks_per_seq;
   int64_t num_blocks;
   int ctx_limit;         // min(max_context_len, max_blocks_per_seq * block_size)
-  int part_tokens;       // tokens per context partition (multiple of 64)
-  int max_parts;         // ceil(max_context_len / part_tokens)
+  DecodePlan* plan;      // workspace head: plan summary for the merge kernel
+  int plan_cus;          // CUs of the device (sizes the plan)
+  int plan_units_per_cu; // target units per CU for ragged batches
+  int part_floor;        // smallest partition size the plan may choose
+  int part_cap;          // largest partition size the plan may choose
+  int waves;             // waves per partition workgroup (4 or 8)
+  int max_parts;         // ceil(max_context_len / part_floor): workspace layout
   float scale_log2;      // softmax scale * log2(e)
 };
 
@@ -65,9 +79,19 @@ struct PrefillArgs {
   float scale_log2;
 };
 
+struct DecodeLaunch {
+  int part_floor;
+  int part_cap;
+  int max_parts;
+  int waves;
+};
+
 int decode_target_workgroups();
-int decode_part_tokens(int num_seqs, int num_kv_heads, int block_size, int max_context_len);
+int decode_waves_per_workgroup();
+DecodeLaunch decode_launch_shape(int num_seqs, int num_kv_heads, int block_size,
+                                 int max_context_len);
 hipError_t launch_decode(const DecodeArgs& a, bool bf16, hipStream_t stream);
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t stream);
 hipError_t launch_scatter(const ScatterArgs& a, hipStream_t stream);
 
 int prefill_kv_splits(int num_seqs, int max_q_len, int num_kv_heads, int max_context_len);

@@ -139,3 +139,9 @@ def test_binding_raises_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         L.lib()
+
+
+def test_workspace_init_rejects(lib):
+    assert lib.pa_decode_workspace_init(None, 256, None) == NULL
+    assert lib.pa_decode_workspace_init(A + 4, 256, None) == ALIGN
+    assert lib.pa_decode_workspace_init(None, 0, None) == OK

@@ -167,3 +167,38 @@ def test_workspace_size_matches_partition_geometry():
     # every launch shape in this file fits the advertised workspace
     need = pa.pa_decode_workspace_size(64, 16, 4, 256, 32, 8192)
     assert need > 0 and need % 16 == 0
+
+
+def test_workspace_reused_across_batches():
+    # One zero-filled workspace, sized for the largest call, serves a ragged
+    # batch, a uniform batch and a ragged batch again in stream order (the
+    # work-queue counter is left at zero by every call).
+    cases = [
+        make_case(name="reuse_a", seed=21, context_lens=[700, 33, 5000, 1], num_q_heads=16,
+                  num_kv_heads=4, head_dim=256, block_size=16, device=DEV),
+        make_case(name="reuse_b", seed=22, context_lens=[4096] * 8, num_q_heads=16,
+                  num_kv_heads=4, head_dim=256, block_size=16, device=DEV),
+        make_case(name="reuse_c", seed=23, context_lens=[64, 8000, 300], num_q_heads=16,
+                  num_kv_heads=4, head_dim=256, block_size=16, device=DEV),
+    ]
+    ws = pa.decode_workspace(8, 16, 4, 256, 16, 8192, torch.device(DEV))
+    for case in cases:
+        out = pa.pa_decode(case.queries[0], case.key_caches[0], case.value_caches[0],
+                           case.block_tables, case.context_lens, case.scale, 8192, workspace=ws)
+        torch.cuda.synchronize()
+        err = max_abs_err(out.cpu().numpy(), oracle_decode(case))
+        say(f"[decode] {case.name} with a shared workspace: max-abs err {err:.3e}")
+        assert err <= ATOL
+
+
+def test_large_batch_spans_several_launches():
+    # more than 4096 sequences: the library splits the batch into launches
+    lens = np.random.default_rng(24).integers(1, 80, size=4500)
+    case = make_case(name="big_batch", seed=24, context_lens=lens, num_q_heads=2,
+                     num_kv_heads=1, head_dim=64, block_size=16, device=DEV)
+    out = gpu_decode(case)
+    torch.cuda.synchronize()
+    seqs = [0, 1, 4095, 4096, 4097, 4499]
+    err = max_abs_err(out.cpu().numpy()[seqs], oracle_decode(case, 0, seqs))
+    say(f"[decode] 4500 sequences: sampled max-abs err {err:.3e}")
+    assert err <= ATOL
