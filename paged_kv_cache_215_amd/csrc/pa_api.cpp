@@ -201,7 +201,8 @@ size_t pa_prefill_chunk_workspace_size(int32_t num_seqs, int32_t total_q, int32_
       !supported_block(block_size) || !supported_dim(head_dim) ||
       !supported_group(num_q_heads, num_kv_heads))
     return 0;
-  const int splits = pa::prefill_kv_splits(num_seqs, max_q_len, num_kv_heads, max_context_len);
+  const int splits = pa::prefill_kv_splits(num_seqs, max_q_len, num_q_heads, num_kv_heads, head_dim,
+                                             max_context_len);
   if (splits <= 1) return 0;
   const size_t rows = (size_t)total_q * num_q_heads * splits;
   return rows * head_dim * sizeof(float) + rows * 2 * sizeof(float);
@@ -239,7 +240,9 @@ pa_status_t pa_prefill_chunk(float* out, const void* query, const void* key_cach
 
   pa::PrefillArgs a;
   a.out = out;
-  a.kv_splits = pa::prefill_kv_splits(num_seqs, max_q_len, num_kv_heads, max_context_len);
+  a.xcd_remap = 1;
+  a.kv_splits = pa::prefill_kv_splits(num_seqs, max_q_len, num_q_heads, num_kv_heads, head_dim,
+                                             max_context_len);
   if (a.kv_splits < 1) a.kv_splits = 1;
   const size_t rows = (size_t)total_q * num_q_heads * a.kv_splits;
   a.part_o = need ? static_cast<float*>(workspace) : nullptr;

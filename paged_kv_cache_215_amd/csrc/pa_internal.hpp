@@ -76,6 +76,7 @@ struct PrefillArgs {
   int64_t num_blocks;
   int ctx_limit;
   int kv_splits;         // context splits per row tile (1 = no partials)
+  int xcd_remap;         // group workgroups of one (KV head, split) on one XCD
   float scale_log2;
 };
 
@@ -94,7 +95,8 @@ hipError_t launch_decode(const DecodeArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t stream);
 hipError_t launch_scatter(const ScatterArgs& a, hipStream_t stream);
 
-int prefill_kv_splits(int num_seqs, int max_q_len, int num_kv_heads, int max_context_len);
+int prefill_kv_splits(int num_seqs, int max_q_len, int num_q_heads, int num_kv_heads,
+                      int head_dim, int max_context_len);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
 }  // namespace pa

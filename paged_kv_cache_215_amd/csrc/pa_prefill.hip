@@ -31,6 +31,8 @@
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
 
+#include <cstdlib>
+
 namespace pa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -56,10 +58,11 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
   return (uint32_t)__builtin_bit_cast(unsigned short, static_cast<__bf16>(f));
 }
 
-template <int D, int G>
+template <int D, int G, int HPW>
 struct PrefillShape {
-  static constexpr int NW = G >= 4 ? G : 4;       // waves per workgroup
-  static constexpr int RT = NW / G;               // 16-row sub-tiles per workgroup
+  static constexpr int HG = G / HPW;              // head groups (waves across heads)
+  static constexpr int NW = HG >= 4 ? HG : 4;     // waves per workgroup
+  static constexpr int RT = NW / HG;              // 16-row sub-tiles per workgroup
   static constexpr int ROWS = 16 * RT;            // query rows per workgroup
   static constexpr int NT = NW * kWave;           // threads
   static constexpr int DCH = D / 8;               // 16-byte chunks per K/V row
@@ -68,17 +71,34 @@ struct PrefillShape {
   static constexpr int DTILES = D / 16;           // 16-row tiles of O^T
   static constexpr int KCHUNKS = kKeyTile * DCH;  // K chunks per tile
   static constexpr int VJOBS = (kKeyTile / 4) * (D / 8);  // 4-key x 8-dim V jobs
+  // K staging: TPR threads per key row, each loading KPT chunks of that row
+  static constexpr int TPR = (NT / kKeyTile) < DCH ? (NT / kKeyTile) : DCH;
+  static constexpr int KPT = DCH / TPR;
+  static constexpr int VPT = (VJOBS + NT - 1) / NT;       // V jobs per thread
 };
 
-template <int D, int G>
-__global__ __launch_bounds__((PrefillShape<D, G>::NT)) void prefill_kernel(PrefillArgs a) {
-  using S = PrefillShape<D, G>;
-  constexpr int DCH = S::DCH;
-  __shared__ uint4 k_lds[kKeyTile * DCH];                   // swizzled K rows
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D * kVtStride];  // V^T
+constexpr int kPfMaxBlocks = 1024;  // table entries one context split may span
 
-  const int row_tile = blockIdx.x, kvh = blockIdx.y;
-  const int seq = blockIdx.z / a.kv_splits, split = blockIdx.z % a.kv_splits;
+template <int D, int G, int HPW>
+__global__ __launch_bounds__((PrefillShape<D, G, HPW>::NT))
+__attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
+  using S = PrefillShape<D, G, HPW>;
+  constexpr int DCH = S::DCH;
+  __shared__ uint4 k_lds[2][kKeyTile * DCH];                          // swizzled K rows
+  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][D * kVtStride];  // V^T
+  __shared__ int s_bt[kPfMaxBlocks];
+
+  // XCD-aware order: the hardware deals consecutive workgroup ids to the 8
+  // XCDs in turn, so ids are regrouped so that all row tiles of one (KV head,
+  // split) run on one XCD and share its L2 copy of that split's K/V.
+  const int n_rt = gridDim.x;
+  const int total = n_rt * gridDim.y * gridDim.z;
+  int lin = blockIdx.x + n_rt * (blockIdx.y + gridDim.y * blockIdx.z);
+  if (a.xcd_remap && total % 8 == 0) lin = (lin % 8) * (total / 8) + lin / 8;
+  const int row_tile = lin % n_rt;
+  const int kvh = (lin / n_rt) % gridDim.y;
+  const int zz = lin / (n_rt * gridDim.y);
+  const int seq = zz / a.kv_splits, split = zz % a.kv_splits;
   const int q0 = a.cu_q_lens[seq];
   const int L = a.cu_q_lens[seq + 1] - q0;
   const int r0 = row_tile * S::ROWS;
@@ -94,18 +114,22 @@ __global__ __launch_bounds__((PrefillShape<D, G>::NT)) void prefill_kernel(Prefi
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
   const int lrow = lane % 16, lq = lane / 16;
-  const int head = kvh * G + wave % G;
-  const int rsub = wave / G;
+  // this wave: HPW query heads of the group, one 16-row sub-tile; every K/V
+  // operand read from LDS feeds one product per head
+  const int head0 = kvh * G + (wave % S::HG) * HPW;
+  const int rsub = wave / S::HG;
   const int my_row = r0 + rsub * 16 + lrow;          // chunk row of this lane's query
   const int qrow = my_row < L ? my_row : L - 1;       // clamp padding rows (not written)
 
-  // Q^T operand: query row my_row, dims 32*ks + 8*lq .. +8
-  bf16x8_t qop[S::KSTEPS];
-  {
-    const uint4* qp = reinterpret_cast<const uint4*>(a.query) +
-                      ((int64_t)(q0 + qrow) * a.num_q_heads + head) * DCH;
+  // Q^T operands: query row my_row, dims 32*ks + 8*lq .. +8, per head
+  bf16x8_t qop[HPW][S::KSTEPS];
 #pragma unroll
-    for (int ks = 0; ks < S::KSTEPS; ++ks) qop[ks] = __builtin_bit_cast(bf16x8_t, qp[4 * ks + lq]);
+  for (int hh = 0; hh < HPW; ++hh) {
+    const uint4* qp = reinterpret_cast<const uint4*>(a.query) +
+                      ((int64_t)(q0 + qrow) * a.num_q_heads + head0 + hh) * DCH;
+#pragma unroll
+    for (int ks = 0; ks < S::KSTEPS; ++ks)
+      qop[hh][ks] = __builtin_bit_cast(bf16x8_t, qp[4 * ks + lq]);
   }
 
   // Key range of this split: keys visible to some row of the workgroup.
@@ -120,167 +144,250 @@ __global__ __launch_bounds__((PrefillShape<D, G>::NT)) void prefill_kernel(Prefi
   const uint4* vcache = reinterpret_cast<const uint4*>(a.value_cache);
   const int64_t block_stride = (int64_t)a.num_kv_heads * bs * DCH;
   const int64_t head_off = (int64_t)kvh * bs * DCH;
-  const int32_t* bt = a.block_tables + (int64_t)seq * a.max_blocks_per_seq;
 
-  // Global chunk offset of key k's row, or -1 if the key is past the context
-  // or its table entry is outside the pool.
-  auto row_offset = [&](int k) -> int64_t {
-    if (k >= n) return -1;
-    const int e = bt[k >> bs_log2];
-    if (e < 0 || (int64_t)e >= a.num_blocks) return -1;
-    return (int64_t)e * block_stride + head_off + (int64_t)(k & (bs - 1)) * DCH;
+  // Table entries of the split's keys, staged once (-1: outside the pool).
+  const int blk_first = (kt_begin * kKeyTile) >> bs_log2;
+  {
+    const int key_end = min(kt_end * kKeyTile, n);
+    const int nblk = key_end > kt_begin * kKeyTile ? ((key_end + bs - 1) >> bs_log2) - blk_first : 0;
+    const int32_t* bt = a.block_tables + (int64_t)seq * a.max_blocks_per_seq + blk_first;
+    for (int i = tid; i < nblk && i < kPfMaxBlocks; i += S::NT) {
+      const int e = bt[i];
+      s_bt[i] = (e >= 0 && (int64_t)e < a.num_blocks) ? e : -1;
+    }
+  }
+  __syncthreads();
+
+  // Global chunk offset of key k's row. Keys past the context (and entries
+  // outside the pool) read block 0 instead: their scores are masked and
+  // their V rows zeroed, so the address only has to be valid.
+  auto row_base = [&](int k) -> int64_t {
+    const int i = (k >> bs_log2) - blk_first;
+    const int e = (k < n && i < kPfMaxBlocks) ? s_bt[i] : -1;  // split rule keeps i in range
+    return (int64_t)(e < 0 ? 0 : e) * block_stride + head_off + (int64_t)(k & (bs - 1)) * DCH;
   };
 
-  f32x4_t acc[S::DTILES];
+  // Tile staging, split in two so that the next tile's global loads are in
+  // flight while the current tile's products run: load_regs issues them,
+  // store_lds writes them (K swizzled, V transposed) into the other buffer.
+  // K: thread t stages chunks (t % TPR) + TPR * i of key row t / TPR.
+  // V: a job stages 4 consecutive keys (one block) x 8 dims.
+  const int k_row = tid / S::TPR, k_c0 = tid % S::TPR;
+  const bool k_active = k_row < kKeyTile;
+  uint4 kreg[S::KPT];
+  uint4 vreg[S::VPT][4];
+  auto load_regs = [&](int kt) {
+    const int key0 = kt * kKeyTile;
+    if (k_active) {
+      const uint4* src = kcache + row_base(key0 + k_row) + k_c0;
 #pragma unroll
-  for (int i = 0; i < S::DTILES; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;  // this lane's query row, log2 units
-  float l_part = 0.f;       // sum of this lane's rounded weights
+      for (int i = 0; i < S::KPT; ++i) kreg[i] = src[S::TPR * i];
+    }
+#pragma unroll
+    for (int j = 0; j < S::VPT; ++j) {
+      const int job = tid + j * S::NT;
+      if (job < S::VJOBS) {
+        const int kg = job % (kKeyTile / 4), dg = job / (kKeyTile / 4);
+        const uint4* src = vcache + row_base(key0 + 4 * kg) + dg;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vreg[j][r] = src[r * DCH];
+      }
+    }
+    if (key0 + kKeyTile > n) {  // tail tile: rows past the context may hold NaN
+#pragma unroll
+      for (int j = 0; j < S::VPT; ++j) {
+        const int job = tid + j * S::NT;
+        const int kg = job % (kKeyTile / 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (key0 + 4 * kg + r >= n) vreg[j][r] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto store_lds = [&](int buf) {
+    // K: chunk c of row r lives at c ^ (r & SWZ), so the 16 rows one MFMA
+    // operand read touches fall in distinct banks
+    if (k_active) {
+#pragma unroll
+      for (int i = 0; i < S::KPT; ++i) {
+        const int c = k_c0 + S::TPR * i;
+        k_lds[buf][k_row * DCH + (c ^ (k_row & S::SWZ))] = kreg[i];
+      }
+    }
+    // V^T: each job transposes 4 keys x 8 dims
+#pragma unroll
+    for (int j = 0; j < S::VPT; ++j) {
+      const int job = tid + j * S::NT;
+      if (job < S::VJOBS) {
+        const int kg = job % (kKeyTile / 4), dg = job / (kKeyTile / 4);
+        const int slot = vt_slot(4 * kg);
+        const uint32_t* w0 = &vreg[j][0].x;
+        const uint32_t* w1 = &vreg[j][1].x;
+        const uint32_t* w2 = &vreg[j][2].x;
+        const uint32_t* w3 = &vreg[j][3].x;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          uint2 even, odd;  // dims 8*dg + 2c and 8*dg + 2c + 1, keys 4kg..4kg+3
+          even.x = pack_lo(w0[c], w1[c]);
+          even.y = pack_lo(w2[c], w3[c]);
+          odd.x = pack_hi(w0[c], w1[c]);
+          odd.y = pack_hi(w2[c], w3[c]);
+          const int d = 8 * dg + 2 * c;
+          *reinterpret_cast<uint2*>(&vt_lds[buf][d * kVtStride + slot]) = even;
+          *reinterpret_cast<uint2*>(&vt_lds[buf][(d + 1) * kVtStride + slot]) = odd;
+        }
+      }
+    }
+  };
 
+  f32x4_t acc[HPW][S::DTILES];
+  float m_run[HPW];   // this lane's query row, per head, log2 units
+  float l_part[HPW];  // sum of this lane's weights, per head
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+#pragma unroll
+    for (int i = 0; i < S::DTILES; ++i) acc[hh][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m_run[hh] = -INFINITY;
+    l_part[hh] = 0.f;
+  }
+
+  if (kt_begin < kt_end) {
+    load_regs(kt_begin);
+    store_lds(0);
+  }
+  __syncthreads();
   for (int kt = kt_begin; kt < kt_end; ++kt) {
     const int key0 = kt * kKeyTile;
-    __syncthreads();  // previous tile fully consumed
-    // ---- stage K (row-chunk swizzle: chunk c of row r lives at c ^ (r & SWZ),
-    // so the 16 rows one MFMA operand read touches fall in distinct banks)
-    for (int idx = tid; idx < S::KCHUNKS; idx += S::NT) {
-      const int r = idx / DCH, c = idx % DCH;
-      const int64_t off = row_offset(key0 + r);
-      const uint4 v = off >= 0 ? kcache[off + c] : make_uint4(0, 0, 0, 0);
-      k_lds[r * DCH + (c ^ (r & S::SWZ))] = v;
-    }
-    // ---- stage V^T: each job transposes 4 keys x 8 dims
-    for (int job = tid; job < S::VJOBS; job += S::NT) {
-      const int kg = job % (kKeyTile / 4), dg = job / (kKeyTile / 4);
-      uint4 rows[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t off = row_offset(key0 + 4 * kg + r);
-        rows[r] = off >= 0 ? vcache[off + dg] : make_uint4(0, 0, 0, 0);
-      }
-      const int slot = vt_slot(4 * kg);
-      const uint32_t* w0 = &rows[0].x;
-      const uint32_t* w1 = &rows[1].x;
-      const uint32_t* w2 = &rows[2].x;
-      const uint32_t* w3 = &rows[3].x;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        uint2 even, odd;  // dims 8*dg + 2c and 8*dg + 2c + 1, keys 4kg..4kg+3
-        even.x = pack_lo(w0[c], w1[c]);
-        even.y = pack_lo(w2[c], w3[c]);
-        odd.x = pack_hi(w0[c], w1[c]);
-        odd.y = pack_hi(w2[c], w3[c]);
-        const int d = 8 * dg + 2 * c;
-        *reinterpret_cast<uint2*>(&vt_lds[d * kVtStride + slot]) = even;
-        *reinterpret_cast<uint2*>(&vt_lds[(d + 1) * kVtStride + slot]) = odd;
-      }
-    }
-    __syncthreads();
+    const int buf = (kt - kt_begin) & 1;
+    const bool has_next = kt + 1 < kt_end;
+    if (has_next) load_regs(kt + 1);
 
-    // ---- S^T = K Q^T for keys key0..key0+31 (two 16-key halves)
-    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    // ---- S^T = K Q^T for keys key0..key0+31 (two 16-key halves), per head
+    f32x4_t s0[HPW], s1[HPW];
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      s0[hh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      s1[hh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
     for (int ks = 0; ks < S::KSTEPS; ++ks) {
       const int c = 4 * ks + lq;
       const bf16x8_t k0 =
-          __builtin_bit_cast(bf16x8_t, k_lds[lrow * DCH + (c ^ (lrow & S::SWZ))]);
+          __builtin_bit_cast(bf16x8_t, k_lds[buf][lrow * DCH + (c ^ (lrow & S::SWZ))]);
       const bf16x8_t k1 =
-          __builtin_bit_cast(bf16x8_t, k_lds[(16 + lrow) * DCH + (c ^ ((16 + lrow) & S::SWZ))]);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qop[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qop[ks], s1, 0, 0, 0);
-    }
-
-    // ---- scale and causal / context mask (lane: keys 4lq+i and 16+4lq+i)
-    float sv[8];
-    const int limit = base_pos + my_row;  // last key this row may see
+          __builtin_bit_cast(bf16x8_t, k_lds[buf][(16 + lrow) * DCH + (c ^ ((16 + lrow) & S::SWZ))]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sv[i] = s0[i] * a.scale_log2;
-      sv[4 + i] = s1[i] * a.scale_log2;
-    }
-    const bool diag = key0 + kKeyTile - 1 > base_pos + r0 || key0 + kKeyTile > n;
-    if (diag) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ka = key0 + 4 * lq + i, kb = key0 + 16 + 4 * lq + i;
-        sv[i] = (ka <= limit && ka < n) ? sv[i] : -INFINITY;
-        sv[4 + i] = (kb <= limit && kb < n) ? sv[4 + i] : -INFINITY;
+      for (int hh = 0; hh < HPW; ++hh) {
+        s0[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qop[hh][ks], s0[hh], 0, 0, 0);
+        s1[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qop[hh][ks], s1[hh], 0, 0, 0);
       }
     }
 
-    // ---- online softmax over this lane's query row
-    float mx = sv[0];
+    const int limit = base_pos + my_row;  // last key this row may see
+    const bool diag = key0 + kKeyTile - 1 > base_pos + r0 || key0 + kKeyTile > n;
+    bf16x8_t pop_hi[HPW], pop_lo[HPW];
 #pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
-    mx = fmaxf(mx, xor_lane<16>(mx));
-    mx = fmaxf(mx, xor_lane<32>(mx));
-    const float m_new = fmaxf(m_run, mx);
-    if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
-      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
-      l_part *= alpha;
+    for (int hh = 0; hh < HPW; ++hh) {
+      // ---- scale and causal / context mask (lane: keys 4lq+i and 16+4lq+i)
+      float sv[8];
 #pragma unroll
-      for (int i = 0; i < S::DTILES; ++i) acc[i] *= alpha;
-      m_run = m_new;
-    }
-    // Each weight p is carried as p_hi + p_lo, both BF16 (p_hi = RNE(p),
-    // p_lo = RNE(p - p_hi)): 16 significant bits instead of 8, so the PV
-    // product on the BF16 matrix cores keeps the weights' float32 accuracy to
-    // about 2^-17 relative. The running sum uses the same p_hi + p_lo.
-    const float moff = m_run == -INFINITY ? 0.f : m_run;
-    uint32_t ph[8], pl[8];
+      for (int i = 0; i < 4; ++i) {
+        sv[i] = s0[hh][i] * a.scale_log2;
+        sv[4 + i] = s1[hh][i] * a.scale_log2;
+      }
+      if (diag) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float pf = fast_exp2(sv[i] - moff);
-      ph[i] = bf16_bits_rne(pf);
-      const float hi = __uint_as_float(ph[i] << 16);
-      pl[i] = bf16_bits_rne(pf - hi);
-      l_part += hi + __uint_as_float(pl[i] << 16);
-    }
-    uint4 wh, wl;
-    wh.x = ph[0] | (ph[1] << 16);
-    wh.y = ph[2] | (ph[3] << 16);
-    wh.z = ph[4] | (ph[5] << 16);
-    wh.w = ph[6] | (ph[7] << 16);
-    wl.x = pl[0] | (pl[1] << 16);
-    wl.y = pl[2] | (pl[3] << 16);
-    wl.z = pl[4] | (pl[5] << 16);
-    wl.w = pl[6] | (pl[7] << 16);
-    const bf16x8_t pop_hi = __builtin_bit_cast(bf16x8_t, wh);
-    const bf16x8_t pop_lo = __builtin_bit_cast(bf16x8_t, wl);
+        for (int i = 0; i < 4; ++i) {
+          const int ka = key0 + 4 * lq + i, kb = key0 + 16 + 4 * lq + i;
+          sv[i] = (ka <= limit && ka < n) ? sv[i] : -INFINITY;
+          sv[4 + i] = (kb <= limit && kb < n) ? sv[4 + i] : -INFINITY;
+        }
+      }
 
-    // ---- O^T += V^T (P_hi + P_lo)^T
+      // ---- online softmax over this lane's query row
+      float mx = sv[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+      mx = fmaxf(mx, xor_lane<16>(mx));
+      mx = fmaxf(mx, xor_lane<32>(mx));
+      // Rescale only when some row's maximum grew by more than 2^8: the
+      // softmax does not depend on the offset subtracted, and weights of up
+      // to 2^8 are far from float32 / BF16 overflow. This keeps the rescale
+      // of the accumulators off almost every tile.
+      const float m_new = fmaxf(m_run[hh], mx);
+      if (__builtin_amdgcn_ballot_w64(m_new > m_run[hh] + 8.f) != 0) {
+        const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run[hh] - m_new);
+        l_part[hh] *= alpha;
+#pragma unroll
+        for (int i = 0; i < S::DTILES; ++i) acc[hh][i] *= alpha;
+        m_run[hh] = m_new;
+      }
+      // Each weight p is carried as p_hi + p_lo, both BF16 (p_hi = RNE(p),
+      // p_lo = RNE(p - p_hi)): 16 significant bits instead of 8, so the PV
+      // product on the BF16 matrix cores keeps the weights' float32 accuracy
+      // to about 2^-17 relative. The running sum uses the same p_hi + p_lo.
+      const float moff = m_run[hh] == -INFINITY ? 0.f : m_run[hh];
+      uint32_t ph[8], pl[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float pf = fast_exp2(sv[i] - moff);
+        ph[i] = bf16_bits_rne(pf);
+        const float hi = __uint_as_float(ph[i] << 16);
+        pl[i] = bf16_bits_rne(pf - hi);
+        l_part[hh] += hi + __uint_as_float(pl[i] << 16);
+      }
+      uint4 wh, wl;
+      wh.x = ph[0] | (ph[1] << 16);
+      wh.y = ph[2] | (ph[3] << 16);
+      wh.z = ph[4] | (ph[5] << 16);
+      wh.w = ph[6] | (ph[7] << 16);
+      wl.x = pl[0] | (pl[1] << 16);
+      wl.y = pl[2] | (pl[3] << 16);
+      wl.z = pl[4] | (pl[5] << 16);
+      wl.w = pl[6] | (pl[7] << 16);
+      pop_hi[hh] = __builtin_bit_cast(bf16x8_t, wh);
+      pop_lo[hh] = __builtin_bit_cast(bf16x8_t, wl);
+    }
+
+    // ---- O^T += V^T (P_hi + P_lo)^T, one V^T operand read for all heads
 #pragma unroll
     for (int dt = 0; dt < S::DTILES; ++dt) {
       const bf16x8_t vop = __builtin_bit_cast(
-          bf16x8_t, *reinterpret_cast<const uint4*>(&vt_lds[(16 * dt + lrow) * kVtStride + 8 * lq]));
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_hi, acc[dt], 0, 0, 0);
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_lo, acc[dt], 0, 0, 0);
+          bf16x8_t, *reinterpret_cast<const uint4*>(&vt_lds[buf][(16 * dt + lrow) * kVtStride + 8 * lq]));
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh) {
+        acc[hh][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_hi[hh], acc[hh][dt], 0, 0, 0);
+        acc[hh][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_lo[hh], acc[hh][dt], 0, 0, 0);
+      }
     }
+    if (has_next) store_lds(buf ^ 1);
+    __syncthreads();  // next buffer complete; this one free for reuse
   }
 
-  // ---- row totals and output
-  float l_row = l_part + xor_lane<16>(l_part);
-  l_row += xor_lane<32>(l_row);
-  if (my_row >= L) return;
-  const int64_t orow = (int64_t)(q0 + my_row) * a.num_q_heads + head;
-  if (a.kv_splits == 1) {
-    const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
-    float4* o = reinterpret_cast<float4*>(a.out + orow * D);
+  // ---- row totals and output, per head
 #pragma unroll
-    for (int dt = 0; dt < S::DTILES; ++dt)
-      o[4 * dt + lq] = make_float4(acc[dt][0] * inv, acc[dt][1] * inv, acc[dt][2] * inv,
-                                   acc[dt][3] * inv);
-  } else {
-    const int64_t slot = orow * a.kv_splits + split;
+  for (int hh = 0; hh < HPW; ++hh) {
+    float l_row = l_part[hh] + xor_lane<16>(l_part[hh]);
+    l_row += xor_lane<32>(l_row);
+    if (my_row >= L) continue;
+    const int64_t orow = (int64_t)(q0 + my_row) * a.num_q_heads + head0 + hh;
     const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
-    float4* o = reinterpret_cast<float4*>(a.part_o + slot * D);
-#pragma unroll
-    for (int dt = 0; dt < S::DTILES; ++dt)
-      o[4 * dt + lq] = make_float4(acc[dt][0] * inv, acc[dt][1] * inv, acc[dt][2] * inv,
-                                   acc[dt][3] * inv);
-    if (lq == 0) {
-      a.part_ml[2 * slot] = m_run;
-      a.part_ml[2 * slot + 1] = l_row;
+    float* dst;
+    if (a.kv_splits == 1) {
+      dst = a.out + orow * D;
+    } else {
+      const int64_t slot = orow * a.kv_splits + split;
+      dst = a.part_o + slot * D;
+      if (lq == 0) {
+        a.part_ml[2 * slot] = m_run[hh];
+        a.part_ml[2 * slot + 1] = l_row;
+      }
     }
+    float4* o = reinterpret_cast<float4*>(dst);
+#pragma unroll
+    for (int dt = 0; dt < S::DTILES; ++dt)
+      o[4 * dt + lq] = make_float4(acc[hh][dt][0] * inv, acc[hh][dt][1] * inv,
+                                   acc[hh][dt][2] * inv, acc[hh][dt][3] * inv);
   }
 }
 
@@ -316,23 +423,61 @@ __global__ __launch_bounds__(kWave) void prefill_merge_kernel(PrefillArgs a) {
 // ---------------------------------------------------------------------------
 // Host side.
 
-int prefill_kv_splits(int num_seqs, int max_q_len, int num_kv_heads, int max_context_len) {
-  // Split the keys of each row tile until the launch has about two
-  // workgroups per CU, keeping at least 8 key tiles per split.
-  const int rows = 16;  // the smallest row tile (group size 4 or 8)
+// Heads of a GQA group one wave holds (the environment override exists for
+// tuning sweeps only).
+int prefill_heads_per_wave(int group) {
+  static const int want = [] {
+    const char* s = std::getenv("PA_PREFILL_HPW");
+    const int v = s ? std::atoi(s) : 0;
+    return v == 1 || v == 2 || v == 4 ? v : 1;
+  }();
+  int h = want < group ? want : group;
+  return h < 1 ? 1 : h;
+}
+
+int prefill_rows_per_workgroup(int group, int head_dim) {
+  int hpw = prefill_heads_per_wave(group);
+  if (head_dim > 128 && hpw > 2) hpw = 2;
+  const int hg = group / hpw;
+  const int nw = hg >= 4 ? hg : 4;
+  return 16 * (nw / hg);
+}
+
+int prefill_kv_splits(int num_seqs, int max_q_len, int num_q_heads, int num_kv_heads,
+                      int head_dim, int max_context_len) {
+  // Split the keys of each row tile until the launch has about one
+  // workgroup per CU, keeping at least 8 key tiles per split.
+  const int rows = prefill_rows_per_workgroup(num_q_heads / num_kv_heads, head_dim);
   const int64_t wgs = (int64_t)num_seqs * num_kv_heads * ((max_q_len + rows - 1) / rows);
+  static const int target = [] {
+    const char* s = std::getenv("PA_PREFILL_TARGET_WGS");
+    const int v = s ? std::atoi(s) : 0;
+    return v > 0 ? v : 512;
+  }();
   int splits = 1;
-  while (splits < 8 && wgs * splits < 512 &&
+  while (splits < 8 && wgs * splits < target &&
          (max_context_len / kKeyTile) / (2 * splits) >= 8)
     splits *= 2;
+  // each split's keys must fit the staged table: a split spans at most
+  // max_context_len / splits + 64 keys (tile rounding), i.e. at most
+  // (kPfMaxBlocks - 8) * 16 + 64 keys, which touch at most kPfMaxBlocks - 2
+  // blocks of 16 tokens
+  const int64_t span = (int64_t)(kPfMaxBlocks - 8) * 16;
+  while ((int64_t)splits * span < max_context_len) ++splits;
   return splits;
 }
 
-template <int D, int G>
-static hipError_t launch_pf(const PrefillArgs& a, hipStream_t stream) {
-  using S = PrefillShape<D, G>;
+template <int D, int G, int HPW>
+static hipError_t launch_pf(const PrefillArgs& a_in, hipStream_t stream) {
+  static const int remap = [] {
+    const char* s = std::getenv("PA_PREFILL_XCD");
+    return s ? std::atoi(s) : 1;
+  }();
+  PrefillArgs a = a_in;
+  a.xcd_remap = remap;
+  using S = PrefillShape<D, G, HPW>;
   dim3 grid((a.max_q_len + S::ROWS - 1) / S::ROWS, a.num_kv_heads, a.num_seqs * a.kv_splits);
-  hipLaunchKernelGGL((prefill_kernel<D, G>), grid, dim3(S::NT), 0, stream, a);
+  hipLaunchKernelGGL((prefill_kernel<D, G, HPW>), grid, dim3(S::NT), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.kv_splits == 1) return err;
   hipLaunchKernelGGL((prefill_merge_kernel<D>), dim3(a.num_q_heads, a.total_q), dim3(kWave), 0,
@@ -340,13 +485,25 @@ static hipError_t launch_pf(const PrefillArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D, int G>
+static hipError_t launch_ph(const PrefillArgs& a, hipStream_t stream) {
+  const int hpw = prefill_heads_per_wave(G);
+  if constexpr (G >= 4 && D <= 128) {  // four heads of d = 256 exceed the register file
+    if (hpw == 4) return launch_pf<D, G, 4>(a, stream);
+  }
+  if constexpr (G >= 2) {
+    if (hpw == 2) return launch_pf<D, G, 2>(a, stream);
+  }
+  return launch_pf<D, G, 1>(a, stream);
+}
+
 template <int D>
 static hipError_t launch_pg(const PrefillArgs& a, hipStream_t stream) {
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: return launch_pf<D, 1>(a, stream);
-    case 2: return launch_pf<D, 2>(a, stream);
-    case 4: return launch_pf<D, 4>(a, stream);
-    case 8: return launch_pf<D, 8>(a, stream);
+    case 1: return launch_ph<D, 1>(a, stream);
+    case 2: return launch_ph<D, 2>(a, stream);
+    case 4: return launch_ph<D, 4>(a, stream);
+    case 8: return launch_ph<D, 8>(a, stream);
   }
   return hipErrorInvalidValue;
 }
