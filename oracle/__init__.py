@@ -20,6 +20,10 @@ definitions state:
 * ``accounting``                      - KV footprint closed form and slot
                                         accounting for paged vs contiguous
                                         allocation.
+* ``fp8``                             - E4M3 code values, the saturating
+                                        round-to-nearest-even quantizer with
+                                        per-head scales, FP8 scatter and decode
+                                        on the dequantized cache.
 
 Pins (checked by ``tests/test_oracle*.py`` with ``-m "not gpu"``): dense
 brute force, closed forms (n = 1, uniform keys, two-token softmax, GQA head
@@ -35,6 +39,7 @@ from .accounting import (  # noqa: F401
     kv_bytes,
     paged_slots,
 )
+from . import fp8  # noqa: F401
 from .dense_ref import dense_attention_ref  # noqa: F401
 from .numerics import bf16_bits_to_f64, to_f64  # noqa: F401
 from .paged_ref import decode_ref, prefill_chunk_ref, reshape_and_cache_ref  # noqa: F401
