@@ -25,6 +25,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -46,10 +47,12 @@ def log(msg):
 
 
 def decode_bytes(layout, num_decode, num_q_heads, num_kv_heads, head_dim, elem_bytes,
-                 unique_blocks=False):
+                 unique_blocks=False, kv_bytes=None):
     """Algorithmic bytes of one pa_decode call: K+V rows of every attended
     token (each distinct physical block once when unique_blocks), q, float32
-    out and the block-table entries in use."""
+    out and the block-table entries in use. kv_bytes is the cache's element
+    size when it differs from the query's (FP8: 1 byte per element, plus the
+    two per-head float32 scale arrays)."""
     lens = layout.context_lens[:num_decode].astype(np.int64)
     bs = layout.block_size
     nblk = -(-lens // bs)
@@ -64,18 +67,24 @@ def decode_bytes(layout, num_decode, num_q_heads, num_kv_heads, head_dim, elem_b
         kv_tokens = sum(seen.values())
     else:
         kv_tokens = int(lens.sum())
-    kv = 2 * kv_tokens * num_kv_heads * head_dim * elem_bytes
+    kv = 2 * kv_tokens * num_kv_heads * head_dim * (elem_bytes if kv_bytes is None else kv_bytes)
+    scales = 0 if kv_bytes is None else 2 * num_kv_heads * 4
     q = num_decode * num_q_heads * head_dim * elem_bytes
     out = num_decode * num_q_heads * head_dim * 4
     bt = int(nblk.sum()) * 4
-    return kv + q + out + bt
+    return kv + scales + q + out + bt
 
 
 def source_hash(paths):
+    """Hash of the sources' code: comments and blank space are dropped, so a
+    comment edit keeps the counters that were taken on the same kernel."""
     h = hashlib.sha256()
     for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
@@ -108,13 +117,16 @@ def _cpu_arr(name):
 
 
 def _cpu_worker(args):
-    layer, b, scale = args
+    layer, b, scale, fp8 = args
     import oracle  # the oracle is used here only, to time it
     q = _cpu_arr(f"q{layer}")
     kc = _cpu_arr(f"kc{layer}")
     vc = _cpu_arr(f"vc{layer}")
     bt = _cpu_arr("bt")
     lens = _cpu_arr("lens")
+    if fp8:
+        return oracle.fp8.decode_fp8_ref(q[b:b + 1], kc, vc, _cpu_arr(f"ks{layer}"),
+                                         _cpu_arr(f"vs{layer}"), bt[b:b + 1], lens[b:b + 1], scale)
     return oracle.decode_ref(q[b:b + 1], kc, vc, bt[b:b + 1], lens[b:b + 1], scale)
 
 
@@ -135,6 +147,9 @@ def cpu_baseline(case, layers, seq_layers_per_step):
             np.save(os.path.join(folder, f"q{layer}.npy"), to_numpy_bits(case.queries[layer]))
             np.save(os.path.join(folder, f"kc{layer}.npy"), to_numpy_bits(case.key_caches[layer]))
             np.save(os.path.join(folder, f"vc{layer}.npy"), to_numpy_bits(case.value_caches[layer]))
+            if case.kv_fp8:
+                np.save(os.path.join(folder, f"ks{layer}.npy"), case.k_scales[layer].cpu().numpy())
+                np.save(os.path.join(folder, f"vs{layer}.npy"), case.v_scales[layer].cpu().numpy())
         try:
             cores = len(os.sched_getaffinity(0))
         except AttributeError:
@@ -148,9 +163,9 @@ def cpu_baseline(case, layers, seq_layers_per_step):
             ctx = get_context("spawn")
             with ctx.Pool(workers, initializer=_cpu_worker_init, initargs=(folder,)) as pool:
                 # warm every worker (imports, page cache) outside the timed region
-                pool.map(_cpu_worker, [(layers[0], b % S, case.scale) for b in range(workers)],
-                         chunksize=1)
-                tasks = [(layer, b, case.scale) for layer in layers for b in range(S)]
+                pool.map(_cpu_worker, [(layers[0], b % S, case.scale, case.kv_fp8)
+                                       for b in range(workers)], chunksize=1)
+                tasks = [(layer, b, case.scale, case.kv_fp8) for layer in layers for b in range(S)]
                 t0 = time.perf_counter()
                 pool.map(_cpu_worker, tasks, chunksize=1)
                 wall = time.perf_counter() - t0
@@ -179,8 +194,11 @@ def run(args):
     pa.lib()                                   # fail loudly if the library is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    log(f"[bench] generating {args.workload} ...")
-    case = make_config_case(args.workload, device=dev)
+    fp8 = args.kv == "fp8"
+    if fp8 and args.workload == "c5_mixed_step":
+        raise SystemExit("the prefill chunk reads BF16 caches only: no FP8 line for c5_mixed_step")
+    log(f"[bench] generating {args.workload} (kv {args.kv}) ...")
+    case = make_config_case(args.workload, device=dev, kv_fp8=fp8)
     torch.cuda.synchronize()
     L = case.num_layers
     S = case.num_decode_seqs
@@ -211,16 +229,33 @@ def run(args):
         e1.record(stream)
         events.append((e0, e1))
 
+    def write(layer):
+        if fp8:
+            pa.pa_reshape_and_cache_fp8(case.new_keys[layer], case.new_values[layer],
+                                        case.key_caches[layer], case.value_caches[layer],
+                                        case.slot_mapping, case.k_scales[layer],
+                                        case.v_scales[layer])
+        else:
+            pa.pa_reshape_and_cache(case.new_keys[layer], case.new_values[layer],
+                                    case.key_caches[layer], case.value_caches[layer],
+                                    case.slot_mapping)
+
+    def attend(layer):
+        if fp8:
+            pa.pa_decode_fp8(case.queries[layer], case.key_caches[layer], case.value_caches[layer],
+                             case.k_scales[layer], case.v_scales[layer], case.block_tables,
+                             case.context_lens, case.scale, case.max_context_len,
+                             out=outs[layer], workspace=workspace)
+        else:
+            pa.pa_decode(case.queries[layer], case.key_caches[layer], case.value_caches[layer],
+                         case.block_tables, case.context_lens, case.scale, case.max_context_len,
+                         out=outs[layer], workspace=workspace)
+
     def step(dec_events=None, pf_events=None):
         for layer in range(L):
             if case.slot_mapping is not None:
-                pa.pa_reshape_and_cache(case.new_keys[layer], case.new_values[layer],
-                                        case.key_caches[layer], case.value_caches[layer],
-                                        case.slot_mapping)
-            timed(dec_events, lambda: pa.pa_decode(
-                case.queries[layer], case.key_caches[layer], case.value_caches[layer],
-                case.block_tables, case.context_lens, case.scale, case.max_context_len,
-                out=outs[layer], workspace=workspace))
+                write(layer)
+            timed(dec_events, lambda: attend(layer))
             if pf is not None:
                 timed(pf_events, lambda: pa.pa_prefill_chunk(
                     pf.query, case.key_caches[layer], case.value_caches[layer], pf.block_tables,
@@ -241,7 +276,7 @@ def run(args):
 
     unique = args.workload == "c4_grpo_cow"
     bytes_call = decode_bytes(case.layout, S, case.num_q_heads, case.num_kv_heads, case.head_dim,
-                              elem, unique_blocks=unique)
+                              elem, unique_blocks=unique, kv_bytes=1 if fp8 else None)
     achieved_gbs = bytes_call / avg_decode_s / 1e9
     ms_per_step = elapsed / args.steps * 1e3
     tokens_per_s = S * args.steps / elapsed
@@ -249,7 +284,7 @@ def run(args):
         f"{tokens_per_s:.1f} tok/s; pa_decode avg {avg_decode_s * 1e6:.1f} us "
         f"(min {min(decode_ms) * 1e3:.1f}, max {max(decode_ms) * 1e3:.1f}), "
         f"{achieved_gbs:.1f} GB/s = {achieved_gbs / HBM_PEAK_GBS:.3f} of HBM peak")
-    traffic = load_traffic() if args.workload == "c3_full_step" else None
+    traffic = load_traffic() if args.workload == "c3_full_step" and not fp8 else None
 
     result = {
         "metric": "paged-attn decode tokens/s & achieved HBM GB/s (% of 8 TB/s), 1 MI355X",
@@ -262,7 +297,7 @@ def run(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if elem == 2 else "f32",
+        "dtype": ("fp8_e4m3 kv, bf16 q" if fp8 else "bf16") if elem == 2 else "f32",
         "data": "synthetic",
         "config": {
             "workload": args.workload,
@@ -273,10 +308,13 @@ def run(args):
             "num_kv_heads": case.num_kv_heads,
             "head_dim": case.head_dim,
             "block_size": case.block_size,
-            "step": "per layer: pa_reshape_and_cache(new token) + pa_decode",
+            "kv_cache": "fp8_e4m3 (per-head scales)" if fp8 else "bf16",
+            "step": ("per layer: pa_reshape_and_cache_fp8(new token) + pa_decode_fp8" if fp8 else
+                     "per layer: pa_reshape_and_cache(new token) + pa_decode"),
         },
         "roofline": {
-            "kernel": "pa_decode (decode_partition_kernel + decode_merge_kernel)",
+            "kernel": ("pa_decode_fp8" if fp8 else "pa_decode") +
+                      " (decode_partition_kernel + decode_merge_kernel)",
             "bound": "hbm",
             "achieved": round(achieved_gbs, 1),
             "peak": HBM_PEAK_GBS,
@@ -314,7 +352,8 @@ def run(args):
             "unit": "tokens/s",
             "cores": cb["workers"],
             "kind": "oracle",
-            "sample": f"fp64 oracle decode_ref on all {S} sequences of {len(layers)} of the {L} "
+            "sample": f"fp64 oracle {'decode_fp8_ref' if fp8 else 'decode_ref'} on all {S} "
+                      f"sequences of {len(layers)} of the {L} "
                       f"layers ({cb['tasks']} of {S * L} sequence-layers per step; "
                       f"{cb['wall_s']:.2f} s wall on {cb['workers']} worker processes), "
                       f"scaled to a full step",
@@ -344,6 +383,9 @@ PROFILE_COMMANDS = {
     "kt_c5": "cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats --output-format csv "
              "-d <out>/kt_c5 -o kt -- python3 <repo>/bench.py --workload c5_mixed_step "
              "--steps 5 --warmup 1 --no-cpu-baseline",
+    "kt_c3_fp8": "cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats --output-format csv "
+                 "-d <out>/kt_c3_fp8 -o kt -- python3 <repo>/bench.py --kv fp8 --steps 5 "
+                 "--warmup 1 --no-cpu-baseline",
     "pmc_fetch_c3": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/pmc_fetch_c3 -o p -- "
                     "python3 <repo>/bench.py --steps 2 --warmup 1 --no-cpu-baseline",
     "pmc_write_c3": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/pmc_write_c3 -o p -- "
@@ -388,8 +430,12 @@ def summarize_profiles(src, dst):
     """Turn rocprofv3 CSV output (folders named as in PROFILE_COMMANDS) into
     the short text summaries kept under profiles/."""
     os.makedirs(dst, exist_ok=True)
+    names = {"kt_c3": "decode_c3_kernel_trace.md", "kt_c5": "mixed_c5_kernel_trace.md",
+             "kt_c3_fp8": "decode_fp8_c3_kernel_trace.md"}
     for tag, title in (("kt_c3", "pa kernels, 64 seqs x 8192 ctx x 16 layers (bs 32)"),
-                       ("kt_c5", "pa kernels, mixed step: 255 decode seqs + 512-row prefill chunk")):
+                       ("kt_c5", "pa kernels, mixed step: 255 decode seqs + 512-row prefill chunk"),
+                       ("kt_c3_fp8", "pa kernels, FP8 E4M3 cache, 64 seqs x 8192 ctx x 16 layers "
+                                     "(bs 32)")):
         folder = os.path.join(src, tag)
         if not os.path.isdir(folder):
             continue
@@ -405,7 +451,7 @@ def summarize_profiles(src, dst):
                          f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
         lines.append("")
         lines.append("Kernels not listed are torch's input generation (outside the timed steps).")
-        name = "decode_c3_kernel_trace.md" if tag == "kt_c3" else "mixed_c5_kernel_trace.md"
+        name = names[tag]
         with open(os.path.join(dst, name), "w") as f:
             f.write("\n".join(lines) + "\n")
         log(f"wrote {name}")
@@ -467,6 +513,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c3_full_step",
                     choices=["c2_layer_decode", "c3_full_step", "c4_grpo_cow", "c5_mixed_step"])
+    ap.add_argument("--kv", choices=["bf16", "fp8"], default="bf16",
+                    help="KV cache element type (fp8: E4M3 codes with per-head scales)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-layers", type=int, default=4)
     ap.add_argument("--copy-calib", action="store_true",

@@ -46,7 +46,8 @@
  *                       group size not 1/2/4/8, or a dtype the entry point
  *                       does not take
  *   PA_ERR_ALIGN        a tensor or workspace pointer is not 16-byte aligned,
- *                       or an index array is not aligned to its element size
+ *                       or an index or scale array is not aligned to its
+ *                       element size
  *   PA_ERR_WORKSPACE    the workspace is smaller than the size query returns
  *   PA_ERR_HIP          a kernel launch failed (hipGetLastError after launch)
  * Device-resident values (table entries, lengths, slots) are not checked on
@@ -150,6 +151,57 @@ pa_status_t pa_decode(float* out, const void* query,
                       int64_t num_blocks, int32_t max_context_len,
                       float scale, pa_dtype_t dtype,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * FP8 KV cache. Quantizing the cache to FP8 halves the bytes every decode
+ * step re-reads, which the pages count as doubling the effective memory
+ * bandwidth (vLLM architecture, memory and benchmarks deep dive,
+ * "Hardware-level optimizations"). They fix no format; the one used here:
+ *   codes     OCP E4M3: 1 sign, 4 exponent bits (bias 7), 3 mantissa bits;
+ *             exponent 0 is subnormal (m/8 * 2^-6); no infinities;
+ *             S.1111.111 is NaN; largest magnitude 448. One byte per element,
+ *             same cache layout as above.
+ *   scales    float32 device arrays k_scale, v_scale [num_kv_heads]: the value
+ *             of K code c of head h is E4M3(c) * k_scale[h] (V likewise).
+ *             They must be positive and finite (not checked: device memory).
+ *
+ * pa_reshape_and_cache_fp8: the scatter above, writing codes
+ *   code = E4M3(x / scale[h])
+ * with x widened to float32 and divided in IEEE float32, rounded to nearest
+ * with ties to even, magnitudes above 448 (infinity included) saturated to
+ * +-448, NaN kept as NaN with its sign, the sign of zero kept.
+ *   key, value   [num_tokens, num_kv_heads, head_dim], src_dtype F32 or BF16
+ *   key_cache, value_cache  uint8 codes [num_blocks, num_kv_heads, block_size, head_dim]
+ */
+pa_status_t pa_reshape_and_cache_fp8(const void* key, const void* value,
+                                     void* key_cache, void* value_cache,
+                                     const int64_t* slot_mapping,
+                                     const float* k_scale, const float* v_scale,
+                                     int32_t num_tokens, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t block_size,
+                                     int64_t num_blocks, pa_dtype_t src_dtype,
+                                     void* stream);
+
+/*
+ * pa_decode over an FP8 cache: the attention of pa_decode with k_j and v_j
+ * the dequantized rows (code value times the head's scale). The products
+ * q . k_j are exact in float32 (E4M3 values are BF16 values), so the result
+ * differs from pa_decode on the dequantized cache only by float32 rounding.
+ * The workspace is the one pa_decode_workspace_size / pa_decode_workspace_init
+ * describe for the same sizes (the two entry points may share it in stream
+ * order).
+ * query_dtype: PA_DTYPE_BF16 only.
+ */
+pa_status_t pa_decode_fp8(float* out, const void* query,
+                          const void* key_cache, const void* value_cache,
+                          const float* k_scale, const float* v_scale,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          int32_t num_seqs, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int32_t max_blocks_per_seq,
+                          int64_t num_blocks, int32_t max_context_len,
+                          float scale, pa_dtype_t query_dtype,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Bytes of device workspace pa_prefill_chunk needs for these sizes; may be 0.

@@ -9,7 +9,10 @@ HIP kernels behind the C ABI in ``include/pa.h``:
                              paged context, split over the context with a
                              separate merge kernel;
 * ``pa_prefill_chunk``     - a causal query chunk against the paged cache on
-                             the matrix cores.
+                             the matrix cores;
+* ``pa_reshape_and_cache_fp8`` / ``pa_decode_fp8`` - the same scatter and
+                             decode over an FP8 (E4M3) cache with one scale
+                             per KV head for K and for V.
 
 The Python functions below only marshal torch tensors to that ABI.
 """
@@ -23,9 +26,11 @@ from ._lib import (  # noqa: F401
     lib,
     decode_workspace,
     pa_decode,
+    pa_decode_fp8,
     pa_decode_workspace_init,
     pa_decode_workspace_size,
     pa_prefill_chunk,
     pa_prefill_chunk_workspace_size,
     pa_reshape_and_cache,
+    pa_reshape_and_cache_fp8,
 )

@@ -32,6 +32,10 @@ SIGNATURES = {
     "pa_decode_workspace_init": (_i32, [_vp, _sz, _vp]),
     "pa_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
                          _i32, _f32, _i32, _vp, _sz, _vp]),
+    "pa_reshape_and_cache_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                        _i64, _i32, _vp]),
+    "pa_decode_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                             _i32, _i64, _i32, _f32, _i32, _vp, _sz, _vp]),
     "pa_prefill_chunk_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_prefill_chunk": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                 _i32, _i32, _i32, _i64, _i32, _f32, _i32, _vp, _sz, _vp]),
@@ -159,6 +163,65 @@ def pa_decode(query, key_cache, value_cache, block_tables, context_lens, scale,
         _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
         _ptr(context_lens), num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
         block_tables.shape[1], num_blocks, int(max_context_len), float(scale),
+        _dtype_code(query), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return out
+
+
+def _fp8_cache(t):
+    if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise TypeError("an FP8 cache holds E4M3 codes (uint8 or float8_e4m3fn)")
+
+
+def _scales(*ts):
+    for t in ts:
+        if t.dtype != torch.float32:
+            raise TypeError("FP8 scales are float32 [num_kv_heads]")
+
+
+def pa_reshape_and_cache_fp8(key, value, key_cache, value_cache, slot_mapping, k_scale, v_scale):
+    """Quantize token t's K/V rows to E4M3 with per-head scales and write them
+    into slot slot_mapping[t] of the FP8 caches (in place)."""
+    dev = _dev(key, value, key_cache, value_cache, slot_mapping, k_scale, v_scale)
+    if slot_mapping.dtype != torch.int64:
+        raise TypeError("slot_mapping must be int64")
+    _fp8_cache(key_cache)
+    _fp8_cache(value_cache)
+    _scales(k_scale, v_scale)
+    if key.dtype != value.dtype:
+        raise TypeError("key and value dtypes must match")
+    num_tokens, num_kv_heads, head_dim = key.shape
+    num_blocks, _, block_size, _ = key_cache.shape
+    if k_scale.numel() != num_kv_heads or v_scale.numel() != num_kv_heads:
+        raise ValueError("one scale per KV head")
+    _check("pa_reshape_and_cache_fp8", lib().pa_reshape_and_cache_fp8(
+        _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache), _ptr(slot_mapping),
+        _ptr(k_scale), _ptr(v_scale), num_tokens, num_kv_heads, head_dim, block_size,
+        num_blocks, _dtype_code(key), _stream(dev)))
+
+
+def pa_decode_fp8(query, key_cache, value_cache, k_scale, v_scale, block_tables, context_lens,
+                  scale, max_context_len, out=None, workspace=None):
+    """Decode attention over an FP8 (E4M3) paged cache; returns float32 [S, Hq, d]."""
+    dev = _dev(query, key_cache, value_cache, k_scale, v_scale, block_tables, context_lens)
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    _fp8_cache(key_cache)
+    _fp8_cache(value_cache)
+    _scales(k_scale, v_scale)
+    num_seqs, num_q_heads, head_dim = query.shape
+    num_blocks, num_kv_heads, block_size, _ = key_cache.shape
+    if k_scale.numel() != num_kv_heads or v_scale.numel() != num_kv_heads:
+        raise ValueError("one scale per KV head")
+    if out is None:
+        out = torch.empty((num_seqs, num_q_heads, head_dim), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = decode_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                     max_context_len, dev)
+    _dev(out, workspace)
+    _check("pa_decode_fp8", lib().pa_decode_fp8(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_tables), _ptr(context_lens), num_seqs, num_q_heads, num_kv_heads, head_dim,
+        block_size, block_tables.shape[1], num_blocks, int(max_context_len), float(scale),
         _dtype_code(query), _ptr(workspace), workspace.numel(), _stream(dev)))
     return out
 

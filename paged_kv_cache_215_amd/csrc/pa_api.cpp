@@ -82,6 +82,69 @@ DecodeGeometry decode_geometry(int32_t num_seqs, int32_t hq, int32_t hkv, int32_
 
 pa_status_t from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
+// Validation (NULL -> SHAPE -> UNSUPPORTED -> ALIGN -> WORKSPACE) and launch of
+// a decode over a cache of type kv. type_ok is the caller's check of its
+// element types (reported as UNSUPPORTED); an FP8 cache also needs its two
+// scale arrays.
+pa_status_t decode_impl(float* out, const void* query, const void* key_cache,
+                        const void* value_cache, const float* k_scale, const float* v_scale,
+                        const int32_t* block_tables, const int32_t* context_lens,
+                        int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                        int64_t num_blocks, int32_t max_context_len, float scale, pa::KvType kv,
+                        bool type_ok, void* workspace, size_t workspace_bytes, void* stream) {
+  const bool scaled = kv == pa::KvType::FP8;
+  if (num_seqs < 0) return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens ||
+      !workspace || (scaled && (!k_scale || !v_scale)))
+    return PA_ERR_NULL;
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      max_blocks_per_seq <= 0 || num_blocks <= 0 || max_context_len < 0 ||
+      num_q_heads % num_kv_heads != 0 || !std::isfinite(scale))
+    return PA_ERR_SHAPE;
+  if (!supported_block(block_size) || !supported_dim(head_dim) ||
+      !supported_group(num_q_heads, num_kv_heads) || !type_ok)
+    return PA_ERR_UNSUPPORTED;
+  if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) ||
+      !aligned(value_cache, 16) || !aligned(workspace, 16) || !aligned(block_tables, 4) ||
+      !aligned(context_lens, 4) || (scaled && (!aligned(k_scale, 4) || !aligned(v_scale, 4))))
+    return PA_ERR_ALIGN;
+  const DecodeGeometry geo = decode_geometry(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                             block_size, max_context_len);
+  if (workspace_bytes < geo.bytes) return PA_ERR_WORKSPACE;
+
+  pa::DecodeArgs a;
+  char* ws = static_cast<char*>(workspace);
+  a.out = out;
+  a.plan = reinterpret_cast<pa::DecodePlan*>(ws);
+  a.plan_cus = 0;
+  a.plan_units_per_cu = 0;
+  a.part_o = reinterpret_cast<float*>(ws + geo.part_o_off);
+  a.part_ml = reinterpret_cast<float*>(ws + geo.part_ml_off);
+  a.query = query;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size_log2 = log2_exact(block_size);
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.ctx_limit = ctx_limit(max_context_len, max_blocks_per_seq, block_size);
+  a.part_floor = geo.launch.part_floor;
+  a.part_cap = geo.launch.part_cap;
+  a.waves = geo.launch.waves;
+  a.max_parts = geo.launch.max_parts;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  return from_hip(pa::launch_decode(a, kv, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -116,6 +179,42 @@ pa_status_t pa_reshape_and_cache(const void* key, const void* value, void* key_c
   return from_hip(pa::launch_scatter(a, static_cast<hipStream_t>(stream)));
 }
 
+pa_status_t pa_reshape_and_cache_fp8(const void* key, const void* value, void* key_cache,
+                                     void* value_cache, const int64_t* slot_mapping,
+                                     const float* k_scale, const float* v_scale,
+                                     int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t block_size, int64_t num_blocks,
+                                     pa_dtype_t src_dtype, void* stream) {
+  if (num_tokens < 0) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping || !k_scale || !v_scale)
+    return PA_ERR_NULL;
+  if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return PA_ERR_SHAPE;
+  if (!supported_block(block_size) || !supported_dim(head_dim) ||
+      (src_dtype != PA_DTYPE_F32 && src_dtype != PA_DTYPE_BF16))
+    return PA_ERR_UNSUPPORTED;
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(key_cache, 16) ||
+      !aligned(value_cache, 16) || !aligned(slot_mapping, 8) || !aligned(k_scale, 4) ||
+      !aligned(v_scale, 4))
+    return PA_ERR_ALIGN;
+  pa::ScatterFp8Args a;
+  a.key = key;
+  a.value = value;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.slot_mapping = slot_mapping;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.num_tokens = num_tokens;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.num_slots = num_blocks * block_size;
+  a.src_bf16 = src_dtype == PA_DTYPE_BF16;
+  return from_hip(pa::launch_scatter_fp8(a, static_cast<hipStream_t>(stream)));
+}
+
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t block_size, int32_t max_context_len) {
   if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0 ||
@@ -142,54 +241,26 @@ pa_status_t pa_decode(float* out, const void* query, const void* key_cache,
                       int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len,
                       float scale, pa_dtype_t dtype, void* workspace, size_t workspace_bytes,
                       void* stream) {
-  if (num_seqs < 0) return PA_ERR_SHAPE;
-  if (num_seqs == 0) return PA_OK;
-  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens ||
-      !workspace)
-    return PA_ERR_NULL;
-  if (num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
-      max_blocks_per_seq <= 0 || num_blocks <= 0 || max_context_len < 0 ||
-      num_q_heads % num_kv_heads != 0 || !std::isfinite(scale))
-    return PA_ERR_SHAPE;
-  if (!supported_block(block_size) || !supported_dim(head_dim) ||
-      !supported_group(num_q_heads, num_kv_heads) ||
-      (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16))
-    return PA_ERR_UNSUPPORTED;
-  if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) ||
-      !aligned(value_cache, 16) || !aligned(workspace, 16) || !aligned(block_tables, 4) ||
-      !aligned(context_lens, 4))
-    return PA_ERR_ALIGN;
-  const DecodeGeometry geo = decode_geometry(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                             block_size, max_context_len);
-  if (workspace_bytes < geo.bytes) return PA_ERR_WORKSPACE;
+  const bool type_ok = dtype == PA_DTYPE_F32 || dtype == PA_DTYPE_BF16;
+  return decode_impl(out, query, key_cache, value_cache, nullptr, nullptr, block_tables,
+                     context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                     max_blocks_per_seq, num_blocks, max_context_len, scale,
+                     dtype == PA_DTYPE_BF16 ? pa::KvType::BF16 : pa::KvType::F32, type_ok,
+                     workspace, workspace_bytes, stream);
+}
 
-  pa::DecodeArgs a;
-  char* ws = static_cast<char*>(workspace);
-  a.out = out;
-  a.plan = reinterpret_cast<pa::DecodePlan*>(ws);
-  a.plan_cus = 0;
-  a.plan_units_per_cu = 0;
-  a.part_o = reinterpret_cast<float*>(ws + geo.part_o_off);
-  a.part_ml = reinterpret_cast<float*>(ws + geo.part_ml_off);
-  a.query = query;
-  a.key_cache = key_cache;
-  a.value_cache = value_cache;
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  a.num_seqs = num_seqs;
-  a.num_q_heads = num_q_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.head_dim = head_dim;
-  a.block_size_log2 = log2_exact(block_size);
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.num_blocks = num_blocks;
-  a.ctx_limit = ctx_limit(max_context_len, max_blocks_per_seq, block_size);
-  a.part_floor = geo.launch.part_floor;
-  a.part_cap = geo.launch.part_cap;
-  a.waves = geo.launch.waves;
-  a.max_parts = geo.launch.max_parts;
-  a.scale_log2 = scale * 1.4426950408889634f;
-  return from_hip(pa::launch_decode(a, dtype == PA_DTYPE_BF16, static_cast<hipStream_t>(stream)));
+pa_status_t pa_decode_fp8(float* out, const void* query, const void* key_cache,
+                          const void* value_cache, const float* k_scale, const float* v_scale,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                          int64_t num_blocks, int32_t max_context_len, float scale,
+                          pa_dtype_t query_dtype, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return decode_impl(out, query, key_cache, value_cache, k_scale, v_scale, block_tables,
+                     context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                     max_blocks_per_seq, num_blocks, max_context_len, scale, pa::KvType::FP8,
+                     query_dtype == PA_DTYPE_BF16, workspace, workspace_bytes, stream);
 }
 
 size_t pa_prefill_chunk_workspace_size(int32_t num_seqs, int32_t total_q, int32_t max_q_len,

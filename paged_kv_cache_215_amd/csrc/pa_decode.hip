@@ -8,15 +8,19 @@
 // rows of KV head h / G over the sequence's n logical positions, the K/V rows
 // being gathered through the block table at run time.
 //
-// Work decomposition. A workgroup (4 waves) owns one (sequence, KV head,
-// context partition of P tokens). Its waves take interleaved 16-token tiles of
-// the partition; a tile never crosses a physical block (block sizes 16, 32).
-// Each wave keeps an online softmax (running max m, running sum l, unnormalised
-// accumulator) per query head of the GQA group, the 4 waves are merged in LDS,
-// and the workgroup writes one normalised partial (o, m, l) per query head. A
-// sequence that needs one partition writes its output directly; otherwise the
-// merge kernel combines the partials. Decode moves ~4 FLOP per byte of KV, far
-// below the matrix-core ridge, so the contractions stay on the VALU.
+// Work decomposition. A work unit is one (sequence, KV head, context
+// partition of P tokens); the partition size comes from a plan that every
+// workgroup derives from the context lengths at the start of the launch. The
+// grid is persistent (a few workgroups per CU): each workgroup (NW waves, 8
+// for the BF16 d 256 shapes) loops over units. In a unit the waves take
+// interleaved 16-token tiles of the partition; a tile never crosses a
+// physical block (block sizes 16, 32). Each wave keeps an online softmax
+// (running max m, running sum l, unnormalised accumulator) per query head of
+// the GQA group, the waves are merged in LDS, and the unit writes one
+// normalised partial (o, m, l) per query head. A sequence that needs one
+// partition writes its output directly; otherwise the merge kernel combines
+// the partials. Decode moves ~4 FLOP per byte of KV, far below the
+// matrix-core ridge, so the contractions stay on the VALU.
 //
 // Register layout of a 16-token tile (per wave):
 //   K: each row (token) is spread over KL lanes that each hold KCH 16-byte
@@ -45,8 +49,8 @@ constexpr int kMaxPartBlocks = 512;  // table entries staged per partition
 
 constexpr int choose_k_lanes(int row_chunks, int group) {
   // Enough lanes per K row that the q chunks held per lane (group * KCH
-  // 16-byte chunks) fit in 32 VGPRs, at least 4 so that a tile holds whole
-  // load groups.
+  // 16-byte chunks, times the q chunks per K chunk) fit in 32 VGPRs, at
+  // least 4 so that a tile holds whole load groups.
   int need = group * row_chunks / 8;
   if (need < 4) need = 4;
   int kl = 4;
@@ -58,7 +62,9 @@ template <typename T, int D, int G>
 struct DecodeShape {
   static constexpr int E = 16 / T::kBytes;          // elements per 16-byte chunk
   static constexpr int RC = D * T::kBytes / 16;     // chunks per row
-  static constexpr int KL = choose_k_lanes(RC, G);  // lanes per K row
+  static constexpr int QCH = T::Query::kBytes / T::kBytes;  // q chunks per K chunk
+  static constexpr int QRC = RC * QCH;              // q chunks per row
+  static constexpr int KL = choose_k_lanes(RC, G * QCH);  // lanes per K row
   static constexpr int KCH = RC / KL;               // chunks per lane per K row
   static constexpr int RK = kWave / KL;             // K rows per load instruction
   static constexpr int NGK = kTile / RK;            // K load groups per tile
@@ -70,6 +76,7 @@ struct DecodeShape {
   static constexpr int NGV = kTile / RV;            // V load groups per tile
   static constexpr int NHS = NVF < G ? NVF : G;     // distinct heads among a lane's scores
   static_assert(RC <= kWave && RK <= kTile && RV <= kTile, "tile shape");
+  static_assert(VL >= 4, "the V row-group sum covers at most 16 row groups");
   static_assert((KL & (KL - 1)) == 0 && KL >= 4, "K lanes");
 
   // Score slot j of lane l after the transposing reduction holds partial-dot
@@ -344,16 +351,25 @@ __global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(DecodeArgs
   const int lane = tid % kWave;
 
   // q of the G heads of this KV group, in the K-lane layout.
-  uint4 q[G][KCH];
+  constexpr int QCH = S::QCH, QRC = S::QRC;
+  using QT = typename T::Query;
+  uint4 q[G][KCH][QCH];
   {
     const uint4* qb = reinterpret_cast<const uint4*>(a.query) +
-                      ((int64_t)seq * a.num_q_heads + (int64_t)kvh * G) * RC;
+                      ((int64_t)seq * a.num_q_heads + (int64_t)kvh * G) * QRC;
     const int kc = lane % KL;
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int i = 0; i < KCH; ++i) q[g][i] = qb[g * RC + kc + KL * i];
+      for (int i = 0; i < KCH; ++i)
+#pragma unroll
+        for (int j = 0; j < QCH; ++j) q[g][i][j] = qb[g * QRC + (kc + KL * i) * QCH + j];
   }
+  // FP8 cache: the per-head K scale folds into the score scale, the V scale
+  // into the output normalisation
+  constexpr bool kScaled = std::is_same<T, FP8>::value;
+  const float score_scale = kScaled ? a.scale_log2 * a.k_scale[kvh] : a.scale_log2;
+  const float out_scale = kScaled ? a.v_scale[kvh] : 1.f;
 
   // Block-table entries of this partition, staged in LDS (at most
   // kMaxPartBlocks by construction of part_tokens); -1 marks an entry outside
@@ -396,7 +412,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(DecodeArgs
            (int64_t)((start + t * kTile) & (bs - 1)) * RC;
   };
 
-  // Software pipeline over this wave's tiles t = wave, wave + 4, ...: the K
+  // Software pipeline over this wave's tiles t = wave, wave + NW, ...: the K
   // registers are refilled for the next tile as soon as the scores are done,
   // the V registers as soon as the PV update is done, so one tile's loads are
   // always in flight behind the current tile's arithmetic. All branches are
@@ -412,15 +428,33 @@ __global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(DecodeArgs
 
     // ---- scores: partial dots, then transposing reduction over KL lanes
     float sc[NV];
+    if constexpr (QCH == 1) {  // K chunks are used as they are
 #pragma unroll
-    for (int gk = 0; gk < NGK; ++gk)
+      for (int gk = 0; gk < NGK; ++gk)
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float c = 0.f;
+        for (int g = 0; g < G; ++g) {
+          float c = 0.f;
 #pragma unroll
-        for (int i = 0; i < KCH; ++i) c = dot_chunk(T{}, kb[gk][i], q[g][i], c);
-        sc[gk * G + g] = c;
+          for (int i = 0; i < KCH; ++i) c = dot_chunk(QT{}, kb[gk][i], q[g][i][0], c);
+          sc[gk * G + g] = c;
+        }
+    } else {  // each K chunk is converted once for all G heads
+#pragma unroll
+      for (int gk = 0; gk < NGK; ++gk) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) sc[gk * G + g] = 0.f;
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) {
+          uint4 kq[QCH];
+          k_as_query(T{}, kb[gk][i], kq);
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int j = 0; j < QCH; ++j)
+              sc[gk * G + g] = dot_chunk(QT{}, kq[j], q[g][i][j], sc[gk * G + g]);
+        }
       }
+    }
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (kPrefetch) load_k<S>(kcache + off_next, lane, kb);
     __builtin_amdgcn_sched_barrier(0);
@@ -432,7 +466,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(DecodeArgs
     float s[NVF];
 #pragma unroll
     for (int j = 0; j < NVF; ++j) {
-      s[j] = sc[j] * a.scale_log2;
+      s[j] = sc[j] * score_scale;
       if (masked_tile) {
         const int tok = tok0 + S::slot_token(lane, j);
         s[j] = (valid && tok < n) ? s[j] : -INFINITY;
@@ -564,6 +598,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(DecodeArgs
         if constexpr (VL <= 32 && RV > 1) x += xor_lane<(VL <= 32 ? 32 : 1)>(x);
         if constexpr (VL <= 16 && RV > 2) x += xor_lane<(VL <= 16 ? 16 : 1)>(x);
         if constexpr (VL <= 8 && RV > 4) x += xor_lane<(VL <= 8 ? 8 : 1)>(x);
+        if constexpr (VL <= 4 && RV > 8) x += xor_lane<(VL <= 4 ? 4 : 1)>(x);
         acc[g][e] = x;
       }
     if (lane < VL) {
@@ -578,7 +613,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(DecodeArgs
   }
   __syncthreads();
 
-  // ---- merge the 4 waves and write o (normalised), m, l
+  // ---- merge the waves and write o (normalised), m, l
   for (int idx = tid; idx < G * D / 4; idx += kThreads) {
     const int g = idx / (D / 4), d4 = idx % (D / 4);
     float M = s_m[0][g];
@@ -593,7 +628,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(DecodeArgs
       const float4 x = s_acc[w][g][d4];
       o.x += sw * x.x; o.y += sw * x.y; o.z += sw * x.z; o.w += sw * x.w;
     }
-    const float inv = 1.f / L;
+    const float inv = out_scale / L;
     o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
     const int64_t head = (int64_t)seq * a.num_q_heads + (int64_t)kvh * G + g;
     if (nparts == 1) {
@@ -646,6 +681,7 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeArgs a) {
   const int P = a.plan->part_tokens;
   if (a.plan->max_nparts <= 1) return;
   const int rows = a.num_seqs * a.num_q_heads;
+  const int lane = threadIdx.x;
   for (int row = blockIdx.x; row < rows; row += gridDim.x) {
     const int seq = row / a.num_q_heads;
     int n = a.context_lens[seq];
@@ -655,21 +691,32 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeArgs a) {
     if (nparts <= 1) continue;  // written by the partition kernel (zeros if empty)
     const int64_t head = row;
     const float* ml = a.part_ml + 2 * head * a.max_parts;
+    // lane p holds partition p's (m, l), 64 partitions per pass
     float M = -INFINITY;
-    for (int p = 0; p < nparts; ++p) M = fmaxf(M, ml[2 * p]);
+    for (int p = lane; p < nparts; p += kWave) M = fmaxf(M, ml[2 * p]);
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) M = fmaxf(M, __shfl_xor(M, m));
     float o[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) o[e] = 0.f;
     float L = 0.f;
-    const float* po = a.part_o + head * a.max_parts * D + threadIdx.x * PER;
-    for (int p = 0; p < nparts; ++p) {
-      const float w = ml[2 * p + 1] * fast_exp2(ml[2 * p] - M);
-      L += w;
+    const float* po = a.part_o + head * a.max_parts * D + lane * PER;
+    for (int p0 = 0; p0 < nparts; p0 += kWave) {
+      const int p = p0 + lane;
+      const float w_lane = p < nparts ? ml[2 * p + 1] * fast_exp2(ml[2 * p] - M) : 0.f;
+      L += w_lane;
+      const int cnt = nparts - p0 < kWave ? nparts - p0 : kWave;
+#pragma unroll 4
+      for (int j = 0; j < cnt; ++j) {
+        const float w = __shfl(w_lane, j);
 #pragma unroll
-      for (int e = 0; e < PER; ++e) o[e] = __builtin_fmaf(w, po[(int64_t)p * D + e], o[e]);
+        for (int e = 0; e < PER; ++e) o[e] = __builtin_fmaf(w, po[(int64_t)(p0 + j) * D + e], o[e]);
+      }
     }
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) L += __shfl_xor(L, m);
     const float inv = 1.f / L;
-    float* out = a.out + head * D + threadIdx.x * PER;
+    float* out = a.out + head * D + lane * PER;
 #pragma unroll
     for (int e = 0; e < PER; ++e) out[e] = o[e] * inv;
   }
@@ -755,7 +802,7 @@ static hipError_t launch_nw(const DecodeArgs& a, hipStream_t stream) {
     DecodeArgs c = a;
     c.num_seqs = a.num_seqs - s0 < kPlanSeqs ? a.num_seqs - s0 : kPlanSeqs;
     c.out = a.out + (int64_t)s0 * a.num_q_heads * D;
-    c.query = static_cast<const char*>(a.query) + (int64_t)s0 * a.num_q_heads * D * T::kBytes;
+    c.query = static_cast<const char*>(a.query) + (int64_t)s0 * a.num_q_heads * D * T::Query::kBytes;
     c.block_tables = a.block_tables + (int64_t)s0 * a.max_blocks_per_seq;
     c.context_lens = a.context_lens + s0;
     c.plan_cus = cus;
@@ -768,7 +815,9 @@ static hipError_t launch_nw(const DecodeArgs& a, hipStream_t stream) {
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int64_t rows = (int64_t)c.num_seqs * c.num_q_heads;
-    const int64_t mgrid = rows < (int64_t)cus ? rows : (int64_t)cus;
+    // up to 8 one-wave workgroups per CU: each row is a short chain of
+    // dependent loads, so rows run side by side rather than in turn
+    const int64_t mgrid = rows < 8 * (int64_t)cus ? rows : 8 * (int64_t)cus;
     hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)mgrid), dim3(kWave), 0, stream, c);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -779,8 +828,9 @@ static hipError_t launch_nw(const DecodeArgs& a, hipStream_t stream) {
 template <typename T, int D, int G>
 static hipError_t launch_t(const DecodeArgs& a, int waves, hipStream_t stream) {
   // 8-wave workgroups are limited to 256 VGPRs per lane; the d = 256 shapes
-  // with 8 query heads per KV head or float32 data need more and use 4 waves.
-  constexpr bool kFits8 = !(D == 256 && (G == 8 || T::kBytes == 4));
+  // with 8 query heads per KV head or float32 data, and FP8 with 8 query heads
+  // per KV head (16 accumulators per head and lane), need more and use 4 waves.
+  constexpr bool kFits8 = !(D == 256 && (G == 8 || T::kBytes == 4)) && G * (16 / T::kBytes) <= 64;
   if constexpr (kFits8) {
     if (waves == 8) return launch_nw<T, D, G, 8>(a, stream);
   }
@@ -808,9 +858,14 @@ static hipError_t launch_d(const DecodeArgs& a, int group, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, bool bf16, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs& a, KvType kv, hipStream_t stream) {
   const int group = a.num_q_heads / a.num_kv_heads;
-  return bf16 ? launch_d<BF16>(a, group, stream) : launch_d<F32>(a, group, stream);
+  switch (kv) {
+    case KvType::BF16: return launch_d<BF16>(a, group, stream);
+    case KvType::F32: return launch_d<F32>(a, group, stream);
+    case KvType::FP8: return launch_d<FP8>(a, group, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pa

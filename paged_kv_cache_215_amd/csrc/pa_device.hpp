@@ -8,13 +8,20 @@ namespace pa {
 
 constexpr int kWave = 64;
 
-// Element-type tags. The cache stores either binary32 or bfloat16 (the top
-// half of a binary32); both move through 16-byte vectors.
+// Element-type tags of the KV cache. The cache stores binary32, bfloat16 (the
+// top half of a binary32) or FP8 E4M3 codes, all moved through 16-byte
+// vectors; Query is the element type of the queries that attend to it.
 struct F32 {
   static constexpr int kBytes = 4;
+  using Query = F32;
 };
 struct BF16 {
   static constexpr int kBytes = 2;
+  using Query = BF16;
+};
+struct FP8 {
+  static constexpr int kBytes = 1;
+  using Query = BF16;
 };
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -57,12 +64,40 @@ __device__ __forceinline__ float dot_chunk(F32, const uint4& k, const uint4& q, 
   return c;
 }
 
-// Widen one 16-byte chunk to binary32 (8 bfloat16 or 4 binary32 values).
+// A 16-byte K chunk in the query's element type: BF16 and binary32 chunks
+// are used as they are; 16 E4M3 codes become 16 bfloat16 (two chunks) with
+// the hardware conversion (v_cvt_scalef32_pk_bf16_fp8 at scale 1), which is
+// exact: every E4M3 value is a bfloat16 value.
+template <bool Hi>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, Hi));
+}
+__device__ __forceinline__ void k_as_query(F32, const uint4& k, uint4* out) { out[0] = k; }
+__device__ __forceinline__ void k_as_query(BF16, const uint4& k, uint4* out) { out[0] = k; }
+__device__ __forceinline__ void k_as_query(FP8, const uint4& k, uint4* out) {
+  out[0] = make_uint4(fp8x2_to_bf16x2<false>(k.x), fp8x2_to_bf16x2<true>(k.x),
+                      fp8x2_to_bf16x2<false>(k.y), fp8x2_to_bf16x2<true>(k.y));
+  out[1] = make_uint4(fp8x2_to_bf16x2<false>(k.z), fp8x2_to_bf16x2<true>(k.z),
+                      fp8x2_to_bf16x2<false>(k.w), fp8x2_to_bf16x2<true>(k.w));
+}
+
+// Widen one 16-byte chunk to binary32 (16 E4M3, 8 bfloat16 or 4 binary32
+// values). E4M3 uses v_cvt_pk_f32_fp8, exact for every code.
 __device__ __forceinline__ void widen_chunk(BF16, const uint4& v, float* out) {
   out[0] = bf16_lo(v.x); out[1] = bf16_hi(v.x);
   out[2] = bf16_lo(v.y); out[3] = bf16_hi(v.y);
   out[4] = bf16_lo(v.z); out[5] = bf16_hi(v.z);
   out[6] = bf16_lo(v.w); out[7] = bf16_hi(v.w);
+}
+__device__ __forceinline__ void widen_chunk(FP8, const uint4& v, float* out) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+    out[4 * i] = a[0]; out[4 * i + 1] = a[1];
+    out[4 * i + 2] = b[0]; out[4 * i + 3] = b[1];
+  }
 }
 __device__ __forceinline__ void widen_chunk(F32, const uint4& v, float* out) {
   out[0] = __uint_as_float(v.x); out[1] = __uint_as_float(v.y);

@@ -40,6 +40,8 @@ struct DecodeArgs {
   int waves;             // waves per partition workgroup (4 or 8)
   int max_parts;         // ceil(max_context_len / part_floor): workspace layout
   float scale_log2;      // softmax scale * log2(e)
+  const float* k_scale;  // [Hkv] FP8 cache: K = code value * k_scale (else null)
+  const float* v_scale;  // [Hkv] FP8 cache: V = code value * v_scale (else null)
 };
 
 struct ScatterArgs {
@@ -53,6 +55,22 @@ struct ScatterArgs {
   int row_chunks;        // D * elem_bytes / 16
   int block_size;
   int64_t num_slots;     // num_blocks * block_size
+};
+
+struct ScatterFp8Args {
+  const void* key;       // [T, Hkv, D] BF16 or float32
+  const void* value;
+  void* key_cache;       // [num_blocks, Hkv, bs, D] E4M3 codes
+  void* value_cache;
+  const int64_t* slot_mapping;  // [T]
+  const float* k_scale;  // [Hkv]
+  const float* v_scale;  // [Hkv]
+  int num_tokens;
+  int num_kv_heads;
+  int head_dim;
+  int block_size;
+  int64_t num_slots;     // num_blocks * block_size
+  bool src_bf16;         // source rows are BF16 (else float32)
 };
 
 struct PrefillArgs {
@@ -91,9 +109,11 @@ int decode_target_workgroups();
 int decode_waves_per_workgroup();
 DecodeLaunch decode_launch_shape(int num_seqs, int num_kv_heads, int block_size,
                                  int max_context_len);
-hipError_t launch_decode(const DecodeArgs& a, bool bf16, hipStream_t stream);
+enum class KvType { F32, BF16, FP8 };
+hipError_t launch_decode(const DecodeArgs& a, KvType kv, hipStream_t stream);
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t stream);
 hipError_t launch_scatter(const ScatterArgs& a, hipStream_t stream);
+hipError_t launch_scatter_fp8(const ScatterFp8Args& a, hipStream_t stream);
 
 int prefill_kv_splits(int num_seqs, int max_q_len, int num_q_heads, int num_kv_heads,
                       int head_dim, int max_context_len);

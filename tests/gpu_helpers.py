@@ -24,10 +24,18 @@ def gpu_decode(case, layer=0, **kw):
                         case.max_context_len, **kw)
 
 
-def compact_inputs(case, layer, seqs):
+def gpu_decode_fp8(case, layer=0, **kw):
+    return pa.pa_decode_fp8(case.queries[layer], case.key_caches[layer], case.value_caches[layer],
+                            case.k_scales[layer], case.v_scales[layer], case.block_tables,
+                            case.context_lens, case.scale, case.max_context_len, **kw)
+
+
+def compact_inputs(case, layer, seqs, key_cache=None, value_cache=None):
     """Host copies of the blocks the given sequences use, with their tables
     renumbered into the compacted pool (the oracle is invariant under block
-    renumbering, which its own tests pin)."""
+    renumbering, which its own tests pin). Also returns the renumbering."""
+    kcache = case.key_caches[layer] if key_cache is None else key_cache
+    vcache = case.value_caches[layer] if value_cache is None else value_cache
     bt = case.layout.block_tables
     bs = case.block_size
     used = []
@@ -36,10 +44,9 @@ def compact_inputs(case, layer, seqs):
         used.extend(int(x) for x in bt[b, : -(-n // bs)])
     uniq = sorted(set(used))
     remap = {blk: i for i, blk in enumerate(uniq)}
-    idx = torch.as_tensor(uniq if uniq else [0], dtype=torch.int64,
-                          device=case.key_caches[layer].device)
-    kc = to_numpy_bits(case.key_caches[layer].index_select(0, idx))
-    vc = to_numpy_bits(case.value_caches[layer].index_select(0, idx))
+    idx = torch.as_tensor(uniq if uniq else [0], dtype=torch.int64, device=kcache.device)
+    kc = to_numpy_bits(kcache.index_select(0, idx))
+    vc = to_numpy_bits(vcache.index_select(0, idx))
     tables = np.full((len(seqs), bt.shape[1]), -1, dtype=np.int32)
     for i, b in enumerate(seqs):
         n = int(case.layout.context_lens[b])
@@ -47,13 +54,42 @@ def compact_inputs(case, layer, seqs):
             tables[i, j] = remap[int(bt[b, j])]
     lens = np.array([case.layout.context_lens[b] for b in seqs], dtype=np.int64)
     q = to_numpy_bits(case.queries[layer])[list(seqs)]
-    return q, kc, vc, tables, lens
+    return q, kc, vc, tables, lens, remap
+
+
+def _oracle_attend(case, layer, q, kc, vc, tables, lens):
+    if case.kv_fp8:
+        return oracle.fp8.decode_fp8_ref(q, kc, vc, case.k_scales[layer].cpu().numpy(),
+                                         case.v_scales[layer].cpu().numpy(), tables, lens,
+                                         case.scale)
+    return oracle.decode_ref(q, kc, vc, tables, lens, case.scale)
 
 
 def oracle_decode(case, layer=0, seqs=None):
     seqs = list(range(case.num_decode_seqs)) if seqs is None else list(seqs)
-    q, kc, vc, tables, lens = compact_inputs(case, layer, seqs)
-    return oracle.decode_ref(q, kc, vc, tables, lens, case.scale)
+    q, kc, vc, tables, lens, _ = compact_inputs(case, layer, seqs)
+    return _oracle_attend(case, layer, q, kc, vc, tables, lens)
+
+
+def oracle_decode_after_write(case, key_before, value_before, layer=0, seqs=None):
+    """Oracle of "write the new tokens, then attend": the blocks are taken
+    from copies of the caches made before the device wrote the new tokens, and
+    the oracle's own scatter writes them (so no oracle input comes from the
+    device path)."""
+    seqs = list(range(case.num_decode_seqs)) if seqs is None else list(seqs)
+    q, kc, vc, tables, lens, remap = compact_inputs(case, layer, seqs, key_before, value_before)
+    bs = case.block_size
+    slots = case.slot_mapping.cpu().numpy()
+    local = np.array([remap[int(s) // bs] * bs + int(s) % bs if int(s) // bs in remap else -1
+                      for s in slots], dtype=np.int64)
+    nk, nv = to_numpy_bits(case.new_keys[layer]), to_numpy_bits(case.new_values[layer])
+    if case.kv_fp8:
+        kc, vc = oracle.fp8.reshape_and_cache_fp8_ref(nk, nv, kc, vc, local,
+                                                      case.k_scales[layer].cpu().numpy(),
+                                                      case.v_scales[layer].cpu().numpy())
+    else:
+        kc, vc = oracle.reshape_and_cache_ref(nk, nv, kc, vc, local)
+    return _oracle_attend(case, layer, q, kc, vc, tables, lens)
 
 
 def max_abs_err(got, want):
@@ -68,11 +104,30 @@ def gpu_prefill(case, **kw):
                                int(max(int(x) for x in p.context_lens.cpu())), **kw)
 
 
-def oracle_prefill_rows(case, seq, rows):
+def _oracle_written_blocks(case, blocks, key_before, value_before):
+    """Host copies of the given physical blocks taken before the device wrote
+    the case's new tokens, with the oracle's own scatter of those tokens
+    applied (tokens bound for other blocks are skipped)."""
+    idx = torch.as_tensor(blocks, dtype=torch.int64, device=key_before.device)
+    kc = to_numpy_bits(key_before.index_select(0, idx))
+    vc = to_numpy_bits(value_before.index_select(0, idx))
+    if case.slot_mapping is None:
+        return kc, vc
+    bs = case.block_size
+    where = {blk: i for i, blk in enumerate(blocks)}
+    local = np.array([where[int(s) // bs] * bs + int(s) % bs if int(s) // bs in where else -1
+                      for s in case.slot_mapping.cpu().numpy()], dtype=np.int64)
+    return oracle.reshape_and_cache_ref(to_numpy_bits(case.new_keys[0]),
+                                        to_numpy_bits(case.new_values[0]), kc, vc, local)
+
+
+def oracle_prefill_rows(case, seq, rows, key_before, value_before):
     """Oracle rows of prefill sequence `seq` (index among the prefill
-    sequences). Row i of a chunk of L rows at context n equals a one-row chunk
-    at context n - L + i + 1 (the oracle's chunking invariance, pinned by its
-    own tests), so sampled rows need only the blocks that row can see."""
+    sequences), on the caches as they were before the device wrote the step's
+    tokens plus the oracle's own write. Row i of a chunk of L rows at context
+    n equals a one-row chunk at context n - L + i + 1 (the oracle's chunking
+    invariance, pinned by its own tests), so sampled rows need only the blocks
+    that row can see."""
     p = case.prefill
     b = case.num_decode_seqs + seq
     n = int(case.layout.context_lens[b])
@@ -84,9 +139,7 @@ def oracle_prefill_rows(case, seq, rows):
     for i in rows:
         visible = n - L + i + 1
         blocks = [int(x) for x in case.layout.block_tables[b, : -(-visible // bs)]]
-        idx = torch.as_tensor(blocks, dtype=torch.int64, device=case.key_caches[0].device)
-        kc = to_numpy_bits(case.key_caches[0].index_select(0, idx))
-        vc = to_numpy_bits(case.value_caches[0].index_select(0, idx))
+        kc, vc = _oracle_written_blocks(case, blocks, key_before, value_before)
         table = np.arange(len(blocks), dtype=np.int32)[None, :]
         out.append(oracle.prefill_chunk_ref(qh[q0 + i:q0 + i + 1], kc, vc, table,
                                             np.array([visible]), np.array([0, 1]), case.scale)[0])

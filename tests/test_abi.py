@@ -145,3 +145,53 @@ def test_workspace_init_rejects(lib):
     assert lib.pa_decode_workspace_init(None, 256, None) == NULL
     assert lib.pa_decode_workspace_init(A + 4, 256, None) == ALIGN
     assert lib.pa_decode_workspace_init(None, 0, None) == OK
+
+
+def fp8_scatter_args(**over):
+    args = dict(key=A, value=A, key_cache=A, value_cache=A, slot_mapping=A, k_scale=A, v_scale=A,
+                num_tokens=8, num_kv_heads=4, head_dim=256, block_size=16, num_blocks=100,
+                src_dtype=BF16, stream=None)
+    args.update(over)
+    return list(args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(key=None), NULL), (dict(k_scale=None), NULL), (dict(v_scale=None), NULL),
+    (dict(num_tokens=-1), SHAPE), (dict(num_kv_heads=0), SHAPE), (dict(block_size=8), UNSUP),
+    (dict(head_dim=48), UNSUP), (dict(src_dtype=9), UNSUP), (dict(key_cache=A + 8), ALIGN),
+    (dict(k_scale=A + 2), ALIGN), (dict(slot_mapping=A + 4), ALIGN),
+])
+def test_fp8_scatter_rejects(lib, over, code):
+    assert lib.pa_reshape_and_cache_fp8(*fp8_scatter_args(**over)) == code
+
+
+def test_fp8_scatter_zero_tokens_is_noop(lib):
+    assert lib.pa_reshape_and_cache_fp8(*fp8_scatter_args(num_tokens=0, k_scale=None)) == OK
+
+
+def fp8_decode_args(**over):
+    args = dict(out=A, query=A, key_cache=A, value_cache=A, k_scale=A, v_scale=A,
+                block_tables=A, context_lens=A, num_seqs=4, num_q_heads=16, num_kv_heads=4,
+                head_dim=256, block_size=16, max_blocks_per_seq=64, num_blocks=1000,
+                max_context_len=1024, scale=0.0625, query_dtype=BF16, workspace=A,
+                workspace_bytes=1 << 30, stream=None)
+    args.update(over)
+    return list(args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(out=None), NULL), (dict(k_scale=None), NULL), (dict(v_scale=None), NULL),
+    (dict(workspace=None), NULL), (dict(num_seqs=-2), SHAPE), (dict(num_kv_heads=3), SHAPE),
+    (dict(scale=float("inf")), SHAPE), (dict(query_dtype=F32), UNSUP), (dict(head_dim=80), UNSUP),
+    (dict(block_size=64), UNSUP), (dict(key_cache=A + 8), ALIGN), (dict(v_scale=A + 1), ALIGN),
+    (dict(workspace_bytes=64), WORKSPACE),
+])
+def test_fp8_decode_rejects(lib, over, code):
+    assert lib.pa_decode_fp8(*fp8_decode_args(**over)) == code
+
+
+def test_fp8_decode_error_order(lib):
+    assert lib.pa_decode_fp8(*fp8_decode_args(num_seqs=0, out=None, k_scale=None)) == OK
+    assert lib.pa_decode_fp8(*fp8_decode_args(k_scale=None, num_q_heads=0)) == NULL
+    assert lib.pa_decode_fp8(*fp8_decode_args(query_dtype=F32, num_q_heads=14)) == SHAPE
+    assert lib.pa_decode_fp8(*fp8_decode_args(query_dtype=F32, v_scale=A + 2)) == UNSUP

@@ -8,7 +8,8 @@ import pytest
 import torch
 
 import paged_kv_cache_215_amd as pa
-from gpu_helpers import ATOL, compact_inputs, gpu_decode, max_abs_err, oracle_decode, say
+from gpu_helpers import (ATOL, gpu_decode, max_abs_err, oracle_decode, oracle_decode_after_write,
+                         say)
 from workloads import make_case, make_config_case
 
 pytestmark = pytest.mark.gpu
@@ -71,16 +72,27 @@ def test_c4_grpo_cow_full():
 
 def test_c5_mixed_decode_part_full():
     case = make_config_case("c5_mixed_step", device=DEV)
-    # write, then attend: the new tokens go in first
+    # write, then attend: the new tokens go in first; the oracle applies its
+    # own write to a copy of the caches taken before the device's
+    kb, vb = case.key_caches[0].clone(), case.value_caches[0].clone()
     pa.pa_reshape_and_cache(case.new_keys[0], case.new_values[0], case.key_caches[0],
                             case.value_caches[0], case.slot_mapping)
-    _check(case)
+    say(f"[decode] {case.name} (write, then attend)")
+    got = gpu_decode(case).cpu().numpy()
+    want = oracle_decode_after_write(case, kb, vb)
+    err = max_abs_err(got, want)
+    say(f"    max-abs err {err:.3e}")
+    assert np.all(np.isfinite(got)) and err <= ATOL
 
 
 def test_c3_full_step_sampled():
     # The full 16-layer, 64 x 8192-token step in the launch configuration the
     # benchmark times; the oracle checks sampled (layer, sequence) pairs.
     case = make_config_case("c3_full_step", device=DEV)
+    samples = [(0, [0, 37]), (7, [5]), (15, [63, 12])]
+    # copies of the sampled layers before the device writes the new tokens
+    before = {layer: (case.key_caches[layer].clone(), case.value_caches[layer].clone())
+              for layer, _ in samples}
     outs = []
     for layer in range(case.num_layers):
         pa.pa_reshape_and_cache(case.new_keys[layer], case.new_values[layer],
@@ -88,9 +100,9 @@ def test_c3_full_step_sampled():
                                 case.slot_mapping)
         outs.append(gpu_decode(case, layer))
     torch.cuda.synchronize()
-    for layer, seqs in [(0, [0, 37]), (7, [5]), (15, [63, 12])]:
+    for layer, seqs in samples:
         got = outs[layer].cpu().numpy()[seqs]
-        want = oracle_decode(case, layer, seqs)
+        want = oracle_decode_after_write(case, *before[layer], layer=layer, seqs=seqs)
         err = max_abs_err(got, want)
         say(f"[decode] c3 layer {layer} seqs {seqs}: max-abs err {err:.3e}")
         assert err <= ATOL

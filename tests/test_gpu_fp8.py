@@ -1,0 +1,218 @@
+"""GPU parity of the FP8 (E4M3) cache path through the C ABI: the quantizing
+scatter bit for bit against the oracle's quantizer, and decode over FP8
+caches within 1e-3 max-abs of the fp64 oracle on the dequantized cache."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_215_amd as pa
+from gpu_helpers import (ATOL, gpu_decode_fp8, max_abs_err, oracle_decode,
+                         oracle_decode_after_write, say)
+from workloads import make_case, make_config_case, to_numpy_bits
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _scatter_and_compare(key, value, kc, vc, slots, ks, vs, tag):
+    say(f"[fp8 scatter] {tag}")
+    want_k, want_v = oracle.fp8.reshape_and_cache_fp8_ref(
+        to_numpy_bits(key), to_numpy_bits(value), to_numpy_bits(kc), to_numpy_bits(vc),
+        slots.cpu().numpy(), ks.cpu().numpy(), vs.cpu().numpy())
+    pa.pa_reshape_and_cache_fp8(key, value, kc, vc, slots, ks, vs)
+    torch.cuda.synchronize()
+    got_k, got_v = kc.cpu().numpy(), vc.cpu().numpy()
+    nk = int(np.sum(got_k != want_k))
+    nv = int(np.sum(got_v != want_v))
+    say(f"    differing bytes: K {nk}, V {nv}")
+    assert nk == 0 and nv == 0
+
+
+def _special_values():
+    """Every E4M3 value, every midpoint between neighbours, values around the
+    saturation bound, infinities, NaN, signed zeros and the subnormal range."""
+    vals = oracle.fp8.e4m3_value(np.arange(0x7F))
+    mids = (vals[:-1] + vals[1:]) / 2
+    extra = np.array([448.0, 449.0, 463.0, 464.0, 465.0, 480.0, 1e5, np.inf, np.nan, 0.0,
+                      2.0 ** -10, 3 * 2.0 ** -10, 2.0 ** -11, 2.0 ** -20, 1e-30])
+    x = np.concatenate([vals, mids, extra])
+    x = np.concatenate([x, -x])
+    return x.astype(np.float32)
+
+
+@pytest.mark.parametrize("src", ["bf16", "f32"])
+@pytest.mark.parametrize("head_dim", [64, 128, 256])
+def test_scatter_special_values_bit_exact(src, head_dim):
+    # power-of-two scales keep x / s exact, so ties and bounds land on the
+    # quantizer's own decision points; the float32 source also runs with
+    # scales whose division rounds
+    x = _special_values()
+    hkv, bs = 2, 16
+    per_token = hkv * head_dim
+    reps = -(-x.size // per_token) + 1
+    rng = np.random.default_rng(head_dim)
+    flat = np.concatenate([x, rng.standard_normal(reps * per_token - x.size).astype(np.float32)
+                           * 100])[: reps * per_token]
+    key = torch.from_numpy(flat.reshape(reps, hkv, head_dim)).to(DEV)
+    value = torch.from_numpy(-flat.reshape(reps, hkv, head_dim)[::-1].copy()).to(DEV)
+    if src == "bf16":
+        key, value = key.to(torch.bfloat16), value.to(torch.bfloat16)
+    nb = reps // bs + 2
+    kc = torch.randint(0, 256, (nb, hkv, bs, head_dim), dtype=torch.uint8, device=DEV)
+    vc = torch.randint(0, 256, (nb, hkv, bs, head_dim), dtype=torch.uint8, device=DEV)
+    slots = torch.from_numpy(rng.permutation(nb * bs)[:reps].astype(np.int64)).to(DEV)
+    scale_sets = [([1.0, 0.5], [2.0, 0.25])]
+    if src == "f32":
+        scale_sets.append(([0.3173, 1.7], [0.0131, 3.3]))
+    for ks, vs in scale_sets:
+        kst = torch.tensor(ks, dtype=torch.float32, device=DEV)
+        vst = torch.tensor(vs, dtype=torch.float32, device=DEV)
+        _scatter_and_compare(key, value, kc, vc, slots, kst, vst,
+                             f"{src} d{head_dim} scales {ks} {vs}")
+
+
+@pytest.mark.parametrize("block_size", [16, 32])
+def test_scatter_skips_and_out_of_range(block_size):
+    rng = np.random.default_rng(block_size)
+    hkv, d, nb, t = 4, 256, 40, 300
+    key = torch.randn(t, hkv, d, device=DEV).to(torch.bfloat16)
+    value = torch.randn(t, hkv, d, device=DEV).to(torch.bfloat16)
+    kc = torch.randint(0, 256, (nb, hkv, block_size, d), dtype=torch.uint8, device=DEV)
+    vc = torch.randint(0, 256, (nb, hkv, block_size, d), dtype=torch.uint8, device=DEV)
+    slots = rng.permutation(nb * block_size)[:t].astype(np.int64)
+    slots[::7] = -1
+    slots[5] = nb * block_size + 3        # out of range: skipped by the kernel
+    ks = torch.tensor([0.01, 0.02, 0.005, 0.03], device=DEV)
+    vs = torch.tensor([0.011, 0.021, 0.0051, 0.031], device=DEV)
+    slots_t = torch.from_numpy(slots).to(DEV)
+    # the oracle skips negative slots only; give it the kernel's reading of
+    # the out-of-range one (skipped) explicitly
+    oracle_slots = slots.copy()
+    oracle_slots[5] = -1
+    want_k, want_v = oracle.fp8.reshape_and_cache_fp8_ref(
+        to_numpy_bits(key), to_numpy_bits(value), kc.cpu().numpy(), vc.cpu().numpy(),
+        oracle_slots, ks.cpu().numpy(), vs.cpu().numpy())
+    pa.pa_reshape_and_cache_fp8(key, value, kc, vc, slots_t, ks, vs)
+    torch.cuda.synchronize()
+    assert np.array_equal(kc.cpu().numpy(), want_k)
+    assert np.array_equal(vc.cpu().numpy(), want_v)
+
+
+def _check_decode(case, tag=""):
+    say(f"[fp8 decode] {case.name} {tag}")
+    out = gpu_decode_fp8(case)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    want = oracle_decode(case)
+    assert np.all(np.isfinite(got)), "non-finite output"
+    err = max_abs_err(got, want)
+    say(f"    max-abs err {err:.3e}")
+    assert err <= ATOL
+    return out
+
+
+@pytest.mark.parametrize("head_dim", [64, 128, 256])
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+@pytest.mark.parametrize("block_size", [16, 32])
+def test_decode_shapes_ragged(head_dim, group, block_size):
+    lens = [1, 15, 16, 17, block_size - 1, block_size + 1, 63, 64, 65, 200, 1000, 2500]
+    case = make_case(name=f"fp8_d{head_dim}_g{group}_bs{block_size}", seed=3 * head_dim + group,
+                     context_lens=lens, num_q_heads=2 * group, num_kv_heads=2,
+                     head_dim=head_dim, block_size=block_size, device=DEV, kv_fp8=True)
+    _check_decode(case)
+
+
+def test_decode_zero_and_single_token_contexts():
+    case = make_case(name="fp8_zeros", seed=17, context_lens=[0, 1, 0, 9], num_q_heads=16,
+                     num_kv_heads=4, head_dim=256, block_size=16, device=DEV, kv_fp8=True)
+    o = _check_decode(case).cpu().numpy()
+    assert np.all(o[0] == 0) and np.all(o[2] == 0)
+    # n = 1: the token's dequantized value row, up to the float32 product
+    # code value * scale (exact) -- compare with the oracle's dequantization
+    blk = int(case.layout.block_tables[1, 0])
+    codes = case.value_caches[0][blk, :, 0, :].cpu().numpy()
+    vs = case.v_scales[0].cpu().numpy()
+    for h in range(16):
+        want = oracle.fp8.e4m3_value(codes[h // 4]) * np.float64(vs[h // 4])
+        assert np.max(np.abs(o[1, h] - want)) <= 1e-6 * (1 + np.max(np.abs(want)))
+
+
+@pytest.mark.parametrize("name", ["c2_layer_decode", "c4_grpo_cow"])
+def test_decode_configs_full(name):
+    _check_decode(make_config_case(name, device=DEV, kv_fp8=True))
+
+
+def test_c5_write_then_attend():
+    # the mixed step's decode part over an FP8 cache: quantizing write of the
+    # 767 new tokens (checked byte for byte), then decode
+    case = make_config_case("c5_mixed_step", device=DEV, kv_fp8=True)
+    kb, vb = case.key_caches[0].clone(), case.value_caches[0].clone()
+    pa.pa_reshape_and_cache_fp8(case.new_keys[0], case.new_values[0], case.key_caches[0],
+                                case.value_caches[0], case.slot_mapping, case.k_scales[0],
+                                case.v_scales[0])
+    out = gpu_decode_fp8(case)
+    torch.cuda.synchronize()
+    # bytes of the written slots against the oracle's quantizer
+    slots = case.slot_mapping.cpu().numpy()
+    bs = case.block_size
+    blk = torch.as_tensor(slots // bs, device=DEV)
+    off = torch.as_tensor(slots % bs, device=DEV)
+    got_k = case.key_caches[0][blk, :, off, :].cpu().numpy()
+    got_v = case.value_caches[0][blk, :, off, :].cpu().numpy()
+    want_k = oracle.fp8.quantize_rows(to_numpy_bits(case.new_keys[0]), case.k_scales[0].cpu().numpy())
+    want_v = oracle.fp8.quantize_rows(to_numpy_bits(case.new_values[0]),
+                                      case.v_scales[0].cpu().numpy())
+    assert np.array_equal(got_k, want_k) and np.array_equal(got_v, want_v)
+    got = out.cpu().numpy()
+    want = oracle_decode_after_write(case, kb, vb)
+    err = max_abs_err(got, want)
+    say(f"[fp8 decode] c5 (write, then attend): max-abs err {err:.3e}")
+    assert np.all(np.isfinite(got)) and err <= ATOL
+
+
+def test_c3_full_size_sampled():
+    # one layer of the 64 x 8192-token step at full size, FP8 cache, in the
+    # benchmark's launch configuration; sampled sequences against the oracle
+    case = make_config_case("c3_full_step", device=DEV, kv_fp8=True, num_layers=1)
+    kb, vb = case.key_caches[0].clone(), case.value_caches[0].clone()
+    pa.pa_reshape_and_cache_fp8(case.new_keys[0], case.new_values[0], case.key_caches[0],
+                                case.value_caches[0], case.slot_mapping, case.k_scales[0],
+                                case.v_scales[0])
+    out = gpu_decode_fp8(case)
+    torch.cuda.synchronize()
+    seqs = [0, 31, 63]
+    got = out.cpu().numpy()[seqs]
+    want = oracle_decode_after_write(case, kb, vb, seqs=seqs)
+    err = max_abs_err(got, want)
+    say(f"[fp8 decode] c3 sampled {seqs}: max-abs err {err:.3e}")
+    assert err <= ATOL
+
+
+def test_fp8_matches_bf16_decode_on_dequantized_cache():
+    # the FP8 path against the BF16 path on the same values: every E4M3 value
+    # times a power-of-two scale is a BF16 value, so both decode the same
+    # numbers and differ only by float32 rounding
+    case = make_case(name="fp8_vs_bf16", seed=23, context_lens=[5, 300, 2000], num_q_heads=16,
+                     num_kv_heads=4, head_dim=256, block_size=16, device=DEV, kv_fp8=True)
+    ks = torch.tensor([1 / 64, 1 / 32, 1 / 128, 1 / 16], device=DEV)
+    vs = torch.tensor([1 / 32, 1 / 64, 1 / 16, 1 / 128], device=DEV)
+    case.k_scales[0], case.v_scales[0] = ks, vs
+    out8 = gpu_decode_fp8(case)
+    kf = case.key_caches[0].view(torch.float8_e4m3fn).float() * ks[None, :, None, None]
+    vf = case.value_caches[0].view(torch.float8_e4m3fn).float() * vs[None, :, None, None]
+    out16 = pa.pa_decode(case.queries[0], kf.to(torch.bfloat16), vf.to(torch.bfloat16),
+                         case.block_tables, case.context_lens, case.scale, case.max_context_len)
+    torch.cuda.synchronize()
+    diff = float((out8 - out16).abs().max())
+    say(f"[fp8 decode] fp8 vs bf16 path: max diff {diff:.3e}")
+    assert diff <= 1e-4
+
+
+def test_run_to_run_bit_identical():
+    case = make_config_case("c2_layer_decode", device=DEV, kv_fp8=True)
+    a = gpu_decode_fp8(case)
+    b = gpu_decode_fp8(case)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)

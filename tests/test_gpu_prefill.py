@@ -15,22 +15,28 @@ DEV = "cuda"
 
 
 def _write_chunk(case):
+    """Device write of the step's tokens; returns copies of the caches taken
+    before it, from which the oracle makes its own write."""
+    before = (case.key_caches[0].clone(), case.value_caches[0].clone())
     pa.pa_reshape_and_cache(case.new_keys[0], case.new_values[0], case.key_caches[0],
                             case.value_caches[0], case.slot_mapping)
+    return before
 
 
 def _full_check(case, tag=""):
     """Oracle over every row of every chunk (small cases)."""
     say(f"[prefill] {case.name} {tag}")
-    _write_chunk(case)
+    kb, vb = _write_chunk(case)
     out = gpu_prefill(case)
     torch.cuda.synchronize()
     p = case.prefill
     nd = case.num_decode_seqs
     lay = case.layout
+    kc, vc = oracle.reshape_and_cache_ref(
+        to_numpy_bits(case.new_keys[0]), to_numpy_bits(case.new_values[0]), to_numpy_bits(kb),
+        to_numpy_bits(vb), case.slot_mapping.cpu().numpy())
     want = oracle.prefill_chunk_ref(
-        to_numpy_bits(p.query), to_numpy_bits(case.key_caches[0]),
-        to_numpy_bits(case.value_caches[0]), lay.block_tables[nd:], lay.context_lens[nd:],
+        to_numpy_bits(p.query), kc, vc, lay.block_tables[nd:], lay.context_lens[nd:],
         p.cu_q_lens.cpu().numpy(), case.scale)
     got = out.cpu().numpy()
     assert np.all(np.isfinite(got))
@@ -89,12 +95,12 @@ def test_c5_chunk_sampled(prefix):
         case = make_case(name="c5_unaligned", seed=55, context_lens=[100, 2000], num_q_heads=16,
                          num_kv_heads=4, head_dim=256, block_size=16, device=DEV,
                          write_new_token=True, prefill_chunks=[(prefix, 512)])
-    _write_chunk(case)
+    kb, vb = _write_chunk(case)
     out = gpu_prefill(case)
     torch.cuda.synchronize()
     rows = [0, 1, 15, 16, 17, 255, 256, 300, 510, 511]
     got = out.cpu().numpy()[rows]
-    want = oracle_prefill_rows(case, 0, rows)
+    want = oracle_prefill_rows(case, 0, rows, kb, vb)
     err = max_abs_err(got, want)
     say(f"[prefill] c5 prefix {prefix}: sampled max-abs err {err:.3e}")
     assert np.all(np.isfinite(out.cpu().numpy()))

@@ -154,6 +154,9 @@ class DecodeCase:
     new_keys: List[torch.Tensor] = field(default_factory=list)    # per layer [T, H_kv, d]
     new_values: List[torch.Tensor] = field(default_factory=list)
     prefill: Optional[PrefillPart] = None
+    kv_fp8: bool = False            # caches hold E4M3 codes (uint8)
+    k_scales: List[torch.Tensor] = field(default_factory=list)   # per layer float32 [H_kv]
+    v_scales: List[torch.Tensor] = field(default_factory=list)
 
     @property
     def num_seqs(self):
@@ -183,11 +186,38 @@ def _poison_unowned(cache, used_slots):
     cache.masked_fill_(unowned[:, None, :, None], float("nan"))
 
 
+# E4M3 code of NaN (S.1111.111), the poison of unowned slots in an FP8 cache.
+FP8_NAN_CODE = 0x7F
+
+
+def _fp8_codes(shape, device, gen):
+    """E4M3 codes whose values spread like N(0, 64^2): normal draws scaled by
+    64, clipped to the format's +-448 and cast with torch's own E4M3 cast.
+    The per-head scales are separate inputs, so the caches dequantize to
+    roughly N(0, (64 s)^2)."""
+    x = torch.randn(shape, generator=gen, device=device, dtype=F32).mul_(64.0).clamp_(-448.0, 448.0)
+    return x.to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def _fp8_scales(num_kv_heads, device, gen):
+    """Per-head float32 scales drawn around 1/64 (uniform in [0.5, 2] / 64)."""
+    u = torch.rand(num_kv_heads, generator=gen, device=device, dtype=F32)
+    return (0.5 + 1.5 * u) / 64.0
+
+
+def _poison_unowned_codes(cache, used_slots):
+    block_size = cache.shape[2]
+    used = torch.as_tensor(used_slots, device=cache.device).to(torch.int64)
+    slot_idx = torch.arange(block_size, device=cache.device)
+    unowned = slot_idx[None, :] >= used[:, None]
+    cache.masked_fill_(unowned[:, None, :, None], FP8_NAN_CODE)
+
+
 def make_case(*, name, seed, context_lens, num_q_heads, num_kv_heads, head_dim,
               block_size, dtype=BF16, device="cpu", num_layers=1, pool_slack=0.1,
               exact_pool=False, shared_prefix=None, pool_blocks=None,
               write_new_token=False, prefill_chunks=(), poison=True, gen_device=None,
-              structure_only=False):
+              structure_only=False, kv_fp8=False):
     """Build a decode (+ optional prefill-chunk) case.
 
     context_lens: decode sequences' lengths, new token included.
@@ -199,6 +229,9 @@ def make_case(*, name, seed, context_lens, num_q_heads, num_kv_heads, head_dim,
     gen_device: where values are drawn (defaults to ``device``); c1_tiny draws
         on the host and moves the result.
     structure_only: draw lengths, tables and slots but no value tensors.
+    kv_fp8: the caches hold E4M3 codes (uint8) with per-layer, per-head
+        float32 scales in ``k_scales`` / ``v_scales``; queries and new K/V rows
+        keep ``dtype``; unowned slots hold the NaN code.
     """
     rng = np.random.default_rng(seed)
     gen_device = torch.device(gen_device or device)
@@ -230,12 +263,22 @@ def make_case(*, name, seed, context_lens, num_q_heads, num_kv_heads, head_dim,
     gen.manual_seed(int(seed))
     kv_shape = (layout.num_blocks, num_kv_heads, block_size, head_dim)
     key_caches, value_caches, queries, new_keys, new_values = [], [], [], [], []
+    k_scales, v_scales = [], []
     for _ in range(0 if structure_only else num_layers):
-        kc = _randn(kv_shape, dtype, gen_device, gen)
-        vc = _randn(kv_shape, dtype, gen_device, gen)
-        if poison:
-            _poison_unowned(kc, layout.used_slots)
-            _poison_unowned(vc, layout.used_slots)
+        if kv_fp8:
+            kc = _fp8_codes(kv_shape, gen_device, gen)
+            vc = _fp8_codes(kv_shape, gen_device, gen)
+            if poison:
+                _poison_unowned_codes(kc, layout.used_slots)
+                _poison_unowned_codes(vc, layout.used_slots)
+            k_scales.append(_fp8_scales(num_kv_heads, gen_device, gen).to(device))
+            v_scales.append(_fp8_scales(num_kv_heads, gen_device, gen).to(device))
+        else:
+            kc = _randn(kv_shape, dtype, gen_device, gen)
+            vc = _randn(kv_shape, dtype, gen_device, gen)
+            if poison:
+                _poison_unowned(kc, layout.used_slots)
+                _poison_unowned(vc, layout.used_slots)
         key_caches.append(kc.to(device))
         value_caches.append(vc.to(device))
         queries.append(_randn((num_dec, num_q_heads, head_dim), dtype, gen_device, gen).to(device))
@@ -268,6 +311,7 @@ def make_case(*, name, seed, context_lens, num_q_heads, num_kv_heads, head_dim,
         slot_mapping=(torch.as_tensor(np.asarray(slots, dtype=np.int64)).to(device)
                       if num_new else None),
         new_keys=new_keys, new_values=new_values, prefill=prefill,
+        kv_fp8=kv_fp8, k_scales=k_scales, v_scales=v_scales,
     )
 
 
