@@ -20,6 +20,9 @@ definitions state:
 * ``accounting``                      - KV footprint closed form and slot
                                         accounting for paged vs contiguous
                                         allocation.
+* ``block_manager``                   - block pool with on-demand allocation,
+                                        reference-counted sharing, copy-on-write
+                                        at divergence, and the block copy.
 * ``fp8``                             - E4M3 code values, the saturating
                                         round-to-nearest-even quantizer with
                                         per-head scales, FP8 scatter and decode
@@ -39,7 +42,7 @@ from .accounting import (  # noqa: F401
     kv_bytes,
     paged_slots,
 )
-from . import fp8  # noqa: F401
+from . import block_manager, fp8  # noqa: F401
 from .dense_ref import dense_attention_ref  # noqa: F401
 from .numerics import bf16_bits_to_f64, to_f64  # noqa: F401
 from .paged_ref import decode_ref, prefill_chunk_ref, reshape_and_cache_ref  # noqa: F401
