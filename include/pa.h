@@ -71,7 +71,8 @@ extern "C" {
 
 typedef enum {
   PA_DTYPE_F32 = 0,   /* IEEE binary32 */
-  PA_DTYPE_BF16 = 1   /* bfloat16: the top 16 bits of a binary32 */
+  PA_DTYPE_BF16 = 1,  /* bfloat16: the top 16 bits of a binary32 */
+  PA_DTYPE_FP8_E4M3 = 2  /* OCP E4M3 codes (block copies only; see the FP8 entry points) */
 } pa_dtype_t;
 
 typedef enum {
@@ -81,7 +82,9 @@ typedef enum {
   PA_ERR_UNSUPPORTED = 3,
   PA_ERR_ALIGN = 4,
   PA_ERR_WORKSPACE = 5,
-  PA_ERR_HIP = 6
+  PA_ERR_HIP = 6,
+  PA_ERR_OUT_OF_BLOCKS = 7,  /* block manager: the pool lacks the blocks asked for */
+  PA_ERR_STATE = 8           /* block manager: unknown or duplicate sequence id */
 } pa_status_t;
 
 /*

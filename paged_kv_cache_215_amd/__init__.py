@@ -12,7 +12,10 @@ HIP kernels behind the C ABI in ``include/pa.h``:
                              the matrix cores;
 * ``pa_reshape_and_cache_fp8`` / ``pa_decode_fp8`` - the same scatter and
                              decode over an FP8 (E4M3) cache with one scale
-                             per KV head for K and for V.
+                             per KV head for K and for V;
+* ``BlockManager`` / ``pa_copy_blocks`` - the host block manager (on-demand
+                             blocks, reference-counted sharing, copy-on-write)
+                             and the device block copy it asks for.
 
 The Python functions below only marshal torch tensors to that ABI.
 """
@@ -21,10 +24,13 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     PA_DTYPE_BF16,
     PA_DTYPE_F32,
+    PA_DTYPE_FP8_E4M3,
     SIGNATURES,
+    BlockManager,
     PaError,
     lib,
     decode_workspace,
+    pa_copy_blocks,
     pa_decode,
     pa_decode_fp8,
     pa_decode_workspace_init,

@@ -19,9 +19,12 @@ LIB_PATH = os.path.join(_PKG, "libpa.so")
 PA_DTYPE_F32 = 0
 PA_DTYPE_BF16 = 1
 
+PA_DTYPE_FP8_E4M3 = 2
+
 STATUS_NAMES = {
     0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED",
-    4: "PA_ERR_ALIGN", 5: "PA_ERR_WORKSPACE", 6: "PA_ERR_HIP",
+    4: "PA_ERR_ALIGN", 5: "PA_ERR_WORKSPACE", 6: "PA_ERR_HIP", 7: "PA_ERR_OUT_OF_BLOCKS",
+    8: "PA_ERR_STATE",
 }
 
 # Exported symbols and their C signatures (mirrors include/pa.h).
@@ -39,6 +42,20 @@ SIGNATURES = {
     "pa_prefill_chunk_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_prefill_chunk": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                 _i32, _i32, _i32, _i64, _i32, _f32, _i32, _vp, _sz, _vp]),
+    "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i32, _vp]),
+    "pa_bm_create": (_i32, [_i64, _i32, _i32, ctypes.POINTER(_vp)]),
+    "pa_bm_destroy": (None, [_vp]),
+    "pa_bm_add": (_i32, [_vp, _i64]),
+    "pa_bm_fork": (_i32, [_vp, _i64, _i64]),
+    "pa_bm_append": (_i32, [_vp, _i64, _i32, _vp]),
+    "pa_bm_free": (_i32, [_vp, _i64]),
+    "pa_bm_num_free": (_i64, [_vp]),
+    "pa_bm_length": (_i64, [_vp, _i64]),
+    "pa_bm_blocks_needed": (_i64, [_vp, _i64, _i32]),
+    "pa_bm_refcount": (_i32, [_vp, _i64]),
+    "pa_bm_table": (_i32, [_vp, _i64, _vp, _i32]),
+    "pa_bm_tables": (_i32, [_vp, _vp, _i32, _vp, _i32, _vp]),
+    "pa_bm_take_copies": (_i64, [_vp, _vp, _i64]),
     "pa_status_string": (ctypes.c_char_p, [_i32]),
     "pa_version": (_i32, []),
 }
@@ -84,6 +101,8 @@ def _dtype_code(t):
         return PA_DTYPE_BF16
     if t.dtype == torch.float32:
         return PA_DTYPE_F32
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return PA_DTYPE_FP8_E4M3
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
@@ -255,3 +274,102 @@ def pa_prefill_chunk(query, key_cache, value_cache, block_tables, context_lens, 
         int(max_context_len), float(scale), _dtype_code(query), _ptr(workspace),
         workspace.numel() if workspace is not None else 0, _stream(dev)))
     return out
+
+
+def pa_copy_blocks(key_cache, value_cache, pairs):
+    """Copy block src to block dst of both caches for every row (src, dst) of
+    the int64 [P, 2] device tensor ``pairs`` (pairs must be independent)."""
+    dev = _dev(key_cache, value_cache, pairs)
+    if pairs.dtype != torch.int64 or (pairs.numel() and pairs.shape[-1] != 2):
+        raise TypeError("pairs must be int64 [num_pairs, 2]")
+    if key_cache.dtype != value_cache.dtype:
+        raise TypeError("key and value caches must share a dtype")
+    num_blocks, num_kv_heads, block_size, head_dim = key_cache.shape
+    _check("pa_copy_blocks", lib().pa_copy_blocks(
+        _ptr(key_cache), _ptr(value_cache), _ptr(pairs), pairs.numel() // 2, num_kv_heads,
+        head_dim, block_size, num_blocks, _dtype_code(key_cache), _stream(dev)))
+
+
+class BlockManager:
+    """The host block manager of include/pa_blocks.h (C++ in libpa.so):
+    on-demand blocks from a LIFO pool, reference-counted sharing by fork, and
+    copy-on-write pairs for pa_copy_blocks. Not thread-safe."""
+
+    def __init__(self, num_blocks, block_size, max_blocks_per_seq):
+        self._lib = lib()
+        h = _vp()
+        _check("pa_bm_create", self._lib.pa_bm_create(num_blocks, block_size, max_blocks_per_seq,
+                                                      ctypes.byref(h)))
+        self._h = h
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        self.max_blocks_per_seq = max_blocks_per_seq
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def add(self, seq):
+        return self._lib.pa_bm_add(self._h, seq)
+
+    def fork(self, parent, child):
+        return self._lib.pa_bm_fork(self._h, parent, child)
+
+    def append(self, seq, num_tokens):
+        """(status, slots): slots is an int64 numpy array of num_tokens slots."""
+        import numpy as np
+        slots = np.empty(max(num_tokens, 0), dtype=np.int64)
+        st = self._lib.pa_bm_append(self._h, seq, num_tokens, slots.ctypes.data_as(_vp))
+        return st, (slots if st == 0 else slots[:0])
+
+    def free(self, seq):
+        return self._lib.pa_bm_free(self._h, seq)
+
+    def num_free(self):
+        return int(self._lib.pa_bm_num_free(self._h))
+
+    def length(self, seq):
+        return int(self._lib.pa_bm_length(self._h, seq))
+
+    def blocks_needed(self, seq, num_tokens):
+        return int(self._lib.pa_bm_blocks_needed(self._h, seq, num_tokens))
+
+    def refcount(self, block):
+        return int(self._lib.pa_bm_refcount(self._h, block))
+
+    def table(self, seq):
+        import numpy as np
+        out = np.empty(self.max_blocks_per_seq, dtype=np.int32)
+        n = self._lib.pa_bm_table(self._h, seq, out.ctypes.data_as(_vp), out.size)
+        if n < 0:
+            raise KeyError(seq)
+        return out[:n].copy()
+
+    def tables(self, seqs, row_stride=None):
+        """(tables int32 [len(seqs), row_stride], context_lens int32) for one step."""
+        import numpy as np
+        seqs = np.ascontiguousarray(seqs, dtype=np.int64)
+        stride = row_stride or self.max_blocks_per_seq
+        tables = np.empty((seqs.size, stride), dtype=np.int32)
+        lens = np.empty(seqs.size, dtype=np.int32)
+        _check("pa_bm_tables", self._lib.pa_bm_tables(
+            self._h, seqs.ctypes.data_as(_vp), seqs.size, tables.ctypes.data_as(_vp), stride,
+            lens.ctypes.data_as(_vp)))
+        return tables, lens
+
+    def take_copies(self, max_pairs=1 << 16):
+        """One run of independent (src, dst) pairs as an int64 [P, 2] array."""
+        import numpy as np
+        pairs = np.empty((max_pairs, 2), dtype=np.int64)
+        n = self._lib.pa_bm_take_copies(self._h, pairs.ctypes.data_as(_vp), max_pairs)
+        return pairs[:n].copy()

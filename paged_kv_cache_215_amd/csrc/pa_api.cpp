@@ -3,6 +3,7 @@
 // every entry point are in include/pa.h.
 
 #include "pa.h"
+#include "pa_blocks.h"
 
 #include <hip/hip_runtime.h>
 
@@ -340,6 +341,31 @@ pa_status_t pa_prefill_chunk(float* out, const void* query, const void* key_cach
   return from_hip(pa::launch_prefill(a, static_cast<hipStream_t>(stream)));
 }
 
+pa_status_t pa_copy_blocks(void* key_cache, void* value_cache, const int64_t* pairs,
+                           int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int64_t num_blocks, pa_dtype_t dtype,
+                           void* stream) {
+  if (num_pairs < 0) return PA_ERR_SHAPE;
+  if (num_pairs == 0) return PA_OK;
+  if (!key_cache || !value_cache || !pairs) return PA_ERR_NULL;
+  if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return PA_ERR_SHAPE;
+  if (!supported_block(block_size) || !supported_dim(head_dim) ||
+      (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16 && dtype != PA_DTYPE_FP8_E4M3))
+    return PA_ERR_UNSUPPORTED;
+  if (!aligned(key_cache, 16) || !aligned(value_cache, 16) || !aligned(pairs, 8))
+    return PA_ERR_ALIGN;
+  const int64_t eb = dtype == PA_DTYPE_F32 ? 4 : dtype == PA_DTYPE_BF16 ? 2 : 1;
+  pa::CopyArgs a;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.pairs = pairs;
+  a.num_pairs = num_pairs;
+  a.num_blocks = num_blocks;
+  a.block_chunks = (int64_t)num_kv_heads * block_size * head_dim * eb / 16;
+  return from_hip(pa::launch_copy_blocks(a, static_cast<hipStream_t>(stream)));
+}
+
 const char* pa_status_string(pa_status_t status) {
   switch (status) {
     case PA_OK: return "ok";
@@ -349,6 +375,8 @@ const char* pa_status_string(pa_status_t status) {
     case PA_ERR_ALIGN: return "misaligned pointer (tensors need 16 bytes, index arrays their element size)";
     case PA_ERR_WORKSPACE: return "workspace too small";
     case PA_ERR_HIP: return "HIP launch failed";
+    case PA_ERR_OUT_OF_BLOCKS: return "the block pool lacks the blocks asked for";
+    case PA_ERR_STATE: return "unknown or duplicate sequence id";
   }
   return "unknown status";
 }

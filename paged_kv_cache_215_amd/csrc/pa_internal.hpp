@@ -73,6 +73,15 @@ struct ScatterFp8Args {
   bool src_bf16;         // source rows are BF16 (else float32)
 };
 
+struct CopyArgs {
+  void* key_cache;       // [num_blocks, Hkv, bs, D]
+  void* value_cache;
+  const int64_t* pairs;  // [num_pairs][2] (src, dst), device
+  int64_t num_pairs;
+  int64_t num_blocks;
+  int64_t block_chunks;  // 16-byte chunks per block of one cache
+};
+
 struct PrefillArgs {
   float* out;            // [total_q, Hq, D] float32
   float* part_o;         // split-context partials (may be unused)
@@ -114,6 +123,7 @@ hipError_t launch_decode(const DecodeArgs& a, KvType kv, hipStream_t stream);
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t stream);
 hipError_t launch_scatter(const ScatterArgs& a, hipStream_t stream);
 hipError_t launch_scatter_fp8(const ScatterFp8Args& a, hipStream_t stream);
+hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
 
 int prefill_kv_splits(int num_seqs, int max_q_len, int num_q_heads, int num_kv_heads,
                       int head_dim, int max_context_len);
