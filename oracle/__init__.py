@@ -23,6 +23,9 @@ definitions state:
 * ``block_manager``                   - block pool with on-demand allocation,
                                         reference-counted sharing, copy-on-write
                                         at divergence, and the block copy.
+* ``scheduler``                       - iteration-level batching: eject, resume,
+                                        admit, chunked prefill, decode, and
+                                        preemption by swapping to host blocks.
 * ``fp8``                             - E4M3 code values, the saturating
                                         round-to-nearest-even quantizer with
                                         per-head scales, FP8 scatter and decode
@@ -42,7 +45,7 @@ from .accounting import (  # noqa: F401
     kv_bytes,
     paged_slots,
 )
-from . import block_manager, fp8  # noqa: F401
+from . import block_manager, fp8, scheduler  # noqa: F401
 from .dense_ref import dense_attention_ref  # noqa: F401
 from .numerics import bf16_bits_to_f64, to_f64  # noqa: F401
 from .paged_ref import decode_ref, prefill_chunk_ref, reshape_and_cache_ref  # noqa: F401
