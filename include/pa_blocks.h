@@ -107,6 +107,33 @@ pa_status_t pa_copy_blocks(void* key_cache, void* value_cache, const int64_t* pa
                            int32_t block_size, int64_t num_blocks, pa_dtype_t dtype,
                            void* stream);
 
+/*
+ * Swapping for preemption: when memory runs short a running sequence's blocks
+ * are moved to host memory and its device blocks freed; it resumes later
+ * with its context intact (Dissecting vLLM, "Continuous Batching: Breaking
+ * the Sequence Barrier"). Both calls copy whole blocks, K and V, for each
+ * pair of pairs[num_pairs][2] (int64; device memory or pinned host memory):
+ *   pa_swap_out: pair (device block, host block), device caches -> host pools
+ *   pa_swap_in:  pair (host block, device block), host pools -> device caches
+ * host_key, host_value: [num_host_blocks, num_kv_heads, block_size, head_dim]
+ * in pinned host memory (hipHostMalloc, or torch pin_memory), which the kernel
+ * reads or writes directly, one launch per batch. Pointer kinds are checked
+ * before any launch: pageable host memory or device memory as a host pool is
+ * PA_ERR_UNSUPPORTED. A pair outside the pools is skipped. Pairs of one call
+ * must be independent (the scheduler's plans are). Asynchronous on stream:
+ * the host pool may be read only after the stream has drained.
+ */
+pa_status_t pa_swap_out(const void* key_cache, const void* value_cache, void* host_key,
+                        void* host_value, const int64_t* pairs, int32_t num_pairs,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                        int64_t num_blocks, int64_t num_host_blocks, pa_dtype_t dtype,
+                        void* stream);
+pa_status_t pa_swap_in(void* key_cache, void* value_cache, const void* host_key,
+                       const void* host_value, const int64_t* pairs, int32_t num_pairs,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                       int64_t num_blocks, int64_t num_host_blocks, pa_dtype_t dtype,
+                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -150,3 +150,15 @@ def copy_blocks_ref(key_cache, value_cache, pairs):
         kc[dst] = kc[src]
         vc[dst] = vc[src]
     return kc, vc
+
+
+def move_blocks_ref(src_key, src_value, dst_key, dst_value, pairs):
+    """Copies of the destination pools with block ``dst`` set to source block
+    ``src`` for every pair (swapping between the device cache and a host pool:
+    Dissecting vLLM, "Continuous Batching: Breaking the Sequence Barrier")."""
+    dk = np.array(dst_key, copy=True)
+    dv = np.array(dst_value, copy=True)
+    for src, dst in pairs:
+        dk[dst] = src_key[src]
+        dv[dst] = src_value[src]
+    return dk, dv

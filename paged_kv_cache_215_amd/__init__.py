@@ -15,7 +15,10 @@ HIP kernels behind the C ABI in ``include/pa.h``:
                              per KV head for K and for V;
 * ``BlockManager`` / ``pa_copy_blocks`` - the host block manager (on-demand
                              blocks, reference-counted sharing, copy-on-write)
-                             and the device block copy it asks for.
+                             and the device block copy it asks for;
+* ``pa_swap_out`` / ``pa_swap_in`` - batched block moves between the device
+                             cache and a pinned host pool (preemption);
+* ``Scheduler``            - the iteration-level batching scheduler (C++).
 
 The Python functions below only marshal torch tensors to that ABI.
 """
@@ -27,10 +30,13 @@ from ._lib import (  # noqa: F401
     PA_DTYPE_FP8_E4M3,
     SIGNATURES,
     BlockManager,
+    Scheduler,
     PaError,
     lib,
     decode_workspace,
     pa_copy_blocks,
+    pa_swap_in,
+    pa_swap_out,
     pa_decode,
     pa_decode_fp8,
     pa_decode_workspace_init,

@@ -56,6 +56,15 @@ SIGNATURES = {
     "pa_bm_table": (_i32, [_vp, _i64, _vp, _i32]),
     "pa_bm_tables": (_i32, [_vp, _vp, _i32, _vp, _i32, _vp]),
     "pa_bm_take_copies": (_i64, [_vp, _vp, _i64]),
+    "pa_swap_out": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i64, _i32,
+                           _vp]),
+    "pa_swap_in": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i64, _i32,
+                          _vp]),
+    "pa_sched_create": (_i32, [_vp, _vp, _vp, _i32, ctypes.POINTER(_vp)]),
+    "pa_sched_destroy": (None, [_vp]),
+    "pa_sched_done": (_i32, [_vp]),
+    "pa_sched_step": (_i32, [_vp, _vp]),
+    "pa_sched_blocks": (_vp, [_vp]),
     "pa_status_string": (ctypes.c_char_p, [_i32]),
     "pa_version": (_i32, []),
 }
@@ -290,6 +299,35 @@ def pa_copy_blocks(key_cache, value_cache, pairs):
         head_dim, block_size, num_blocks, _dtype_code(key_cache), _stream(dev)))
 
 
+def _swap(fn_name, key_cache, value_cache, host_key, host_value, pairs):
+    dev = _dev(key_cache, value_cache)
+    for t in (host_key, host_value):
+        if t.device.type != "cpu" or not t.is_pinned() or not t.is_contiguous():
+            raise ValueError("host pools must be contiguous pinned CPU tensors")
+        if t.dtype != key_cache.dtype or t.shape[1:] != key_cache.shape[1:]:
+            raise TypeError("host pools must match the caches' dtype and block shape")
+    if pairs.dtype != torch.int64 or not pairs.is_contiguous() or \
+            (pairs.numel() and pairs.shape[-1] != 2):
+        raise TypeError("pairs must be contiguous int64 [num_pairs, 2]")
+    if pairs.device.type == "cpu" and not pairs.is_pinned():
+        raise ValueError("pairs must be on the GPU or in pinned host memory")
+    num_blocks, num_kv_heads, block_size, head_dim = key_cache.shape
+    _check(fn_name, getattr(lib(), fn_name)(
+        _ptr(key_cache), _ptr(value_cache), _ptr(host_key), _ptr(host_value), _ptr(pairs),
+        pairs.numel() // 2, num_kv_heads, head_dim, block_size, num_blocks, host_key.shape[0],
+        _dtype_code(key_cache), _stream(dev)))
+
+
+def pa_swap_out(key_cache, value_cache, host_key, host_value, pairs):
+    """Copy device block b to host block h for every row (b, h) of pairs."""
+    _swap("pa_swap_out", key_cache, value_cache, host_key, host_value, pairs)
+
+
+def pa_swap_in(key_cache, value_cache, host_key, host_value, pairs):
+    """Copy host block h to device block b for every row (h, b) of pairs."""
+    _swap("pa_swap_in", key_cache, value_cache, host_key, host_value, pairs)
+
+
 class BlockManager:
     """The host block manager of include/pa_blocks.h (C++ in libpa.so):
     on-demand blocks from a LIFO pool, reference-counted sharing by fork, and
@@ -373,3 +411,103 @@ class BlockManager:
         pairs = np.empty((max_pairs, 2), dtype=np.int64)
         n = self._lib.pa_bm_take_copies(self._h, pairs.ctypes.data_as(_vp), max_pairs)
         return pairs[:n].copy()
+
+
+class _SchedConfig(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int64), ("num_host_blocks", ctypes.c_int64),
+                ("block_size", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
+                ("max_batch", ctypes.c_int32), ("chunk_tokens", ctypes.c_int32)]
+
+
+_P64 = ctypes.POINTER(ctypes.c_int64)
+_P32 = ctypes.POINTER(ctypes.c_int32)
+
+
+class _StepPlan(ctypes.Structure):
+    _fields_ = [("iteration", ctypes.c_int32),
+                ("num_decode", ctypes.c_int32), ("decode_seqs", _P64), ("decode_slots", _P64),
+                ("decode_context", _P32),
+                ("num_prefill", ctypes.c_int32), ("prefill_seqs", _P64), ("prefill_start", _P32),
+                ("prefill_cu", _P32), ("prefill_slots", _P64),
+                ("num_swap_out", ctypes.c_int32), ("swap_out", _P64),
+                ("num_swap_in", ctypes.c_int32), ("swap_in", _P64),
+                ("num_finished", ctypes.c_int32), ("finished", _P64),
+                ("num_admitted", ctypes.c_int32), ("admitted", _P64),
+                ("num_preempted", ctypes.c_int32), ("preempted", _P64),
+                ("num_resumed", ctypes.c_int32), ("resumed", _P64)]
+
+
+class Scheduler:
+    """The iteration-level batching scheduler of include/pa_sched.h (C++ in
+    libpa.so) over an offline batch of (prompt_len, output_len) requests.
+    ``step()`` returns the iteration's plan as numpy arrays."""
+
+    def __init__(self, requests, *, num_blocks, num_host_blocks, block_size, max_blocks_per_seq,
+                 max_batch, chunk_tokens):
+        import numpy as np
+        self._lib = lib()
+        prompts = np.ascontiguousarray([int(p) for p, _ in requests], dtype=np.int32)
+        outputs = np.ascontiguousarray([int(o) for _, o in requests], dtype=np.int32)
+        cfg = _SchedConfig(num_blocks, num_host_blocks, block_size, max_blocks_per_seq, max_batch,
+                           chunk_tokens)
+        h = _vp()
+        _check("pa_sched_create", self._lib.pa_sched_create(
+            ctypes.byref(cfg), prompts.ctypes.data_as(_vp), outputs.ctypes.data_as(_vp),
+            len(requests), ctypes.byref(h)))
+        self._h = h
+        self.block_size = block_size
+        self.max_blocks_per_seq = max_blocks_per_seq
+        self.requests = [(int(p), int(o)) for p, o in requests]
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.pa_sched_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def done(self):
+        return bool(self._lib.pa_sched_done(self._h))
+
+    def step(self):
+        import numpy as np
+        plan = _StepPlan()
+        _check("pa_sched_step", self._lib.pa_sched_step(self._h, ctypes.byref(plan)))
+
+        def arr(ptr, n, dtype):
+            if n == 0:
+                return np.zeros(0, dtype=dtype)
+            return np.ctypeslib.as_array(ptr, shape=(n,)).astype(dtype, copy=True)
+
+        npf = plan.num_prefill
+        cu = arr(plan.prefill_cu, npf + 1, np.int32)
+        return {
+            "iteration": plan.iteration,
+            "decode_seqs": arr(plan.decode_seqs, plan.num_decode, np.int64),
+            "decode_slots": arr(plan.decode_slots, plan.num_decode, np.int64),
+            "decode_context": arr(plan.decode_context, plan.num_decode, np.int32),
+            "prefill_seqs": arr(plan.prefill_seqs, npf, np.int64),
+            "prefill_start": arr(plan.prefill_start, npf, np.int32),
+            "prefill_cu": cu,
+            "prefill_slots": arr(plan.prefill_slots, int(cu[-1]), np.int64),
+            "swap_out": arr(plan.swap_out, 2 * plan.num_swap_out, np.int64).reshape(-1, 2),
+            "swap_in": arr(plan.swap_in, 2 * plan.num_swap_in, np.int64).reshape(-1, 2),
+            "finished": arr(plan.finished, plan.num_finished, np.int64),
+            "admitted": arr(plan.admitted, plan.num_admitted, np.int64),
+            "preempted": arr(plan.preempted, plan.num_preempted, np.int64),
+            "resumed": arr(plan.resumed, plan.num_resumed, np.int64),
+        }
+
+    def tables(self, seqs, row_stride=None):
+        """(tables int32 [len(seqs), row_stride], context_lens int32) of live sequences."""
+        import numpy as np
+        seqs = np.ascontiguousarray(seqs, dtype=np.int64)
+        stride = row_stride or self.max_blocks_per_seq
+        tables = np.empty((seqs.size, stride), dtype=np.int32)
+        lens = np.empty(seqs.size, dtype=np.int32)
+        bm = self._lib.pa_sched_blocks(self._h)
+        _check("pa_bm_tables", self._lib.pa_bm_tables(
+            bm, seqs.ctypes.data_as(_vp), seqs.size, tables.ctypes.data_as(_vp), stride,
+            lens.ctypes.data_as(_vp)))
+        return tables, lens

@@ -83,6 +83,65 @@ DecodeGeometry decode_geometry(int32_t num_seqs, int32_t hq, int32_t hkv, int32_
 
 pa_status_t from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
+int64_t dtype_bytes(pa_dtype_t t) { return t == PA_DTYPE_F32 ? 4 : t == PA_DTYPE_BF16 ? 2 : 1; }
+
+// Device-visible address of p: device memory as is, pinned host memory
+// through its mapping; nullptr for memory a kernel cannot reach (pageable
+// host memory, unknown pointers). The query's error, if any, is cleared so
+// that it cannot be reported by a later launch check.
+const void* device_view(const void* p, bool allow_device) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (attr.type == hipMemoryTypeDevice) return allow_device ? p : nullptr;
+  if (attr.type != hipMemoryTypeHost || !attr.devicePointer) return nullptr;
+  const char* base_h = static_cast<const char*>(attr.hostPointer ? attr.hostPointer : p);
+  return static_cast<const char*>(attr.devicePointer) + (static_cast<const char*>(p) - base_h);
+}
+
+// Swap of whole blocks between the device caches and pinned host pools:
+// out = device -> host, else host -> device. Pointer kinds are checked
+// before any launch.
+pa_status_t swap_impl(const void* key_cache, const void* value_cache, const void* host_key,
+                      const void* host_value, const int64_t* pairs, int32_t num_pairs,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                      int64_t num_blocks, int64_t num_host_blocks, pa_dtype_t dtype,
+                      void* stream, bool out) {
+  if (num_pairs < 0) return PA_ERR_SHAPE;
+  if (num_pairs == 0) return PA_OK;
+  if (!key_cache || !value_cache || !host_key || !host_value || !pairs) return PA_ERR_NULL;
+  if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0 ||
+      num_host_blocks <= 0)
+    return PA_ERR_SHAPE;
+  if (!supported_block(block_size) || !supported_dim(head_dim) ||
+      (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16 && dtype != PA_DTYPE_FP8_E4M3))
+    return PA_ERR_UNSUPPORTED;
+  if (!aligned(key_cache, 16) || !aligned(value_cache, 16) || !aligned(host_key, 16) ||
+      !aligned(host_value, 16) || !aligned(pairs, 8))
+    return PA_ERR_ALIGN;
+  const void* hk = device_view(host_key, false);
+  const void* hv = device_view(host_value, false);
+  const void* pp = device_view(pairs, true);
+  const void* dk = device_view(key_cache, true);
+  const void* dv = device_view(value_cache, true);
+  if (!hk || !hv || !pp || !dk || !dv) return PA_ERR_UNSUPPORTED;  // host pools must be pinned
+  key_cache = dk;
+  value_cache = dv;
+  pa::CopyArgs a;
+  a.src_key = out ? key_cache : hk;
+  a.src_value = out ? value_cache : hv;
+  a.dst_key = const_cast<void*>(out ? hk : key_cache);
+  a.dst_value = const_cast<void*>(out ? hv : value_cache);
+  a.pairs = static_cast<const int64_t*>(pp);
+  a.num_pairs = num_pairs;
+  a.src_blocks = out ? num_blocks : num_host_blocks;
+  a.dst_blocks = out ? num_host_blocks : num_blocks;
+  a.block_chunks = (int64_t)num_kv_heads * block_size * head_dim * dtype_bytes(dtype) / 16;
+  return from_hip(pa::launch_copy_blocks(a, static_cast<hipStream_t>(stream)));
+}
+
 // Validation (NULL -> SHAPE -> UNSUPPORTED -> ALIGN -> WORKSPACE) and launch of
 // a decode over a cache of type kv. type_ok is the caller's check of its
 // element types (reported as UNSUPPORTED); an FP8 cache also needs its two
@@ -355,15 +414,35 @@ pa_status_t pa_copy_blocks(void* key_cache, void* value_cache, const int64_t* pa
     return PA_ERR_UNSUPPORTED;
   if (!aligned(key_cache, 16) || !aligned(value_cache, 16) || !aligned(pairs, 8))
     return PA_ERR_ALIGN;
-  const int64_t eb = dtype == PA_DTYPE_F32 ? 4 : dtype == PA_DTYPE_BF16 ? 2 : 1;
   pa::CopyArgs a;
-  a.key_cache = key_cache;
-  a.value_cache = value_cache;
+  a.src_key = key_cache;
+  a.src_value = value_cache;
+  a.dst_key = key_cache;
+  a.dst_value = value_cache;
   a.pairs = pairs;
   a.num_pairs = num_pairs;
-  a.num_blocks = num_blocks;
-  a.block_chunks = (int64_t)num_kv_heads * block_size * head_dim * eb / 16;
+  a.src_blocks = num_blocks;
+  a.dst_blocks = num_blocks;
+  a.block_chunks = (int64_t)num_kv_heads * block_size * head_dim * dtype_bytes(dtype) / 16;
   return from_hip(pa::launch_copy_blocks(a, static_cast<hipStream_t>(stream)));
+}
+
+pa_status_t pa_swap_out(const void* key_cache, const void* value_cache, void* host_key,
+                        void* host_value, const int64_t* pairs, int32_t num_pairs,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                        int64_t num_blocks, int64_t num_host_blocks, pa_dtype_t dtype,
+                        void* stream) {
+  return swap_impl(key_cache, value_cache, host_key, host_value, pairs, num_pairs, num_kv_heads,
+                   head_dim, block_size, num_blocks, num_host_blocks, dtype, stream, true);
+}
+
+pa_status_t pa_swap_in(void* key_cache, void* value_cache, const void* host_key,
+                       const void* host_value, const int64_t* pairs, int32_t num_pairs,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                       int64_t num_blocks, int64_t num_host_blocks, pa_dtype_t dtype,
+                       void* stream) {
+  return swap_impl(key_cache, value_cache, host_key, host_value, pairs, num_pairs, num_kv_heads,
+                   head_dim, block_size, num_blocks, num_host_blocks, dtype, stream, false);
 }
 
 const char* pa_status_string(pa_status_t status) {

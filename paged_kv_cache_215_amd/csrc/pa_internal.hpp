@@ -73,12 +73,17 @@ struct ScatterFp8Args {
   bool src_bf16;         // source rows are BF16 (else float32)
 };
 
+// Whole-block copies from a source pool to a destination pool (the same
+// cache for copy-on-write; the device cache and a pinned host pool for swaps).
 struct CopyArgs {
-  void* key_cache;       // [num_blocks, Hkv, bs, D]
-  void* value_cache;
-  const int64_t* pairs;  // [num_pairs][2] (src, dst), device
+  const void* src_key;   // [src_blocks, Hkv, bs, D]
+  const void* src_value;
+  void* dst_key;         // [dst_blocks, Hkv, bs, D]
+  void* dst_value;
+  const int64_t* pairs;  // [num_pairs][2] (src, dst), device-accessible
   int64_t num_pairs;
-  int64_t num_blocks;
+  int64_t src_blocks;
+  int64_t dst_blocks;
   int64_t block_chunks;  // 16-byte chunks per block of one cache
 };
 

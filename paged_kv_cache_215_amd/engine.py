@@ -1,0 +1,200 @@
+"""Continuous-batching step driver: runs the native scheduler's plans on the
+GPU through the C ABI.
+
+Each iteration (How vLLM gets real throughput on H100s, "Continuous batching
+removes straggler bubbles"; Dissecting vLLM, "Continuous Batching: Breaking
+the Sequence Barrier"; vLLM architecture, memory and benchmarks deep dive,
+"Hardware-level optimizations"):
+
+1. the scheduler (C++, ``Scheduler``) plans the iteration on the host;
+2. swapped-out blocks come back from the pinned host pool (``pa_swap_in``),
+   then a preempted sequence's blocks go out to it (``pa_swap_out``);
+3. for every layer: the iteration's new K/V rows - prompt rows of the
+   prefill chunks and one token per decoding sequence - are written through
+   the slot mapping (``pa_reshape_and_cache``), the chunks attend to their
+   prefix (``pa_prefill_chunk``) and the decode batch attends to its context
+   (``pa_decode``).
+
+The model itself (projections, sampling) is out of scope: queries and new K/V
+rows are inputs the caller provides for each iteration. In graph mode the
+decode-only iterations replay one captured graph of the L layers' scatter and
+decode (record once, replay in one launch: "Hardware-level optimizations"),
+sized for ``max_batch`` sequences: slots, tables and lengths are refreshed in
+static device buffers before each replay; unused batch rows have context 0
+(zero output) and slot -1 (nothing written).
+"""
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+
+class Engine:
+    def __init__(self, requests, *, num_layers, num_q_heads, num_kv_heads, head_dim, block_size,
+                 num_blocks, num_host_blocks, max_blocks_per_seq, max_batch, chunk_tokens,
+                 device="cuda", dtype=torch.bfloat16, use_graph=False):
+        self.dev = torch.device(device)
+        self.dtype = dtype
+        self.L, self.hq, self.hkv, self.d = num_layers, num_q_heads, num_kv_heads, head_dim
+        self.bs = block_size
+        self.max_blocks = max_blocks_per_seq
+        self.max_batch = max_batch
+        self.scale = 1.0 / float(np.sqrt(head_dim))
+        self.sched = L.Scheduler(requests, num_blocks=num_blocks, num_host_blocks=num_host_blocks,
+                                 block_size=block_size, max_blocks_per_seq=max_blocks_per_seq,
+                                 max_batch=max_batch, chunk_tokens=chunk_tokens)
+        shape = (num_blocks, num_kv_heads, block_size, head_dim)
+        hshape = (max(num_host_blocks, 1), num_kv_heads, block_size, head_dim)
+        self.key_caches = [torch.zeros(shape, dtype=dtype, device=self.dev) for _ in range(self.L)]
+        self.value_caches = [torch.zeros(shape, dtype=dtype, device=self.dev)
+                             for _ in range(self.L)]
+        self.host_keys = [torch.zeros(hshape, dtype=dtype).pin_memory() for _ in range(self.L)]
+        self.host_values = [torch.zeros(hshape, dtype=dtype).pin_memory() for _ in range(self.L)]
+        self.max_ctx = max_blocks_per_seq * block_size
+        self.graph_ws = None       # decode workspace captured in the graph
+        self.eager_ws = None       # grown on demand for eager decode calls
+        self.use_graph = use_graph
+        self.graph = None
+        self.decode_tokens = 0
+        self.iterations = 0
+
+    # ---------------------------------------------------------------- helpers
+    def _i64(self, a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int64)).to(self.dev,
+                                                                         non_blocking=True)
+
+    def _i32(self, a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(self.dev,
+                                                                         non_blocking=True)
+
+    def done(self):
+        return self.sched.done()
+
+    def _workspace(self, num_seqs, max_ctx):
+        need = L.pa_decode_workspace_size(num_seqs, self.hq, self.hkv, self.d, self.bs, max_ctx)
+        if self.eager_ws is None or self.eager_ws.numel() < need:
+            self.eager_ws = L.decode_workspace(num_seqs, self.hq, self.hkv, self.d, self.bs,
+                                               max_ctx, self.dev)
+        return self.eager_ws
+
+    # ------------------------------------------------------------------ graph
+    def _static_buffers(self):
+        B = self.max_batch
+        self.g_slots = torch.full((B,), -1, dtype=torch.int64, device=self.dev)
+        self.g_tables = torch.full((B, self.max_blocks), -1, dtype=torch.int32, device=self.dev)
+        self.g_lens = torch.zeros((B,), dtype=torch.int32, device=self.dev)
+        self.g_q = [torch.zeros((B, self.hq, self.d), dtype=self.dtype, device=self.dev)
+                    for _ in range(self.L)]
+        self.g_k = [torch.zeros((B, self.hkv, self.d), dtype=self.dtype, device=self.dev)
+                    for _ in range(self.L)]
+        self.g_v = [torch.zeros((B, self.hkv, self.d), dtype=self.dtype, device=self.dev)
+                    for _ in range(self.L)]
+        self.g_out = [torch.zeros((B, self.hq, self.d), dtype=torch.float32, device=self.dev)
+                      for _ in range(self.L)]
+
+    def _graph_body(self):
+        for layer in range(self.L):
+            L.pa_reshape_and_cache(self.g_k[layer], self.g_v[layer], self.key_caches[layer],
+                                   self.value_caches[layer], self.g_slots)
+            L.pa_decode(self.g_q[layer], self.key_caches[layer], self.value_caches[layer],
+                        self.g_tables, self.g_lens, self.scale, self.max_ctx,
+                        out=self.g_out[layer], workspace=self.graph_ws)
+
+    def _capture(self):
+        self._static_buffers()
+        self.graph_ws = L.decode_workspace(self.max_batch, self.hq, self.hkv, self.d, self.bs,
+                                           self.max_ctx, self.dev)
+        # the body runs once outside capture (one-time library set-up), on
+        # buffers that write nothing (every slot -1, every context 0)
+        side = torch.cuda.Stream(self.dev)
+        side.wait_stream(torch.cuda.current_stream(self.dev))
+        with torch.cuda.stream(side):
+            self._graph_body()
+        torch.cuda.current_stream(self.dev).wait_stream(side)
+        torch.cuda.synchronize(self.dev)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self._graph_body()
+        torch.cuda.synchronize(self.dev)
+
+    # ------------------------------------------------------------------- step
+    def step(self, inputs_fn):
+        """Run one iteration. ``inputs_fn(plan)`` returns the iteration's
+        per-layer inputs: a dict with lists (one tensor per layer) ``q_dec``
+        [n_dec, Hq, d], ``k_dec`` / ``v_dec`` [n_dec, Hkv, d], ``q_pre``
+        [rows, Hq, d], ``k_pre`` / ``v_pre`` [rows, Hkv, d]. Returns
+        (plan, decode outputs per layer, prefill outputs per layer)."""
+        plan = self.sched.step()
+        n_dec = len(plan["decode_seqs"])
+        n_rows = int(plan["prefill_cu"][-1])
+        inputs = inputs_fn(plan)
+        self.iterations += 1
+        self.decode_tokens += n_dec
+
+        if len(plan["swap_in"]):
+            pairs = self._i64(plan["swap_in"])
+            for layer in range(self.L):
+                L.pa_swap_in(self.key_caches[layer], self.value_caches[layer],
+                             self.host_keys[layer], self.host_values[layer], pairs)
+        if len(plan["swap_out"]):
+            pairs = self._i64(plan["swap_out"])
+            for layer in range(self.L):
+                L.pa_swap_out(self.key_caches[layer], self.value_caches[layer],
+                              self.host_keys[layer], self.host_values[layer], pairs)
+
+        dec_tables = dec_lens = None
+        if n_dec:
+            dec_tables, dec_lens = self.sched.tables(plan["decode_seqs"])
+        graph_ok = self.use_graph and n_rows == 0 and n_dec <= self.max_batch
+        if graph_ok and n_dec:
+            if self.graph is None:
+                self._capture()
+            B = self.max_batch
+            slots = np.full(B, -1, dtype=np.int64)
+            slots[:n_dec] = plan["decode_slots"]
+            tables = np.full((B, self.max_blocks), -1, dtype=np.int32)
+            tables[:n_dec] = dec_tables
+            lens = np.zeros(B, dtype=np.int32)
+            lens[:n_dec] = dec_lens
+            self.g_slots.copy_(self._i64(slots))
+            self.g_tables.copy_(self._i32(tables))
+            self.g_lens.copy_(self._i32(lens))
+            for layer in range(self.L):
+                self.g_q[layer][:n_dec].copy_(inputs["q_dec"][layer])
+                self.g_k[layer][:n_dec].copy_(inputs["k_dec"][layer])
+                self.g_v[layer][:n_dec].copy_(inputs["v_dec"][layer])
+            self.graph.replay()
+            return plan, [o[:n_dec] for o in self.g_out], []
+
+        slots = np.concatenate([plan["prefill_slots"], plan["decode_slots"]]).astype(np.int64)
+        slots_d = self._i64(slots) if slots.size else None
+        if n_rows:
+            npf = len(plan["prefill_seqs"])
+            pre_tables, _ = self.sched.tables(plan["prefill_seqs"])
+            cu = plan["prefill_cu"]
+            pre_ctx = plan["prefill_start"] + (cu[1:] - cu[:-1])
+            pt, pc, pcu = self._i32(pre_tables), self._i32(pre_ctx), self._i32(cu)
+            max_q = int((cu[1:] - cu[:-1]).max())
+            max_pre_ctx = int(pre_ctx.max())
+        if n_dec:
+            dt, dl = self._i32(dec_tables), self._i32(dec_lens)
+            max_dec_ctx = int(dec_lens.max())
+            ws = self._workspace(n_dec, max_dec_ctx)
+        dec_out, pre_out = [], []
+        for layer in range(self.L):
+            kc, vc = self.key_caches[layer], self.value_caches[layer]
+            if slots_d is not None:
+                k_new = torch.cat([inputs["k_pre"][layer], inputs["k_dec"][layer]])
+                v_new = torch.cat([inputs["v_pre"][layer], inputs["v_dec"][layer]])
+                L.pa_reshape_and_cache(k_new, v_new, kc, vc, slots_d)
+            if n_rows:
+                pre_out.append(L.pa_prefill_chunk(inputs["q_pre"][layer], kc, vc, pt, pc, pcu,
+                                                  max_q, self.scale, max_pre_ctx))
+            if n_dec:
+                dec_out.append(L.pa_decode(inputs["q_dec"][layer], kc, vc, dt, dl, self.scale,
+                                           max_dec_ctx, workspace=ws))
+        return plan, dec_out, pre_out
+
+    def close(self):
+        self.sched.close()

@@ -200,3 +200,46 @@ def test_fp8_decode_error_order(lib):
     assert lib.pa_decode_fp8(*fp8_decode_args(k_scale=None, num_q_heads=0)) == NULL
     assert lib.pa_decode_fp8(*fp8_decode_args(query_dtype=F32, num_q_heads=14)) == SHAPE
     assert lib.pa_decode_fp8(*fp8_decode_args(query_dtype=F32, v_scale=A + 2)) == UNSUP
+
+
+def copy_args(**over):
+    args = dict(key_cache=A, value_cache=A, pairs=A, num_pairs=4, num_kv_heads=4, head_dim=256,
+                block_size=16, num_blocks=100, dtype=BF16, stream=None)
+    args.update(over)
+    return list(args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(pairs=None), NULL), (dict(value_cache=None), NULL), (dict(num_pairs=-1), SHAPE),
+    (dict(num_blocks=0), SHAPE), (dict(block_size=8), UNSUP), (dict(dtype=3), UNSUP),
+    (dict(key_cache=A + 8), ALIGN), (dict(pairs=A + 4), ALIGN),
+])
+def test_copy_blocks_rejects(lib, over, code):
+    assert lib.pa_copy_blocks(*copy_args(**over)) == code
+
+
+def test_copy_blocks_zero_pairs_is_noop(lib):
+    assert lib.pa_copy_blocks(*copy_args(num_pairs=0, pairs=None)) == OK
+
+
+def swap_args(**over):
+    args = dict(key_cache=A, value_cache=A, host_key=A, host_value=A, pairs=A, num_pairs=2,
+                num_kv_heads=4, head_dim=256, block_size=16, num_blocks=100, num_host_blocks=10,
+                dtype=BF16, stream=None)
+    args.update(over)
+    return list(args.values())
+
+
+@pytest.mark.parametrize("fn", ["pa_swap_out", "pa_swap_in"])
+@pytest.mark.parametrize("over,code", [
+    (dict(host_key=None), NULL), (dict(pairs=None), NULL), (dict(num_pairs=-2), SHAPE),
+    (dict(num_host_blocks=0), SHAPE), (dict(head_dim=100), UNSUP), (dict(dtype=9), UNSUP),
+    (dict(host_value=A + 8), ALIGN), (dict(pairs=A + 1), ALIGN),
+])
+def test_swap_rejects(lib, fn, over, code):
+    assert getattr(lib, fn)(*swap_args(**over)) == code
+
+
+@pytest.mark.parametrize("fn", ["pa_swap_out", "pa_swap_in"])
+def test_swap_zero_pairs_is_noop(lib, fn):
+    assert getattr(lib, fn)(*swap_args(num_pairs=0, host_key=None)) == OK

@@ -274,3 +274,17 @@ def test_planted_block_manager_mistake_fails_a_pin(cls):
             _invariants(bm)
 
     assert fails(sharing) or fails(simulation)
+
+
+def test_move_blocks_ref_round_trip():
+    from oracle.block_manager import move_blocks_ref
+    rng = np.random.default_rng(2)
+    dk = rng.integers(0, 1 << 16, size=(8, 2, 4, 8), dtype=np.uint16)
+    dv = rng.integers(0, 1 << 16, size=(8, 2, 4, 8), dtype=np.uint16)
+    hk = np.zeros((5, 2, 4, 8), np.uint16)
+    hv = np.zeros((5, 2, 4, 8), np.uint16)
+    hk2, hv2 = move_blocks_ref(dk, dv, hk, hv, [(6, 0), (1, 4)])
+    assert np.array_equal(hk2[0], dk[6]) and np.array_equal(hv2[4], dv[1])
+    assert not hk2[1:4].any() and not hv2[1:4].any()
+    back_k, back_v = move_blocks_ref(hk2, hv2, np.zeros_like(dk), np.zeros_like(dv), [(0, 2), (4, 7)])
+    assert np.array_equal(back_k[2], dk[6]) and np.array_equal(back_v[7], dv[1])
