@@ -506,6 +506,156 @@ def summarize_profiles(src, dst):
     log("wrote decode_c3_hbm_counters.{json,md}")
 
 
+# ------------------------------------------------------------ components ---
+
+def _event_ms(fn, reps, stream):
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def run_copy_swap(args):
+    """Block moves: copy-on-write copies inside the device cache, and swaps
+    between the device cache and a pinned host pool."""
+    import torch
+    import paged_kv_cache_215_amd as pa
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    hkv, bs, d, nb = 4, 32, 256, 16384          # the full step's block shape, one layer
+    n = 4096                                    # blocks moved per call
+    kc = torch.randn((nb, hkv, bs, d), device=dev).to(torch.bfloat16)
+    vc = torch.randn((nb, hkv, bs, d), device=dev).to(torch.bfloat16)
+    g = np.random.default_rng(0)
+    perm = g.permutation(nb)
+    pairs = torch.from_numpy(np.stack([perm[:n], perm[n:2 * n]], 1).astype(np.int64)).to(dev)
+    block_bytes = hkv * bs * d * 2 * 2          # K and V
+    copy_ms = _event_ms(lambda: pa.pa_copy_blocks(kc, vc, pairs), 20, stream)
+    copy_gbs = 2 * n * block_bytes / (copy_ms / 1e3) / 1e9   # read + write
+    hk = torch.empty((n, hkv, bs, d), dtype=torch.bfloat16).pin_memory()
+    hv = torch.empty((n, hkv, bs, d), dtype=torch.bfloat16).pin_memory()
+    out_pairs = torch.from_numpy(np.stack([perm[:n], np.arange(n)], 1).astype(np.int64)).to(dev)
+    in_pairs = torch.from_numpy(np.stack([np.arange(n), perm[n:2 * n]], 1).astype(np.int64)).to(dev)
+    out_ms = _event_ms(lambda: pa.pa_swap_out(kc, vc, hk, hv, out_pairs), 5, stream)
+    in_ms = _event_ms(lambda: pa.pa_swap_in(kc, vc, hk, hv, in_pairs), 5, stream)
+    moved = n * block_bytes
+    res = {
+        "metric": "KV block moves: copy-on-write copies (HBM GB/s) and swaps to/from pinned host "
+                  "memory (GB/s), 1 MI355X",
+        "value": round(copy_gbs, 1), "unit": "GB/s", "n_gpus": 1, "higher_is_better": True,
+        "data": "synthetic", "dtype": "bf16",
+        "config": {"component": "copy_swap", "blocks_per_call": n, "block_bytes_kv": block_bytes,
+                   "num_kv_heads": hkv, "block_size": bs, "head_dim": d},
+        "copy_blocks": {"avg_call_us": round(copy_ms * 1e3, 2), "achieved": round(copy_gbs, 1),
+                        "roofline": {"bound": "hbm", "achieved": round(copy_gbs, 1),
+                                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                     "frac": round(copy_gbs / HBM_PEAK_GBS, 4), "traffic": None}},
+        "swap_out": {"avg_call_us": round(out_ms * 1e3, 2),
+                     "achieved_gbs": round(moved / (out_ms / 1e3) / 1e9, 2)},
+        "swap_in": {"avg_call_us": round(in_ms * 1e3, 2),
+                    "achieved_gbs": round(moved / (in_ms / 1e3) / 1e9, 2)},
+    }
+    print(json.dumps(res), flush=True)
+
+
+def _engine_requests(scenario):
+    if scenario == "stragglers":
+        # the pages' four output lengths, short prompts: little work per
+        # iteration, so launch and host costs show
+        return [(16, o) for o in [50, 120, 240, 1024] * 8], dict(
+            num_layers=16, max_batch=4, chunk_tokens=64, num_blocks=4096, num_host_blocks=256,
+            max_blocks_per_seq=128)
+    rng = np.random.default_rng(5)
+    prompts = np.minimum(rng.geometric(1.0 / 1500.0, size=96), 6000)
+    outs = rng.choice(np.array([50, 120, 240, 1024]), size=96)
+    return list(zip(prompts.tolist(), outs.tolist())), dict(
+        num_layers=16, max_batch=32, chunk_tokens=512, num_blocks=16384, num_host_blocks=256,
+        max_blocks_per_seq=512)
+
+
+def run_engine(args):
+    """Continuous batching on the GPU: the native scheduler's plans executed
+    eagerly and with decode-only iterations replayed from a captured graph."""
+    import torch
+    from paged_kv_cache_215_amd.engine import Engine
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    hq, hkv, d, bs = 16, 4, 256, 16
+    result = {"metric": "continuous-batching generated tokens/s (eager vs graph replay), "
+                        "1 MI355X", "unit": "tokens/s", "n_gpus": 1, "higher_is_better": True,
+              "data": "synthetic", "dtype": "bf16", "scenarios": {}}
+    for scenario in ("stragglers", "mixed"):
+        reqs, cfg = _engine_requests(scenario)
+        L = cfg["num_layers"]
+        g = torch.Generator(device=dev)
+        g.manual_seed(0)
+        B, C = cfg["max_batch"], cfg["chunk_tokens"]
+        bank = {"q_dec": [torch.randn((B, hq, d), generator=g, device=dev).to(torch.bfloat16)
+                          for _ in range(L)],
+                "k_dec": [torch.randn((B, hkv, d), generator=g, device=dev).to(torch.bfloat16)
+                          for _ in range(L)],
+                "q_pre": [torch.randn((C, hq, d), generator=g, device=dev).to(torch.bfloat16)
+                          for _ in range(L)],
+                "k_pre": [torch.randn((C, hkv, d), generator=g, device=dev).to(torch.bfloat16)
+                          for _ in range(L)]}
+        bank["v_dec"], bank["v_pre"] = bank["k_dec"], bank["k_pre"]
+
+        out = {"requests": len(reqs), "layers": L, "max_batch": B, "chunk_tokens": C,
+               "generated_tokens": int(sum(o for _, o in reqs))}
+        for mode in ("eager", "graph"):
+            eng = Engine(reqs, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=bs,
+                         device=dev, use_graph=(mode == "graph"), **cfg)
+            if mode == "graph":
+                # decode inputs produced in place in the graph's buffers
+                static = eng.static_decode_inputs()
+                for name in ("q_dec", "k_dec", "v_dec"):
+                    for layer in range(L):
+                        static[name][layer].copy_(bank[name][layer])
+                        bank_mode = static
+            else:
+                bank_mode = bank
+
+            def inputs(plan, src=None):
+                src = bank_mode
+                nd, nr = len(plan["decode_seqs"]), int(plan["prefill_cu"][-1])
+                out = {k: [t[:nd] for t in src[k]] for k in ("q_dec", "k_dec", "v_dec")}
+                out.update({k: [t[:nr] for t in bank[k]] for k in ("q_pre", "k_pre", "v_pre")})
+                return out
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            host = 0.0
+            preempted = decode_only = 0
+            while not eng.done():
+                h0 = time.perf_counter()
+                plan, _, _ = eng.step(inputs)
+                host += time.perf_counter() - h0
+                preempted += len(plan["preempted"])
+                decode_only += int(len(plan["prefill_seqs"]) == 0)
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+            out[mode] = {"tokens_per_s": round(eng.decode_tokens / wall, 1),
+                         "wall_s": round(wall, 3), "iterations": eng.iterations,
+                         "ms_per_iteration": round(wall / eng.iterations * 1e3, 4),
+                         "decode_only_iterations": decode_only, "preemptions": preempted}
+            log(f"[bench] engine {scenario} {mode}: {out[mode]}")
+            eng.close()
+            del eng
+            torch.cuda.empty_cache()
+        out["graph_speedup"] = round(out["graph"]["tokens_per_s"] / out["eager"]["tokens_per_s"], 3)
+        result["scenarios"][scenario] = out
+    result["value"] = result["scenarios"]["mixed"]["graph"]["tokens_per_s"]
+    result["config"] = {"component": "engine", "num_q_heads": hq, "num_kv_heads": hkv,
+                        "head_dim": d, "block_size": bs}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -513,6 +663,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c3_full_step",
                     choices=["c2_layer_decode", "c3_full_step", "c4_grpo_cow", "c5_mixed_step"])
+    ap.add_argument("--component", choices=["engine", "copy_swap"], default=None,
+                    help="measure a component instead of the decode step: the continuous-"
+                         "batching engine, or block copies and swaps")
     ap.add_argument("--kv", choices=["bf16", "fp8"], default="bf16",
                     help="KV cache element type (fp8: E4M3 codes with per-head scales)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -534,6 +687,12 @@ def main():
         sys.exit(2)
     if args.copy_calib:
         copy_calibration()
+        return
+    if args.component == "engine":
+        run_engine(args)
+        return
+    if args.component == "copy_swap":
+        run_copy_swap(args)
         return
     run(args)
 

@@ -56,6 +56,8 @@ class Engine:
         self.eager_ws = None       # grown on demand for eager decode calls
         self.use_graph = use_graph
         self.graph = None
+        if use_graph:
+            self._static_buffers()
         self.decode_tokens = 0
         self.iterations = 0
 
@@ -82,8 +84,16 @@ class Engine:
     def _static_buffers(self):
         B = self.max_batch
         self.g_slots = torch.full((B,), -1, dtype=torch.int64, device=self.dev)
-        self.g_tables = torch.full((B, self.max_blocks), -1, dtype=torch.int32, device=self.dev)
-        self.g_lens = torch.zeros((B,), dtype=torch.int32, device=self.dev)
+        # tables and lengths share one buffer so that one copy refreshes both
+        self.g_meta = torch.zeros((B * (self.max_blocks + 1),), dtype=torch.int32, device=self.dev)
+        self.g_tables = self.g_meta[:B * self.max_blocks].view(B, self.max_blocks)
+        self.g_lens = self.g_meta[B * self.max_blocks:]
+        # two pinned staging sets, each reused once its previous copy is done
+        self.h_slots = [torch.full((B,), -1, dtype=torch.int64).pin_memory() for _ in range(2)]
+        self.h_meta = [torch.zeros((B * (self.max_blocks + 1),), dtype=torch.int32).pin_memory()
+                       for _ in range(2)]
+        self.h_done = [None, None]
+        self.h_next = 0
         self.g_q = [torch.zeros((B, self.hq, self.d), dtype=self.dtype, device=self.dev)
                     for _ in range(self.L)]
         self.g_k = [torch.zeros((B, self.hkv, self.d), dtype=self.dtype, device=self.dev)
@@ -101,8 +111,13 @@ class Engine:
                         self.g_tables, self.g_lens, self.scale, self.max_ctx,
                         out=self.g_out[layer], workspace=self.graph_ws)
 
+    def static_decode_inputs(self):
+        """The graph's input buffers (lists per layer of [max_batch, ...]):
+        decode inputs that a caller writes here in place are used without a
+        copy."""
+        return {"q_dec": self.g_q, "k_dec": self.g_k, "v_dec": self.g_v}
+
     def _capture(self):
-        self._static_buffers()
         self.graph_ws = L.decode_workspace(self.max_batch, self.hq, self.hkv, self.d, self.bs,
                                            self.max_ctx, self.dev)
         # the body runs once outside capture (one-time library set-up), on
@@ -124,7 +139,9 @@ class Engine:
         per-layer inputs: a dict with lists (one tensor per layer) ``q_dec``
         [n_dec, Hq, d], ``k_dec`` / ``v_dec`` [n_dec, Hkv, d], ``q_pre``
         [rows, Hq, d], ``k_pre`` / ``v_pre`` [rows, Hkv, d]. Returns
-        (plan, decode outputs per layer, prefill outputs per layer)."""
+        (plan, decode outputs per layer, prefill outputs per layer); in graph
+        mode the decode outputs are views of the graph's output buffers, valid
+        until the next step."""
         plan = self.sched.step()
         n_dec = len(plan["decode_seqs"])
         n_rows = int(plan["prefill_cu"][-1])
@@ -150,20 +167,30 @@ class Engine:
         if graph_ok and n_dec:
             if self.graph is None:
                 self._capture()
-            B = self.max_batch
-            slots = np.full(B, -1, dtype=np.int64)
-            slots[:n_dec] = plan["decode_slots"]
-            tables = np.full((B, self.max_blocks), -1, dtype=np.int32)
-            tables[:n_dec] = dec_tables
-            lens = np.zeros(B, dtype=np.int32)
-            lens[:n_dec] = dec_lens
-            self.g_slots.copy_(self._i64(slots))
-            self.g_tables.copy_(self._i32(tables))
-            self.g_lens.copy_(self._i32(lens))
+            B, mb = self.max_batch, self.max_blocks
+            k = self.h_next
+            self.h_next ^= 1
+            if self.h_done[k] is not None:
+                self.h_done[k].synchronize()      # this set's previous copy has run
+            hs = self.h_slots[k].numpy()
+            hs[:] = -1
+            hs[:n_dec] = plan["decode_slots"]
+            hm = self.h_meta[k].numpy()
+            tab = hm[:B * mb].reshape(B, mb)
+            tab[:] = -1
+            tab[:n_dec] = dec_tables
+            hm[B * mb:] = 0
+            hm[B * mb:B * mb + n_dec] = dec_lens
+            stream = torch.cuda.current_stream(self.dev)
+            self.g_slots.copy_(self.h_slots[k], non_blocking=True)
+            self.g_meta.copy_(self.h_meta[k], non_blocking=True)
+            self.h_done[k] = torch.cuda.Event()
+            self.h_done[k].record(stream)
             for layer in range(self.L):
-                self.g_q[layer][:n_dec].copy_(inputs["q_dec"][layer])
-                self.g_k[layer][:n_dec].copy_(inputs["k_dec"][layer])
-                self.g_v[layer][:n_dec].copy_(inputs["v_dec"][layer])
+                for name, buf in (("q_dec", self.g_q), ("k_dec", self.g_k), ("v_dec", self.g_v)):
+                    src = inputs[name][layer]
+                    if src.data_ptr() != buf[layer].data_ptr():   # not already in place
+                        buf[layer][:n_dec].copy_(src)
             self.graph.replay()
             return plan, [o[:n_dec] for o in self.g_out], []
 
@@ -185,8 +212,13 @@ class Engine:
         for layer in range(self.L):
             kc, vc = self.key_caches[layer], self.value_caches[layer]
             if slots_d is not None:
-                k_new = torch.cat([inputs["k_pre"][layer], inputs["k_dec"][layer]])
-                v_new = torch.cat([inputs["v_pre"][layer], inputs["v_dec"][layer]])
+                if n_rows and n_dec:
+                    k_new = torch.cat([inputs["k_pre"][layer], inputs["k_dec"][layer]])
+                    v_new = torch.cat([inputs["v_pre"][layer], inputs["v_dec"][layer]])
+                elif n_rows:
+                    k_new, v_new = inputs["k_pre"][layer], inputs["v_pre"][layer]
+                else:
+                    k_new, v_new = inputs["k_dec"][layer], inputs["v_dec"][layer]
                 L.pa_reshape_and_cache(k_new, v_new, kc, vc, slots_d)
             if n_rows:
                 pre_out.append(L.pa_prefill_chunk(inputs["q_pre"][layer], kc, vc, pt, pc, pcu,
