@@ -42,6 +42,13 @@ def common_flags():
     ]
 
 
+# Per-source code-generation flags. The prefill kernel keeps its MFMA
+# accumulators in ordinary VGPRs: with the accumulation registers the compiler
+# copied all 64 accumulators to VGPRs and back on every key tile so that the
+# softmax rescale could scale them.
+EXTRA_FLAGS = {"pa_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _run(cmd):
     proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(line for line in proc.stdout.splitlines()
@@ -58,13 +65,14 @@ def build(asm_dir=None, jobs=8, verbose=False):
 
     def compile_one(src):
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        cmd = [cc] + common_flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+        extra = EXTRA_FLAGS.get(src, [])
+        cmd = [cc] + common_flags() + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".cpp"):
             cmd[1:1] = ["-x", "hip"]
         out = _run(cmd)
         if asm_dir and src.endswith(".hip"):
             os.makedirs(asm_dir, exist_ok=True)
-            _run([cc] + common_flags() + ["-S", "--cuda-device-only", os.path.join(CSRC, src),
+            _run([cc] + common_flags() + extra + ["-S", "--cuda-device-only", os.path.join(CSRC, src),
                                           "-o", os.path.join(asm_dir, src + ".s")])
         return obj, out
 

@@ -772,11 +772,15 @@ int device_cus() {
   return cus[dev];
 }
 
+// Work units per CU the plan aims for on ragged batches: fewer, larger
+// partitions cost less per unit, more give the ticketed tail finer grain; 2
+// measured best on the ragged, shared-prompt and mixed-step batches. The
+// environment override exists for tuning sweeps only.
 int units_per_cu() {
   static const int v = [] {
     const char* s = std::getenv("PA_DECODE_UNITS_PER_CU");
     const int x = s ? std::atoi(s) : 0;
-    return x > 0 ? x : 4;
+    return x > 0 ? x : 2;
   }();
   return v;
 }

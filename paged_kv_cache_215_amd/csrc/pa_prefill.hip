@@ -172,16 +172,23 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
   // store_lds writes them (K swizzled, V transposed) into the other buffer.
   // K: thread t stages chunks (t % TPR) + TPR * i of key row t / TPR.
   // V: a job stages 4 consecutive keys (one block) x 8 dims.
+  // (threads beyond the tile's rows, which only some shapes have, load a
+  // duplicate row and store nothing; the loads stay unconditional so that the
+  // staging registers are never placed in scratch memory)
   const int k_row = tid / S::TPR, k_c0 = tid % S::TPR;
   const bool k_active = k_row < kKeyTile;
-  uint4 kreg[S::KPT];
+  const int k_row_c = k_active ? k_row : kKeyTile - 1;
+  // (K staging uses native vectors: copied as plain structs, the registers
+  // ended up in scratch memory)
+  u32x4_t kreg[S::KPT];
   uint4 vreg[S::VPT][4];
   auto load_regs = [&](int kt) {
     const int key0 = kt * kKeyTile;
-    if (k_active) {
-      const uint4* src = kcache + row_base(key0 + k_row) + k_c0;
+    {
+      const uint4* src = kcache + row_base(key0 + k_row_c) + k_c0;
 #pragma unroll
-      for (int i = 0; i < S::KPT; ++i) kreg[i] = src[S::TPR * i];
+      for (int i = 0; i < S::KPT; ++i)
+        kreg[i] = *reinterpret_cast<const u32x4_t*>(src + S::TPR * i);
     }
 #pragma unroll
     for (int j = 0; j < S::VPT; ++j) {
@@ -211,7 +218,7 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int i = 0; i < S::KPT; ++i) {
         const int c = k_c0 + S::TPR * i;
-        k_lds[buf][k_row * DCH + (c ^ (k_row & S::SWZ))] = kreg[i];
+        *reinterpret_cast<u32x4_t*>(&k_lds[buf][k_row * DCH + (c ^ (k_row & S::SWZ))]) = kreg[i];
       }
     }
     // V^T: each job transposes 4 keys x 8 dims
