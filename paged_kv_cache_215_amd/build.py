@@ -87,6 +87,38 @@ def build(asm_dir=None, jobs=8, verbose=False):
     return LIB
 
 
+def kernel_resources(lib_path=LIB):
+    """Per-kernel resource metadata of the gfx950 code objects inside the
+    built library: {kernel name: {field: int}} with private (scratch) segment
+    size, VGPR / AGPR / SGPR counts, spill counts and LDS size. Reads the
+    library this build made (llvm-objdump --offloading, llvm-readelf --notes)."""
+    import re
+    import tempfile
+    llvm = "/opt/rocm/llvm/bin"
+    out = {}
+    with tempfile.TemporaryDirectory() as tmp:
+        copy = os.path.join(tmp, "lib.so")
+        shutil.copyfile(lib_path, copy)
+        _run([os.path.join(llvm, "llvm-objdump"), "--offloading", copy])
+        for fn in sorted(os.listdir(tmp)):
+            if "amdgcn" not in fn:
+                continue
+            notes = _run([os.path.join(llvm, "llvm-readelf"), "--notes", os.path.join(tmp, fn)])
+            name = None
+            for line in notes.splitlines():
+                m = re.match(r"\s+\.name:\s+(\S+)", line)
+                if m:
+                    name = m.group(1)
+                    out.setdefault(name, {})
+                    continue
+                m = re.match(r"\s+\.(private_segment_fixed_size|vgpr_count|agpr_count|sgpr_count|"
+                             r"vgpr_spill_count|sgpr_spill_count|group_segment_fixed_size):\s+(\d+)",
+                             line)
+                if m and name:
+                    out[name][m.group(1)] = int(m.group(2))
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--asm", default=None, help="write device assembly here")

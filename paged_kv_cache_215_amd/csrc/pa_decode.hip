@@ -108,6 +108,24 @@ struct DecodeShape {
   }
 };
 
+// v[h] for a per-lane index h < 8, as a tree of selects on the bits of h.
+// Used for groups of 8 heads only: there the compiler turns a chain of
+// compares against 1..7 into an indexed load from scratch memory (for
+// smaller groups the chain stays in registers and is used as is).
+template <int G>
+__device__ __forceinline__ float pick_head(const float (&v)[G], int h) {
+  float t[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) t[g] = v[g];
+#pragma unroll
+  for (int w = 1; w < G; w <<= 1) {
+    const bool up = (h & w) != 0;
+#pragma unroll
+    for (int g = 0; g + w < G; g += 2 * w) t[g] = up ? t[g + w] : t[g];
+  }
+  return t[0];
+}
+
 // Transposing butterfly over lane bits M, M/2, .., 1: while a lane holds more
 // than one value, pairs (v[i], v[i+N/2]) are split so that the lane keeps one
 // half and receives its partner's copy of the same half; once one value is
@@ -507,11 +525,17 @@ __global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(DecodeArgs
       for (int j = 0; j < NVF; ++j) {
         // this slot's head, selected from the uniform per-head values
         float mo = m_run[0], mn = m_new[0];
+        if constexpr (G == 8) {
+          const int h = S::slot_head(lane, j);
+          mo = pick_head<G>(m_run, h);
+          mn = pick_head<G>(m_new, h);
+        } else {
 #pragma unroll
-        for (int g = 1; g < G; ++g) {
-          const bool hit = S::slot_head(lane, j) == g;
-          mo = hit ? m_run[g] : mo;
-          mn = hit ? m_new[g] : mn;
+          for (int g = 1; g < G; ++g) {
+            const bool hit = S::slot_head(lane, j) == g;
+            mo = hit ? m_run[g] : mo;
+            mn = hit ? m_new[g] : mn;
+          }
         }
         l_slot[j] *= fast_exp2(mo - mn);
       }
@@ -524,8 +548,12 @@ __global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(DecodeArgs
 #pragma unroll
     for (int j = 0; j < NVF; ++j) {
       float mh_j = m_run[0];
+      if constexpr (G == 8) {
+        mh_j = pick_head<G>(m_run, S::slot_head(lane, j));
+      } else {
 #pragma unroll
-      for (int g = 1; g < G; ++g) mh_j = S::slot_head(lane, j) == g ? m_run[g] : mh_j;
+        for (int g = 1; g < G; ++g) mh_j = S::slot_head(lane, j) == g ? m_run[g] : mh_j;
+      }
       mh_j = mh_j == -INFINITY ? 0.f : mh_j;
       const float p = fast_exp2(s[j] - mh_j);
       l_slot[j] += p;
@@ -832,9 +860,11 @@ static hipError_t launch_nw(const DecodeArgs& a, hipStream_t stream) {
 template <typename T, int D, int G>
 static hipError_t launch_t(const DecodeArgs& a, int waves, hipStream_t stream) {
   // 8-wave workgroups are limited to 256 VGPRs per lane; the d = 256 shapes
-  // with 8 query heads per KV head or float32 data, and FP8 with 8 query heads
-  // per KV head (16 accumulators per head and lane), need more and use 4 waves.
-  constexpr bool kFits8 = !(D == 256 && (G == 8 || T::kBytes == 4)) && G * (16 / T::kBytes) <= 64;
+  // with 8 query heads per KV head or float32 data, float32 at d = 128 with 8
+  // query heads, and FP8 with 8 query heads per KV head (16 accumulators per
+  // head and lane) need more and use 4 waves.
+  constexpr bool kFits8 = !(D == 256 && (G == 8 || T::kBytes == 4)) &&
+                          !(D == 128 && G == 8 && T::kBytes == 4) && G * (16 / T::kBytes) <= 64;
   if constexpr (kFits8) {
     if (waves == 8) return launch_nw<T, D, G, 8>(a, stream);
   }

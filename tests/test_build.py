@@ -1,0 +1,48 @@
+"""Resource checks on the kernels of the built library (CPU only): no kernel
+keeps registers in scratch memory or spills VGPRs, and the main shapes fit
+the register budget that their occupancy relies on."""
+
+import os
+import shutil
+
+import pytest
+
+from paged_kv_cache_215_amd import build
+
+pytestmark = pytest.mark.skipif(
+    not os.path.exists(build.LIB) or not shutil.which("/opt/rocm/llvm/bin/llvm-readelf"),
+    reason="library not built or ROCm LLVM tools missing")
+
+
+@pytest.fixture(scope="module")
+def resources():
+    res = build.kernel_resources()
+    assert res, "no kernel metadata found"
+    return res
+
+
+def test_no_kernel_uses_scratch_or_spills_vgprs(resources):
+    # scratch memory in a kernel means registers went through memory (a
+    # private array or a VGPR spill); SGPR spills are allowed: they go to
+    # VGPR lanes, not memory
+    bad = {k: v for k, v in resources.items()
+           if v.get("private_segment_fixed_size", 0) or v.get("vgpr_spill_count", 0)}
+    assert not bad, bad
+
+
+def test_every_entry_point_kernel_is_present(resources):
+    names = " ".join(resources)
+    for k in ("scatter_kernel", "scatter_fp8_kernel", "decode_partition_kernel",
+              "decode_merge_kernel", "prefill_kernel", "prefill_merge_kernel",
+              "copy_blocks_kernel", "zero_fill_kernel"):
+        assert k in names, k
+
+
+def test_main_shapes_fit_their_occupancy(resources):
+    # 8-wave decode workgroups need <= 256 VGPRs; the prefill shape of the
+    # mixed step runs two workgroups per CU, <= 256 registers
+    for name, r in resources.items():
+        if "decode_partition_kernel" in name and name.endswith("Li8EEEvNS_10DecodeArgsE"):
+            assert r["vgpr_count"] + r.get("agpr_count", 0) <= 256, (name, r)
+        if "prefill_kernelILi256ELi4ELi1E" in name:
+            assert r["vgpr_count"] + r.get("agpr_count", 0) <= 256, (name, r)
