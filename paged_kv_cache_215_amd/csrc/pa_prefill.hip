@@ -267,7 +267,6 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
     const int key0 = kt * kKeyTile;
     const int buf = (kt - kt_begin) & 1;
     const bool has_next = kt + 1 < kt_end;
-    if (has_next) load_regs(kt + 1);
 
     // ---- S^T = K Q^T for keys key0..key0+31 (two 16-key halves), per head
     f32x4_t s0[HPW], s1[HPW];
@@ -289,6 +288,11 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
         s1[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qop[hh][ks], s1[hh], 0, 0, 0);
       }
     }
+
+    // The next tile's global loads go out once the score products have been
+    // issued: issued before them, the compiler made those products wait for
+    // the loads.
+    if (has_next) load_regs(kt + 1);
 
     const int limit = base_pos + my_row;  // last key this row may see
     const bool diag = key0 + kKeyTile - 1 > base_pos + r0 || key0 + kKeyTile > n;
