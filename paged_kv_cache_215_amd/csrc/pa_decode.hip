@@ -134,17 +134,32 @@ template <int N, int M>
 __device__ __forceinline__ void transpose_reduce(float* v) {
   if constexpr (M >= 1) {
     if constexpr (N > 1) {
-      const bool upper = (__lane_id() & M) != 0;
+      if constexpr (M >= 16) {
+        // the half-wave swap keeps a for lower lanes and b for upper lanes and
+        // brings in the partner's other one: exactly keep + partner's send
 #pragma unroll
-      for (int i = 0; i < N / 2; ++i) {
-        const float a = v[i], b = v[i + N / 2];
-        const float keep = upper ? b : a;
-        const float send = upper ? a : b;
-        v[i] = keep + reduce_partner<M>(send);
+        for (int i = 0; i < N / 2; ++i) {
+          float r0, r1;
+          swap_halves<M>(v[i], v[i + N / 2], r0, r1);
+          v[i] = r0 + r1;
+        }
+      } else {
+        const bool upper = (__lane_id() & M) != 0;
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i) {
+          const float a = v[i], b = v[i + N / 2];
+          const float keep = upper ? b : a;
+          const float send = upper ? a : b;
+          v[i] = keep + reduce_partner<M>(send);
+        }
       }
       transpose_reduce<N / 2, M / 2>(v);
     } else {
-      v[0] += reduce_partner<M>(v[0]);
+      if constexpr (M >= 16) {
+        v[0] = pair_sum<M>(v[0]);
+      } else {
+        v[0] += reduce_partner<M>(v[0]);
+      }
       transpose_reduce<1, M / 2>(v);
     }
   }
@@ -155,8 +170,7 @@ template <typename Shape, bool IsMax>
 __device__ __forceinline__ float reduce_neutral(float x) {
 #define PA_STEP(B)                                                    \
   if constexpr (Shape::bit_neutral(B)) {                              \
-    const float y = xor_lane<(1 << B)>(x);                            \
-    x = IsMax ? fmaxf(x, y) : x + y;                                  \
+    x = IsMax ? pair_max<(1 << B)>(x) : pair_sum<(1 << B)>(x);        \
   }
   PA_STEP(0) PA_STEP(1) PA_STEP(2) PA_STEP(3) PA_STEP(4) PA_STEP(5)
 #undef PA_STEP
@@ -623,8 +637,8 @@ __global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(DecodeArgs
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         float x = acc[g][e];
-        if constexpr (VL <= 32 && RV > 1) x += xor_lane<(VL <= 32 ? 32 : 1)>(x);
-        if constexpr (VL <= 16 && RV > 2) x += xor_lane<(VL <= 16 ? 16 : 1)>(x);
+        if constexpr (VL <= 32 && RV > 1) x = pair_sum<32>(x);
+        if constexpr (VL <= 16 && RV > 2) x = pair_sum<16>(x);
         if constexpr (VL <= 8 && RV > 4) x += xor_lane<(VL <= 8 ? 8 : 1)>(x);
         if constexpr (VL <= 4 && RV > 8) x += xor_lane<(VL <= 4 ? 4 : 1)>(x);
         acc[g][e] = x;

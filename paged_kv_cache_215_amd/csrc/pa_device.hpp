@@ -142,6 +142,49 @@ __device__ __forceinline__ float reduce_partner(float x) {
   }
 }
 
+// Lane exchange across 16- or 32-lane halves on the VALU
+// (v_permlane16_swap / v_permlane32_swap, gfx950). swap_halves<M>(a, b)
+// returns {r0, r1}: a lane with bit M clear gets r0 = a[l], r1 = a[l ^ M];
+// a lane with bit M set gets r0 = b[l ^ M], r1 = b[l] (checked on the
+// hardware). So with a = b = x every lane holds the pair {x[l], x[l ^ M]},
+// and with a = the lower lanes' kept value / the upper lanes' sent value, r0 +
+// r1 is a lane's kept value plus its partner's sent one.
+template <int M>
+__device__ __forceinline__ void swap_halves(float a, float b, float& r0, float& r1) {
+  static_assert(M == 16 || M == 32, "half-wave swaps only");
+  if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    r0 = __uint_as_float(r[0]);
+    r1 = __uint_as_float(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    r0 = __uint_as_float(r[0]);
+    r1 = __uint_as_float(r[1]);
+  }
+}
+
+// max / sum of x over lanes l and l ^ M.
+template <int M>
+__device__ __forceinline__ float pair_max(float x) {
+  if constexpr (M == 16 || M == 32) {
+    float r0, r1;
+    swap_halves<M>(x, x, r0, r1);
+    return fmaxf(r0, r1);
+  } else {
+    return fmaxf(x, xor_lane<M>(x));
+  }
+}
+template <int M>
+__device__ __forceinline__ float pair_sum(float x) {
+  if constexpr (M == 16 || M == 32) {
+    float r0, r1;
+    swap_halves<M>(x, x, r0, r1);
+    return r0 + r1;
+  } else {
+    return x + xor_lane<M>(x);
+  }
+}
+
 __device__ __forceinline__ float readlane_f(float x, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }

@@ -319,8 +319,8 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
       float mx = sv[0];
 #pragma unroll
       for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
-      mx = fmaxf(mx, xor_lane<16>(mx));
-      mx = fmaxf(mx, xor_lane<32>(mx));
+      mx = pair_max<16>(mx);
+      mx = pair_max<32>(mx);
       // Rescale only when some row's maximum grew by more than 2^8: the
       // softmax does not depend on the offset subtracted, and weights of up
       // to 2^8 are far from float32 / BF16 overflow. This keeps the rescale
@@ -378,8 +378,8 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
   // ---- row totals and output, per head
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
-    float l_row = l_part[hh] + xor_lane<16>(l_part[hh]);
-    l_row += xor_lane<32>(l_row);
+    float l_row = pair_sum<16>(l_part[hh]);
+    l_row = pair_sum<32>(l_row);
     if (my_row >= L) continue;
     const int64_t orow = (int64_t)(q0 + my_row) * a.num_q_heads + head0 + hh;
     const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
