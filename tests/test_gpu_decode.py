@@ -214,3 +214,22 @@ def test_large_batch_spans_several_launches():
     err = max_abs_err(out.cpu().numpy()[seqs], oracle_decode(case, 0, seqs))
     say(f"[decode] 4500 sequences: sampled max-abs err {err:.3e}")
     assert err <= ATOL
+
+
+@pytest.mark.parametrize("kv_fp8", [False, True])
+def test_very_long_contexts(kv_fp8):
+    # contexts far past one partition's staged block table (up to 128K
+    # tokens) next to short ones; every sequence against the oracle
+    lens = [131072, 100003, 1, 65553]
+    case = make_case(name="long_ctx", seed=31, context_lens=lens, num_q_heads=16, num_kv_heads=4,
+                     head_dim=256, block_size=32, device=DEV, kv_fp8=kv_fp8)
+    if kv_fp8:
+        out = pa.pa_decode_fp8(case.queries[0], case.key_caches[0], case.value_caches[0],
+                               case.k_scales[0], case.v_scales[0], case.block_tables,
+                               case.context_lens, case.scale, case.max_context_len)
+    else:
+        out = gpu_decode(case)
+    torch.cuda.synchronize()
+    err = max_abs_err(out.cpu().numpy(), oracle_decode(case))
+    say(f"[decode] contexts {lens} (fp8={kv_fp8}): max-abs err {err:.3e}")
+    assert np.all(np.isfinite(out.cpu().numpy())) and err <= ATOL

@@ -119,3 +119,18 @@ def test_run_to_run_bit_identical():
 def test_workspace_query():
     assert pa.pa_prefill_chunk_workspace_size(1, 512, 512, 16, 4, 256, 16, 4096) > 0
     assert pa.pa_prefill_chunk_workspace_size(1, 37, 37, 4, 2, 64, 16, 82) == 0
+
+
+def test_long_prefix_spans_several_splits():
+    # a 30000-token prefix (1875 blocks of 16, more than one split stages):
+    # sampled rows of a 300-row chunk against the oracle
+    case = make_case(name="pf_long_prefix", seed=91, context_lens=[], num_q_heads=16,
+                     num_kv_heads=4, head_dim=256, block_size=16, device=DEV,
+                     prefill_chunks=[(30000, 300)])
+    kb, vb = _write_chunk(case)
+    out = gpu_prefill(case)
+    torch.cuda.synchronize()
+    rows = [0, 1, 150, 298, 299]
+    err = max_abs_err(out.cpu().numpy()[rows], oracle_prefill_rows(case, 0, rows, kb, vb))
+    say(f"[prefill] 30000-token prefix: sampled max-abs err {err:.3e}")
+    assert np.all(np.isfinite(out.cpu().numpy())) and err <= ATOL
