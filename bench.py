@@ -584,7 +584,7 @@ def run_engine(args):
     """Continuous batching on the GPU: the native scheduler's plans executed
     eagerly and with decode-only iterations replayed from a captured graph."""
     import torch
-    from paged_kv_cache_215_amd.engine import Engine
+    from paged_kv_cache_215_amd.engine import Engine, NativeEngine
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     hq, hkv, d, bs = 16, 4, 256, 16
@@ -609,25 +609,32 @@ def run_engine(args):
 
         out = {"requests": len(reqs), "layers": L, "max_batch": B, "chunk_tokens": C,
                "generated_tokens": int(sum(o for _, o in reqs))}
-        for mode in ("eager", "graph"):
-            eng = Engine(reqs, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=bs,
-                         device=dev, use_graph=(mode == "graph"), **cfg)
-            if mode == "graph":
-                # decode inputs produced in place in the graph's buffers
-                static = eng.static_decode_inputs()
-                for name in ("q_dec", "k_dec", "v_dec"):
+        for mode in ("eager", "graph", "native_eager", "native_graph"):
+            native = mode.startswith("native")
+            graph = mode.endswith("graph")
+            cls = NativeEngine if native else Engine
+            eng = cls(reqs, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=bs,
+                      device=dev, use_graph=graph, **cfg)
+            if native:
+                # inputs produced in place in the engine's buffers (once: the
+                # values do not matter for timing)
+                for name in ("q_dec", "k_dec", "v_dec", "q_pre", "k_pre", "v_pre"):
                     for layer in range(L):
-                        static[name][layer].copy_(bank[name][layer])
-                        bank_mode = static
+                        eng.inputs[name][layer].copy_(bank[name][layer])
+                inputs = None
             else:
-                bank_mode = bank
+                if graph:
+                    static = eng.static_decode_inputs()
+                    for name in ("q_dec", "k_dec", "v_dec"):
+                        for layer in range(L):
+                            static[name][layer].copy_(bank[name][layer])
+                src_dec = static if graph else bank
 
-            def inputs(plan, src=None):
-                src = bank_mode
-                nd, nr = len(plan["decode_seqs"]), int(plan["prefill_cu"][-1])
-                out = {k: [t[:nd] for t in src[k]] for k in ("q_dec", "k_dec", "v_dec")}
-                out.update({k: [t[:nr] for t in bank[k]] for k in ("q_pre", "k_pre", "v_pre")})
-                return out
+                def inputs(plan, src_dec=src_dec):
+                    nd, nr = len(plan["decode_seqs"]), int(plan["prefill_cu"][-1])
+                    out = {k: [t[:nd] for t in src_dec[k]] for k in ("q_dec", "k_dec", "v_dec")}
+                    out.update({k: [t[:nr] for t in bank[k]] for k in ("q_pre", "k_pre", "v_pre")})
+                    return out
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             host = 0.0
@@ -643,14 +650,17 @@ def run_engine(args):
             out[mode] = {"tokens_per_s": round(eng.decode_tokens / wall, 1),
                          "wall_s": round(wall, 3), "iterations": eng.iterations,
                          "ms_per_iteration": round(wall / eng.iterations * 1e3, 4),
+                         "host_ms_per_iteration": round(host / eng.iterations * 1e3, 4),
                          "decode_only_iterations": decode_only, "preemptions": preempted}
             log(f"[bench] engine {scenario} {mode}: {out[mode]}")
             eng.close()
             del eng
             torch.cuda.empty_cache()
         out["graph_speedup"] = round(out["graph"]["tokens_per_s"] / out["eager"]["tokens_per_s"], 3)
+        out["native_graph_speedup"] = round(out["native_graph"]["tokens_per_s"] /
+                                            out["eager"]["tokens_per_s"], 3)
         result["scenarios"][scenario] = out
-    result["value"] = result["scenarios"]["mixed"]["graph"]["tokens_per_s"]
+    result["value"] = result["scenarios"]["mixed"]["native_graph"]["tokens_per_s"]
     result["config"] = {"component": "engine", "num_q_heads": hq, "num_kv_heads": hkv,
                         "head_dim": d, "block_size": bs}
     print(json.dumps(result), flush=True)

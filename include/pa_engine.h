@@ -1,0 +1,92 @@
+/*
+ * pa_engine.h - continuous-batching step driver in C++ (libpa.so): runs the
+ * scheduler's plans (pa_sched.h) on the GPU through the library's own entry
+ * points, with decode-only iterations replayed from captured HIP graphs.
+ *
+ * An iteration is planned on the host, then executed: swapped blocks come
+ * back from the pinned host pool and preempted ones go out (pa_swap_in,
+ * pa_swap_out), then for every layer the iteration's new K/V rows are written
+ * through the slot mapping (pa_reshape_and_cache), the prefill chunks attend
+ * to their prefix (pa_prefill_chunk) and the decode batch attends to its
+ * context (pa_decode) (How vLLM gets real throughput on H100s, "Continuous
+ * batching removes straggler bubbles"; Dissecting vLLM, "Continuous
+ * Batching: Breaking the Sequence Barrier"; vLLM architecture, memory and
+ * benchmarks deep dive, "Hardware-level optimizations"). Launch overhead is
+ * what the graphs remove: a decode-only iteration is one graph launch that
+ * copies slots, tables and lengths from pinned staging and runs every
+ * layer's scatter and decode for max_batch rows (rows past the batch have
+ * context 0 and slot -1).
+ *
+ * The model is outside: between pa_engine_plan and pa_engine_execute the
+ * caller writes the iteration's inputs into the buffers it registered - for
+ * layer l, decode row i (the plan's i-th decode sequence) of q_dec[l],
+ * k_dec[l], v_dec[l], and prefill row r (rows of the plan's chunks, in order)
+ * of q_pre[l], k_pre[l], v_pre[l]. Outputs land in out_dec[l] (decode rows)
+ * and out_pre[l] (prefill rows) when the stream reaches them.
+ *
+ * Ownership: the caller owns every registered buffer and keeps it alive;
+ * the engine allocates its own index buffers, staging (pinned) and
+ * workspaces at creation and frees them in pa_engine_destroy. All work is
+ * enqueued on the stream given at creation. BF16 caches only.
+ */
+#ifndef PA_ENGINE_H
+#define PA_ENGINE_H
+
+#include "pa_sched.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct pa_engine pa_engine;
+
+typedef struct {
+  int32_t num_layers;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  float scale;
+  int32_t use_graph;              /* replay decode-only iterations from graphs */
+  pa_sched_config sched;          /* pools, block size, batch, chunk budget */
+} pa_engine_config;
+
+/* Arrays of num_layers pointers each (copied at creation). */
+typedef struct {
+  void* const* key_caches;        /* device BF16 [num_blocks, Hkv, bs, d] */
+  void* const* value_caches;
+  void* const* host_keys;         /* pinned BF16 [num_host_blocks, Hkv, bs, d] */
+  void* const* host_values;
+  void* const* q_dec;             /* device BF16 [max_batch, Hq, d] */
+  void* const* k_dec;             /* device BF16 [max_batch, Hkv, d] */
+  void* const* v_dec;
+  void* const* q_pre;             /* device BF16 [chunk_tokens, Hq, d] */
+  void* const* k_pre;             /* device BF16 [chunk_tokens, Hkv, d] */
+  void* const* v_pre;
+  float* const* out_dec;          /* device float32 [max_batch, Hq, d] */
+  float* const* out_pre;          /* device float32 [chunk_tokens, Hq, d] */
+} pa_engine_buffers;
+
+pa_status_t pa_engine_create(const pa_engine_config* cfg, const pa_engine_buffers* bufs,
+                             const int32_t* prompt_lens, const int32_t* output_lens,
+                             int32_t num_requests, void* stream, pa_engine** out);
+void pa_engine_destroy(pa_engine* e);
+
+int32_t pa_engine_done(const pa_engine* e);
+
+/* Plan the next iteration (the scheduler's step). The plan's arrays stay
+ * valid until the next pa_engine_plan. */
+pa_status_t pa_engine_plan(pa_engine* e, pa_step_plan* plan);
+
+/* Enqueue the device work of the last plan. Returns after enqueueing; it
+ * waits only for the staging set it reuses (written two iterations ago). */
+pa_status_t pa_engine_execute(pa_engine* e);
+
+/* Iterations executed so far and how many of them were graph launches. */
+int64_t pa_engine_iterations(const pa_engine* e);
+int64_t pa_engine_graph_launches(const pa_engine* e);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_ENGINE_H */

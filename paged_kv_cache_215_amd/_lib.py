@@ -60,6 +60,13 @@ SIGNATURES = {
                            _vp]),
     "pa_swap_in": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i64, _i32,
                           _vp]),
+    "pa_engine_create": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp, ctypes.POINTER(_vp)]),
+    "pa_engine_destroy": (None, [_vp]),
+    "pa_engine_done": (_i32, [_vp]),
+    "pa_engine_plan": (_i32, [_vp, _vp]),
+    "pa_engine_execute": (_i32, [_vp]),
+    "pa_engine_iterations": (_i64, [_vp]),
+    "pa_engine_graph_launches": (_i64, [_vp]),
     "pa_sched_create": (_i32, [_vp, _vp, _vp, _i32, ctypes.POINTER(_vp)]),
     "pa_sched_destroy": (None, [_vp]),
     "pa_sched_done": (_i32, [_vp]),
@@ -471,43 +478,51 @@ class Scheduler:
         return bool(self._lib.pa_sched_done(self._h))
 
     def step(self):
-        import numpy as np
         plan = _StepPlan()
         _check("pa_sched_step", self._lib.pa_sched_step(self._h, ctypes.byref(plan)))
-
-        def arr(ptr, n, dtype):
-            if n == 0:
-                return np.zeros(0, dtype=dtype)
-            return np.ctypeslib.as_array(ptr, shape=(n,)).astype(dtype, copy=True)
-
-        npf = plan.num_prefill
-        cu = arr(plan.prefill_cu, npf + 1, np.int32)
-        return {
-            "iteration": plan.iteration,
-            "decode_seqs": arr(plan.decode_seqs, plan.num_decode, np.int64),
-            "decode_slots": arr(plan.decode_slots, plan.num_decode, np.int64),
-            "decode_context": arr(plan.decode_context, plan.num_decode, np.int32),
-            "prefill_seqs": arr(plan.prefill_seqs, npf, np.int64),
-            "prefill_start": arr(plan.prefill_start, npf, np.int32),
-            "prefill_cu": cu,
-            "prefill_slots": arr(plan.prefill_slots, int(cu[-1]), np.int64),
-            "swap_out": arr(plan.swap_out, 2 * plan.num_swap_out, np.int64).reshape(-1, 2),
-            "swap_in": arr(plan.swap_in, 2 * plan.num_swap_in, np.int64).reshape(-1, 2),
-            "finished": arr(plan.finished, plan.num_finished, np.int64),
-            "admitted": arr(plan.admitted, plan.num_admitted, np.int64),
-            "preempted": arr(plan.preempted, plan.num_preempted, np.int64),
-            "resumed": arr(plan.resumed, plan.num_resumed, np.int64),
-        }
+        return _plan_dict(plan)
 
     def tables(self, seqs, row_stride=None):
         """(tables int32 [len(seqs), row_stride], context_lens int32) of live sequences."""
-        import numpy as np
-        seqs = np.ascontiguousarray(seqs, dtype=np.int64)
-        stride = row_stride or self.max_blocks_per_seq
-        tables = np.empty((seqs.size, stride), dtype=np.int32)
-        lens = np.empty(seqs.size, dtype=np.int32)
-        bm = self._lib.pa_sched_blocks(self._h)
-        _check("pa_bm_tables", self._lib.pa_bm_tables(
-            bm, seqs.ctypes.data_as(_vp), seqs.size, tables.ctypes.data_as(_vp), stride,
-            lens.ctypes.data_as(_vp)))
-        return tables, lens
+        return _bm_tables(self._lib, self._lib.pa_sched_blocks(self._h), seqs,
+                          row_stride or self.max_blocks_per_seq)
+
+
+def _bm_tables(library, bm, seqs, stride):
+    import numpy as np
+    seqs = np.ascontiguousarray(seqs, dtype=np.int64)
+    tables = np.empty((seqs.size, stride), dtype=np.int32)
+    lens = np.empty(seqs.size, dtype=np.int32)
+    _check("pa_bm_tables", library.pa_bm_tables(
+        bm, seqs.ctypes.data_as(_vp), seqs.size, tables.ctypes.data_as(_vp), stride,
+        lens.ctypes.data_as(_vp)))
+    return tables, lens
+
+
+def _plan_dict(plan):
+    """A pa_step_plan as numpy arrays (copied)."""
+    import numpy as np
+
+    def arr(ptr, n, dtype):
+        if n == 0:
+            return np.zeros(0, dtype=dtype)
+        return np.ctypeslib.as_array(ptr, shape=(n,)).astype(dtype, copy=True)
+
+    npf = plan.num_prefill
+    cu = arr(plan.prefill_cu, npf + 1, np.int32)
+    return {
+        "iteration": plan.iteration,
+        "decode_seqs": arr(plan.decode_seqs, plan.num_decode, np.int64),
+        "decode_slots": arr(plan.decode_slots, plan.num_decode, np.int64),
+        "decode_context": arr(plan.decode_context, plan.num_decode, np.int32),
+        "prefill_seqs": arr(plan.prefill_seqs, npf, np.int64),
+        "prefill_start": arr(plan.prefill_start, npf, np.int32),
+        "prefill_cu": cu,
+        "prefill_slots": arr(plan.prefill_slots, int(cu[-1]), np.int64),
+        "swap_out": arr(plan.swap_out, 2 * plan.num_swap_out, np.int64).reshape(-1, 2),
+        "swap_in": arr(plan.swap_in, 2 * plan.num_swap_in, np.int64).reshape(-1, 2),
+        "finished": arr(plan.finished, plan.num_finished, np.int64),
+        "admitted": arr(plan.admitted, plan.num_admitted, np.int64),
+        "preempted": arr(plan.preempted, plan.num_preempted, np.int64),
+        "resumed": arr(plan.resumed, plan.num_resumed, np.int64),
+    }

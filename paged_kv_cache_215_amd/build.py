@@ -20,7 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpa.so")
-SOURCES = ["pa_api.cpp", "pa_block_manager.cpp", "pa_scheduler.cpp", "pa_scatter.hip",
+SOURCES = ["pa_api.cpp", "pa_block_manager.cpp", "pa_scheduler.cpp", "pa_engine.cpp",
+           "pa_scatter.hip",
            "pa_copy.hip",
            "pa_decode.hip", "pa_prefill.hip"]
 ARCH = "gfx950"

@@ -24,6 +24,8 @@ static device buffers before each replay; unused batch rows have context 0
 (zero output) and slot -1 (nothing written).
 """
 
+import ctypes
+
 import numpy as np
 import torch
 
@@ -230,3 +232,130 @@ class Engine:
 
     def close(self):
         self.sched.close()
+
+
+class _EngineConfig(ctypes.Structure):
+    _fields_ = [("num_layers", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("use_graph", ctypes.c_int32),
+                ("sched", L._SchedConfig)]
+
+
+_BUFFER_FIELDS = ("key_caches", "value_caches", "host_keys", "host_values", "q_dec", "k_dec",
+                  "v_dec", "q_pre", "k_pre", "v_pre", "out_dec", "out_pre")
+
+
+class _EngineBuffers(ctypes.Structure):
+    _fields_ = [(n, ctypes.POINTER(ctypes.c_void_p)) for n in _BUFFER_FIELDS]
+
+
+class NativeEngine:
+    """The same driver as ``Engine`` with the per-iteration work in C++
+    (include/pa_engine.h): ``plan()`` schedules, the caller writes the
+    iteration's inputs into ``inputs`` (per layer, rows in plan order), and
+    ``execute()`` enqueues the device work on the engine's own stream (graph
+    launches need a stream other than the legacy default one), ordered after
+    the caller's stream; results are visible to the caller's stream after
+    ``execute()`` returns."""
+
+    def __init__(self, requests, *, num_layers, num_q_heads, num_kv_heads, head_dim, block_size,
+                 num_blocks, num_host_blocks, max_blocks_per_seq, max_batch, chunk_tokens,
+                 device="cuda", use_graph=False):
+        self.dev = torch.device(device)
+        self.L, self.hq, self.hkv, self.d = num_layers, num_q_heads, num_kv_heads, head_dim
+        self.max_batch, self.chunk = max_batch, chunk_tokens
+        bf = torch.bfloat16
+        shape = (num_blocks, num_kv_heads, block_size, head_dim)
+        hshape = (max(num_host_blocks, 1), num_kv_heads, block_size, head_dim)
+        Lr = range(num_layers)
+        self.key_caches = [torch.zeros(shape, dtype=bf, device=self.dev) for _ in Lr]
+        self.value_caches = [torch.zeros(shape, dtype=bf, device=self.dev) for _ in Lr]
+        self.host_keys = [torch.zeros(hshape, dtype=bf).pin_memory() for _ in Lr]
+        self.host_values = [torch.zeros(hshape, dtype=bf).pin_memory() for _ in Lr]
+
+        def dev(rows, heads, dtype=bf):
+            return [torch.zeros((rows, heads, head_dim), dtype=dtype, device=self.dev) for _ in Lr]
+        self.inputs = {"q_dec": dev(max_batch, num_q_heads), "k_dec": dev(max_batch, num_kv_heads),
+                       "v_dec": dev(max_batch, num_kv_heads), "q_pre": dev(chunk_tokens, num_q_heads),
+                       "k_pre": dev(chunk_tokens, num_kv_heads),
+                       "v_pre": dev(chunk_tokens, num_kv_heads)}
+        self.out_dec = dev(max_batch, num_q_heads, torch.float32)
+        self.out_pre = dev(chunk_tokens, num_q_heads, torch.float32)
+
+        def ptrs(ts):
+            a = (ctypes.c_void_p * num_layers)(*[t.data_ptr() for t in ts])
+            self._keep.append(a)
+            return ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p))
+        self._keep = []
+        bufs = _EngineBuffers(ptrs(self.key_caches), ptrs(self.value_caches), ptrs(self.host_keys),
+                              ptrs(self.host_values), ptrs(self.inputs["q_dec"]),
+                              ptrs(self.inputs["k_dec"]), ptrs(self.inputs["v_dec"]),
+                              ptrs(self.inputs["q_pre"]), ptrs(self.inputs["k_pre"]),
+                              ptrs(self.inputs["v_pre"]), ptrs(self.out_dec), ptrs(self.out_pre))
+        cfg = _EngineConfig(num_layers, num_q_heads, num_kv_heads, head_dim,
+                            1.0 / float(np.sqrt(head_dim)), int(bool(use_graph)),
+                            L._SchedConfig(num_blocks, num_host_blocks, block_size,
+                                           max_blocks_per_seq, max_batch, chunk_tokens))
+        prompts = np.ascontiguousarray([int(p) for p, _ in requests], dtype=np.int32)
+        outputs = np.ascontiguousarray([int(o) for _, o in requests], dtype=np.int32)
+        self.stream = torch.cuda.Stream(self.dev)
+        torch.cuda.synchronize(self.dev)        # the zero-filled buffers above are in place
+        self._lib = L.lib()
+        h = ctypes.c_void_p()
+        L._check("pa_engine_create", self._lib.pa_engine_create(
+            ctypes.byref(cfg), ctypes.byref(bufs), prompts.ctypes.data_as(ctypes.c_void_p),
+            outputs.ctypes.data_as(ctypes.c_void_p), len(requests),
+            ctypes.c_void_p(self.stream.cuda_stream), ctypes.byref(h)))
+        self._h = h
+        self.decode_tokens = 0
+
+    def done(self):
+        return bool(self._lib.pa_engine_done(self._h))
+
+    @property
+    def iterations(self):
+        return int(self._lib.pa_engine_iterations(self._h))
+
+    @property
+    def graph_launches(self):
+        return int(self._lib.pa_engine_graph_launches(self._h))
+
+    def plan(self):
+        p = L._StepPlan()
+        L._check("pa_engine_plan", self._lib.pa_engine_plan(self._h, ctypes.byref(p)))
+        plan = L._plan_dict(p)
+        self.decode_tokens += len(plan["decode_seqs"])
+        return plan
+
+    def execute(self):
+        caller = torch.cuda.current_stream(self.dev)
+        self.stream.wait_stream(caller)
+        L._check("pa_engine_execute", self._lib.pa_engine_execute(self._h))
+        caller.wait_stream(self.stream)
+
+    def step(self, inputs_fn=None):
+        """plan(), inputs written (from ``inputs_fn(plan)`` if given), execute();
+        returns (plan, decode outputs per layer, prefill outputs per layer) as
+        views valid until the next step."""
+        plan = self.plan()
+        n_dec = len(plan["decode_seqs"])
+        rows = int(plan["prefill_cu"][-1])
+        if inputs_fn is not None:
+            given = inputs_fn(plan)
+            for name, bufs in self.inputs.items():
+                n = rows if name.endswith("pre") else n_dec
+                for layer in range(self.L):
+                    src = given[name][layer]
+                    if n and src.data_ptr() != bufs[layer].data_ptr():
+                        bufs[layer][:n].copy_(src[:n])
+        self.execute()
+        return plan, [o[:n_dec] for o in self.out_dec] if n_dec else [], \
+            [o[:rows] for o in self.out_pre] if rows else []
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.pa_engine_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()

@@ -243,3 +243,15 @@ def test_swap_rejects(lib, fn, over, code):
 @pytest.mark.parametrize("fn", ["pa_swap_out", "pa_swap_in"])
 def test_swap_zero_pairs_is_noop(lib, fn):
     assert getattr(lib, fn)(*swap_args(num_pairs=0, host_key=None)) == OK
+
+
+def test_engine_create_rejects_before_any_hip_call(lib):
+    import ctypes
+    h = ctypes.c_void_p()
+    assert lib.pa_engine_create(None, None, None, None, 0, None, ctypes.byref(h)) == NULL
+    assert not h.value
+    assert lib.pa_engine_create(None, None, None, None, 0, None, None) == NULL
+    assert lib.pa_engine_plan(None, None) == NULL
+    assert lib.pa_engine_execute(None) == NULL
+    assert lib.pa_engine_done(None) == 0
+    assert lib.pa_engine_iterations(None) == -1
