@@ -639,12 +639,13 @@ def run_engine(args):
             t0 = time.perf_counter()
             host = 0.0
             preempted = decode_only = 0
-            while not eng.done():
-                h0 = time.perf_counter()
-                plan, _, _ = eng.step(inputs)
-                host += time.perf_counter() - h0
-                preempted += len(plan["preempted"])
-                decode_only += int(len(plan["prefill_seqs"]) == 0)
+            with torch.cuda.stream(eng.stream if native else torch.cuda.current_stream()):
+                while not eng.done():
+                    h0 = time.perf_counter()
+                    plan, _, _ = eng.step(inputs)
+                    host += time.perf_counter() - h0
+                    preempted += len(plan["preempted"])
+                    decode_only += int(len(plan["prefill_seqs"]) == 0)
             torch.cuda.synchronize()
             wall = time.perf_counter() - t0
             out[mode] = {"tokens_per_s": round(eng.decode_tokens / wall, 1),

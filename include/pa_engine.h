@@ -1,7 +1,7 @@
 /*
  * pa_engine.h - continuous-batching step driver in C++ (libpa.so): runs the
  * scheduler's plans (pa_sched.h) on the GPU through the library's own entry
- * points, with decode-only iterations replayed from captured HIP graphs.
+ * points, with decode-only iterations replayed from a captured HIP graph.
  *
  * An iteration is planned on the host, then executed: swapped blocks come
  * back from the pinned host pool and preempted ones go out (pa_swap_in,
@@ -12,10 +12,10 @@
  * batching removes straggler bubbles"; Dissecting vLLM, "Continuous
  * Batching: Breaking the Sequence Barrier"; vLLM architecture, memory and
  * benchmarks deep dive, "Hardware-level optimizations"). Launch overhead is
- * what the graphs remove: a decode-only iteration is one graph launch that
- * copies slots, tables and lengths from pinned staging and runs every
- * layer's scatter and decode for max_batch rows (rows past the batch have
- * context 0 and slot -1).
+ * what the graph removes: a decode-only iteration is two copies of slots,
+ * tables and lengths from pinned staging and one graph launch that runs
+ * every layer's scatter and decode for max_batch rows (rows past the batch
+ * have context 0 and slot -1).
  *
  * The model is outside: between pa_engine_plan and pa_engine_execute the
  * caller writes the iteration's inputs into the buffers it registered - for

@@ -13,14 +13,13 @@
 
 namespace {
 
-// One set of pinned staging buffers and the graph that reads it.
+// One set of pinned staging buffers.
 struct Stage {
   int64_t* slots = nullptr;   // [B | C]: decode slots, then prefill slots
   int32_t* meta = nullptr;    // decode tables, decode lens, prefill tables, ctx, cu
   int64_t* pairs = nullptr;   // swap-in pairs, then swap-out pairs
   hipEvent_t done = nullptr;  // recorded after the last work that read this set
   bool used = false;
-  hipGraphExec_t graph = nullptr;
 };
 
 }  // namespace
@@ -35,6 +34,7 @@ struct pa_engine {
   size_t meta_len = 0, pair_len = 0;
   Stage stage[2];
   int next = 0;
+  hipGraphExec_t graph = nullptr;
   int64_t* d_slots = nullptr;
   int32_t* d_meta = nullptr;
   void* dec_ws = nullptr;
@@ -80,33 +80,28 @@ pa_status_t decode_body(pa_engine* e, int32_t rows, int32_t max_ctx) {
   return PA_OK;
 }
 
-// The graph of staging set k: copy its decode slots, tables and lengths to
-// the device index buffers, then the decode body for B rows at full capacity.
-pa_status_t capture(pa_engine* e, int k) {
-  Stage& st = e->stage[k];
-  const size_t meta_bytes = (e->o_dec_len() + e->B) * sizeof(int32_t);
+// The decode-only graph: the decode body for B rows at full capacity, reading
+// the device index buffers. The copies from pinned staging into those buffers
+// are issued before each launch, outside the graph: as memcpy nodes inside it
+// they made every replay slower than the eager launches it replaces.
+pa_status_t capture(pa_engine* e) {
   hipGraph_t g = nullptr;
   if (hipStreamBeginCapture(e->stream, hipStreamCaptureModeThreadLocal) != hipSuccess)
     return PA_ERR_HIP;
-  pa_status_t status = hip_ok(hipMemcpyAsync(e->d_slots, st.slots, e->B * sizeof(int64_t),
-                                             hipMemcpyHostToDevice, e->stream));
-  if (status == PA_OK)
-    status = hip_ok(hipMemcpyAsync(e->d_meta, st.meta, meta_bytes, hipMemcpyHostToDevice,
-                                   e->stream));
-  if (status == PA_OK) status = decode_body(e, e->B, e->capacity);
+  pa_status_t status = decode_body(e, e->B, e->capacity);
   const hipError_t end = hipStreamEndCapture(e->stream, &g);
   if (status != PA_OK || end != hipSuccess) {
     if (g) (void)hipGraphDestroy(g);
     return status != PA_OK ? status : PA_ERR_HIP;
   }
-  status = hip_ok(hipGraphInstantiate(&st.graph, g, nullptr, nullptr, 0));
+  status = hip_ok(hipGraphInstantiate(&e->graph, g, nullptr, nullptr, 0));
   (void)hipGraphDestroy(g);
   return status;
 }
 
 void release(pa_engine* e) {
+  if (e->graph) (void)hipGraphExecDestroy(e->graph);
   for (Stage& st : e->stage) {
-    if (st.graph) (void)hipGraphExecDestroy(st.graph);
     if (st.done) (void)hipEventDestroy(st.done);
     if (st.slots) (void)hipHostFree(st.slots);
     if (st.meta) (void)hipHostFree(st.meta);
@@ -198,7 +193,7 @@ pa_status_t pa_engine_create(const pa_engine_config* cfg, const pa_engine_buffer
                                      hipMemcpyHostToDevice, e->stream));
     if (status == PA_OK) status = decode_body(e, e->B, e->capacity);
     if (status == PA_OK) status = hip_ok(hipStreamSynchronize(e->stream));
-    for (int k = 0; k < 2 && status == PA_OK; ++k) status = capture(e, k);
+    if (status == PA_OK) status = capture(e);
   }
   if (status == PA_OK) status = hip_ok(hipStreamSynchronize(e->stream));
   if (status != PA_OK) {
@@ -277,7 +272,11 @@ pa_status_t pa_engine_execute(pa_engine* e) {
                        PA_DTYPE_BF16, e->stream));
 
   if (graph) {
-    PA_TRY(hip_ok(hipGraphLaunch(st.graph, e->stream)));
+    PA_TRY(hip_ok(hipMemcpyAsync(e->d_slots, st.slots, e->B * sizeof(int64_t),
+                                 hipMemcpyHostToDevice, e->stream)));
+    PA_TRY(hip_ok(hipMemcpyAsync(e->d_meta, st.meta, (e->o_dec_len() + e->B) * sizeof(int32_t),
+                                 hipMemcpyHostToDevice, e->stream)));
+    PA_TRY(hip_ok(hipGraphLaunch(e->graph, e->stream)));
     PA_TRY(hip_ok(hipEventRecord(st.done, e->stream)));
     st.used = true;
     ++e->iterations;

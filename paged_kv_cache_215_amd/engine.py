@@ -256,7 +256,9 @@ class NativeEngine:
     ``execute()`` enqueues the device work on the engine's own stream (graph
     launches need a stream other than the legacy default one), ordered after
     the caller's stream; results are visible to the caller's stream after
-    ``execute()`` returns."""
+    ``execute()`` returns. A caller that works on ``stream`` itself (``with
+    torch.cuda.stream(engine.stream)``) saves the two cross-stream waits per
+    iteration."""
 
     def __init__(self, requests, *, num_layers, num_q_heads, num_kv_heads, head_dim, block_size,
                  num_blocks, num_host_blocks, max_blocks_per_seq, max_batch, chunk_tokens,
@@ -329,9 +331,12 @@ class NativeEngine:
 
     def execute(self):
         caller = torch.cuda.current_stream(self.dev)
-        self.stream.wait_stream(caller)
+        same = caller.cuda_stream == self.stream.cuda_stream
+        if not same:
+            self.stream.wait_stream(caller)
         L._check("pa_engine_execute", self._lib.pa_engine_execute(self._h))
-        caller.wait_stream(self.stream)
+        if not same:
+            caller.wait_stream(self.stream)
 
     def step(self, inputs_fn=None):
         """plan(), inputs written (from ``inputs_fn(plan)`` if given), execute();
