@@ -30,8 +30,9 @@
 //      NGK*G partial dots that a transposing butterfly over the KL lanes turns
 //      into one finished score per lane (G heads x 16 tokens spread over the
 //      wave) without any LDS traffic.
-//   V: each row is spread over RC lanes (one 16-byte chunk each, a fully
-//      coalesced row read); every lane accumulates its head-dim slice for all
+//   V: each row is spread over VL lanes (one 16-byte chunk each, 8 bytes for
+//      E4M3: a fully coalesced row read); every lane accumulates its
+//      head-dim slice for all
 //      G heads from the same registers, so V is read once per KV head however
 //      many query heads share it. Softmax weights reach the V lanes through a
 //      64-float LDS slot per wave.
@@ -60,7 +61,11 @@ constexpr int choose_k_lanes(int row_chunks, int group) {
 
 template <typename T, int D, int G>
 struct DecodeShape {
-  static constexpr int E = 16 / T::kBytes;          // elements per 16-byte chunk
+  // V is read in VB-byte chunks, one per lane and row: 16 bytes, or 8 for
+  // E4M3, whose 16-byte chunk would need 16 accumulators per head and lane.
+  static constexpr int VB = T::kBytes == 1 ? 8 : 16;
+  static constexpr int E = VB / T::kBytes;          // V elements per lane (8, 8, 4)
+  using VChunk = typename std::conditional<VB == 16, uint4, uint2>::type;
   static constexpr int RC = D * T::kBytes / 16;     // chunks per row
   static constexpr int QCH = T::Query::kBytes / T::kBytes;  // q chunks per K chunk
   static constexpr int QRC = RC * QCH;              // q chunks per row
@@ -71,7 +76,7 @@ struct DecodeShape {
   static constexpr int NV = NGK * G;                // partial dots per lane
   static constexpr int NVF = NV >= KL ? NV / KL : 1;  // finished scores per lane
   static constexpr int REP = NV >= KL ? 1 : KL / NV;  // lanes holding the same score
-  static constexpr int VL = RC;                     // lanes per V row
+  static constexpr int VL = D * T::kBytes / VB;     // lanes per V row
   static constexpr int RV = kWave / VL;             // V rows per load instruction
   static constexpr int NGV = kTile / RV;            // V load groups per tile
   static constexpr int NHS = NVF < G ? NVF : G;     // distinct heads among a lane's scores
@@ -191,11 +196,13 @@ __device__ __forceinline__ void load_k(const uint4* __restrict__ kbase, int lane
 
 template <typename Shape>
 __device__ __forceinline__ void load_v(const uint4* __restrict__ vbase, int lane,
-                                       uint4 (&vb)[Shape::NGV]) {
-  constexpr int RC = Shape::RC, VL = Shape::VL, RV = Shape::RV;
+                                       typename Shape::VChunk (&vb)[Shape::NGV]) {
+  using VC = typename Shape::VChunk;
+  constexpr int VL = Shape::VL, RV = Shape::RV;  // a row is VL chunks of VC
+  const VC* base = reinterpret_cast<const VC*>(vbase);
   const int vrow = lane / VL, vc = lane % VL;
 #pragma unroll
-  for (int gv = 0; gv < Shape::NGV; ++gv) vb[gv] = load_stream(vbase + (gv * RV + vrow) * RC + vc);
+  for (int gv = 0; gv < Shape::NGV; ++gv) vb[gv] = load_stream(base + (gv * RV + vrow) * VL + vc);
 }
 
 // ---------------------------------------------------------------------------
@@ -451,7 +458,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(DecodeArgs
   // wave-uniform; the last tile is peeled so that every pipelined iteration
   // prefetches unconditionally.
   uint4 kb[NGK][KCH];
-  uint4 vb[NGV];
+  typename S::VChunk vb[NGV];
 
   auto process = [&](int t, int blk, int64_t off_next, auto prefetch) {
     constexpr bool kPrefetch = decltype(prefetch)::value;
@@ -508,7 +515,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(DecodeArgs
       const int vrow = lane / VL;
 #pragma unroll
       for (int gv = 0; gv < NGV; ++gv)
-        if (!valid || tok0 + gv * RV + vrow >= n) vb[gv] = make_uint4(0, 0, 0, 0);
+        if (!valid || tok0 + gv * RV + vrow >= n) zero_chunk(vb[gv]);
     }
 
     // ---- online softmax: tile max per head, rescale on increase

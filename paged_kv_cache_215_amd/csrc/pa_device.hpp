@@ -26,6 +26,7 @@ struct FP8 {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
 // 16-byte load marked nontemporal (global_load_dwordx4 ... nt): for data read
 // exactly once per launch, such as the K/V rows of a decode step, so that the
@@ -34,6 +35,13 @@ __device__ __forceinline__ uint4 load_stream(const uint4* p) {
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+// The same for an 8-byte chunk (global_load_dwordx2 ... nt).
+__device__ __forceinline__ uint2 load_stream(const uint2* p) {
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ void zero_chunk(uint4& v) { v = make_uint4(0, 0, 0, 0); }
+__device__ __forceinline__ void zero_chunk(uint2& v) { v = make_uint2(0, 0); }
 
 // Widen the low / high bfloat16 of a packed pair: a bfloat16 is the high half
 // of the binary32 with the same value, so widening is a shift or a mask.
@@ -82,7 +90,8 @@ __device__ __forceinline__ void k_as_query(FP8, const uint4& k, uint4* out) {
 }
 
 // Widen one 16-byte chunk to binary32 (16 E4M3, 8 bfloat16 or 4 binary32
-// values). E4M3 uses v_cvt_pk_f32_fp8, exact for every code.
+// values), or an 8-byte chunk of 8 E4M3 codes. E4M3 uses v_cvt_pk_f32_fp8,
+// exact for every code.
 __device__ __forceinline__ void widen_chunk(BF16, const uint4& v, float* out) {
   out[0] = bf16_lo(v.x); out[1] = bf16_hi(v.x);
   out[2] = bf16_lo(v.y); out[3] = bf16_hi(v.y);
@@ -93,6 +102,16 @@ __device__ __forceinline__ void widen_chunk(FP8, const uint4& v, float* out) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+    out[4 * i] = a[0]; out[4 * i + 1] = a[1];
+    out[4 * i + 2] = b[0]; out[4 * i + 3] = b[1];
+  }
+}
+__device__ __forceinline__ void widen_chunk(FP8, const uint2& v, float* out) {
+  const uint32_t w[2] = {v.x, v.y};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
     const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
     const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
     out[4 * i] = a[0]; out[4 * i + 1] = a[1];
