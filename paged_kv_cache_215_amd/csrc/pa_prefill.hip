@@ -58,10 +58,10 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
   return (uint32_t)__builtin_bit_cast(unsigned short, static_cast<__bf16>(f));
 }
 
-template <int D, int G, int HPW>
+template <int D, int G, int HPW, int MW>
 struct PrefillShape {
   static constexpr int HG = G / HPW;              // head groups (waves across heads)
-  static constexpr int NW = HG >= 4 ? HG : 4;     // waves per workgroup
+  static constexpr int NW = HG >= MW ? HG : MW;   // waves per workgroup (at least MW)
   static constexpr int RT = NW / HG;              // 16-row sub-tiles per workgroup
   static constexpr int ROWS = 16 * RT;            // query rows per workgroup
   static constexpr int NT = NW * kWave;           // threads
@@ -79,10 +79,10 @@ struct PrefillShape {
 
 constexpr int kPfMaxBlocks = 1024;  // table entries one context split may span
 
-template <int D, int G, int HPW>
-__global__ __launch_bounds__((PrefillShape<D, G, HPW>::NT))
+template <int D, int G, int HPW, int MW>
+__global__ __launch_bounds__((PrefillShape<D, G, HPW, MW>::NT))
 __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
-  using S = PrefillShape<D, G, HPW>;
+  using S = PrefillShape<D, G, HPW, MW>;
   constexpr int DCH = S::DCH;
   __shared__ uint4 k_lds[2][kKeyTile * DCH];                          // swizzled K rows
   __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][D * kVtStride];  // V^T
@@ -446,25 +446,54 @@ int prefill_heads_per_wave(int group) {
   return h < 1 ? 1 : h;
 }
 
-int prefill_rows_per_workgroup(int group, int head_dim) {
+// Least waves per workgroup: more waves give a workgroup more 16-row
+// sub-tiles, so each staged K/V tile serves more query rows. Groups of 4
+// query heads take 8 waves (two sub-tiles of 16 rows per head), which
+// measured faster than 4 waves on a 512-row chunk against a 4096-token
+// context; other groups keep 4. The environment override exists for tuning
+// sweeps only.
+int prefill_min_waves(int group) {
+  static const int v = [] {
+    const char* s = std::getenv("PA_PREFILL_WAVES");
+    const int x = s ? std::atoi(s) : 0;
+    return x == 4 || x == 8 ? x : 0;
+  }();
+  return v ? v : (group == 4 ? 8 : 4);
+}
+
+// Heads per wave for this group and head size: four heads of d = 256 exceed
+// the register file, and with 8 waves per workgroup (at most 256 VGPRs) a
+// wave holds at most 256 / d heads.
+int prefill_group_heads_per_wave(int group, int head_dim) {
+  const int mw = prefill_min_waves(group);
   int hpw = prefill_heads_per_wave(group);
   if (head_dim > 128 && hpw > 2) hpw = 2;
+  while (mw == 8 && hpw * head_dim > 256) hpw /= 2;
+  return hpw;
+}
+
+int prefill_rows_per_workgroup(int group, int head_dim) {
+  const int mw = prefill_min_waves(group);
+  const int hpw = prefill_group_heads_per_wave(group, head_dim);
   const int hg = group / hpw;
-  const int nw = hg >= 4 ? hg : 4;
+  const int nw = hg >= mw ? hg : mw;
   return 16 * (nw / hg);
 }
 
 int prefill_kv_splits(int num_seqs, int max_q_len, int num_q_heads, int num_kv_heads,
                       int head_dim, int max_context_len) {
-  // Split the keys of each row tile until the launch has about one
-  // workgroup per CU, keeping at least 8 key tiles per split.
-  const int rows = prefill_rows_per_workgroup(num_q_heads / num_kv_heads, head_dim);
+  // Split the keys of each row tile until the launch has about 2048 waves
+  // (two per SIMD on 256 CUs), keeping at least 8 key tiles per split.
+  const int group = num_q_heads / num_kv_heads;
+  const int rows = prefill_rows_per_workgroup(group, head_dim);
   const int64_t wgs = (int64_t)num_seqs * num_kv_heads * ((max_q_len + rows - 1) / rows);
-  static const int target = [] {
+  const int waves = (rows / 16) * (group / prefill_group_heads_per_wave(group, head_dim));
+  static const int env_target = [] {
     const char* s = std::getenv("PA_PREFILL_TARGET_WGS");
     const int v = s ? std::atoi(s) : 0;
-    return v > 0 ? v : 512;
+    return v > 0 ? v : 0;
   }();
+  const int target = env_target ? env_target : 2048 / waves;
   int splits = 1;
   while (splits < 8 && wgs * splits < target &&
          (max_context_len / kKeyTile) / (2 * splits) >= 8)
@@ -478,7 +507,7 @@ int prefill_kv_splits(int num_seqs, int max_q_len, int num_q_heads, int num_kv_h
   return splits;
 }
 
-template <int D, int G, int HPW>
+template <int D, int G, int HPW, int MW>
 static hipError_t launch_pf(const PrefillArgs& a_in, hipStream_t stream) {
   static const int remap = [] {
     const char* s = std::getenv("PA_PREFILL_XCD");
@@ -486,9 +515,9 @@ static hipError_t launch_pf(const PrefillArgs& a_in, hipStream_t stream) {
   }();
   PrefillArgs a = a_in;
   a.xcd_remap = remap;
-  using S = PrefillShape<D, G, HPW>;
+  using S = PrefillShape<D, G, HPW, MW>;
   dim3 grid((a.max_q_len + S::ROWS - 1) / S::ROWS, a.num_kv_heads, a.num_seqs * a.kv_splits);
-  hipLaunchKernelGGL((prefill_kernel<D, G, HPW>), grid, dim3(S::NT), 0, stream, a);
+  hipLaunchKernelGGL((prefill_kernel<D, G, HPW, MW>), grid, dim3(S::NT), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.kv_splits == 1) return err;
   hipLaunchKernelGGL((prefill_merge_kernel<D>), dim3(a.num_q_heads, a.total_q), dim3(kWave), 0,
@@ -496,25 +525,31 @@ static hipError_t launch_pf(const PrefillArgs& a_in, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, int G>
+template <int D, int G, int MW>
 static hipError_t launch_ph(const PrefillArgs& a, hipStream_t stream) {
-  const int hpw = prefill_heads_per_wave(G);
-  if constexpr (G >= 4 && D <= 128) {  // four heads of d = 256 exceed the register file
-    if (hpw == 4) return launch_pf<D, G, 4>(a, stream);
+  const int hpw = prefill_group_heads_per_wave(G, D);
+  if constexpr (G >= 4 && D <= 128 && (MW == 4 || 4 * D <= 256)) {
+    if (hpw == 4) return launch_pf<D, G, 4, MW>(a, stream);
   }
-  if constexpr (G >= 2) {
-    if (hpw == 2) return launch_pf<D, G, 2>(a, stream);
+  if constexpr (G >= 2 && (MW == 4 || 2 * D <= 256)) {
+    if (hpw == 2) return launch_pf<D, G, 2, MW>(a, stream);
   }
-  return launch_pf<D, G, 1>(a, stream);
+  return launch_pf<D, G, 1, MW>(a, stream);
+}
+
+template <int D, int G>
+static hipError_t launch_pw(const PrefillArgs& a, hipStream_t stream) {
+  if (prefill_min_waves(G) == 8) return launch_ph<D, G, 8>(a, stream);
+  return launch_ph<D, G, 4>(a, stream);
 }
 
 template <int D>
 static hipError_t launch_pg(const PrefillArgs& a, hipStream_t stream) {
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: return launch_ph<D, 1>(a, stream);
-    case 2: return launch_ph<D, 2>(a, stream);
-    case 4: return launch_ph<D, 4>(a, stream);
-    case 8: return launch_ph<D, 8>(a, stream);
+    case 1: return launch_pw<D, 1>(a, stream);
+    case 2: return launch_pw<D, 2>(a, stream);
+    case 4: return launch_pw<D, 4>(a, stream);
+    case 8: return launch_pw<D, 8>(a, stream);
   }
   return hipErrorInvalidValue;
 }
