@@ -120,11 +120,28 @@ def reshape_and_cache_fp8_ref(key, value, key_cache, value_cache, slot_mapping,
     return kc, vc
 
 
+class _DequantizedView:
+    """The float64 values ``dequantize(codes, scale)`` of a code cache,
+    computed only for the rows an index selects: ``view[blocks, head, rows,
+    cols]`` with an integer head, as the sequence gather of the decode
+    oracle indexes. Same values as dequantizing the whole cache first,
+    without holding a float64 copy of it (eight times the code bytes)."""
+
+    def __init__(self, codes, scale):
+        self.codes = codes
+        self.scale = np.asarray(scale, dtype=np.float32).astype(np.float64)
+        self.shape = codes.shape
+
+    def __getitem__(self, index):
+        blocks, head, rows, cols = index
+        return e4m3_value(self.codes[blocks, head, rows, cols]) * self.scale[head]
+
+
 def decode_fp8_ref(query, key_codes, value_codes, k_scale, v_scale, block_tables,
                    context_lens, scale):
     """Decode attention over an FP8 cache: the attention of ``decode_ref`` on
     the dequantized K and V (float64 output)."""
     from .paged_ref import decode_ref
 
-    return decode_ref(to_f64(query), dequantize(key_codes, k_scale),
-                      dequantize(value_codes, v_scale), block_tables, context_lens, scale)
+    return decode_ref(to_f64(query), _DequantizedView(key_codes, k_scale),
+                      _DequantizedView(value_codes, v_scale), block_tables, context_lens, scale)
