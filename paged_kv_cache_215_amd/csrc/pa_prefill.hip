@@ -275,6 +275,10 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
       s0[hh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       s1[hh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
+    // Waves raise their priority while they issue matrix products: of the
+    // two waves sharing a SIMD, the one that reaches its products first
+    // keeps the matrix unit while the other runs its softmax.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < S::KSTEPS; ++ks) {
       const int c = 4 * ks + lq;
@@ -289,6 +293,7 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
       }
     }
 
+    __builtin_amdgcn_s_setprio(0);
     // The next tile's global loads go out once the score products have been
     // issued: issued before them, the compiler made those products wait for
     // the loads.
@@ -361,6 +366,7 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
     }
 
     // ---- O^T += V^T (P_hi + P_lo)^T, one V^T operand read for all heads
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int dt = 0; dt < S::DTILES; ++dt) {
       const bf16x8_t vop = __builtin_bit_cast(
@@ -371,6 +377,7 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
         acc[hh][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_lo[hh], acc[hh][dt], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     if (has_next) store_lds(buf ^ 1);
     __syncthreads();  // next buffer complete; this one free for reuse
   }
