@@ -755,11 +755,18 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeArgs a) {
       const float w_lane = p < nparts ? ml[2 * p + 1] * fast_exp2(ml[2 * p] - M) : 0.f;
       L += w_lane;
       const int cnt = nparts - p0 < kWave ? nparts - p0 : kWave;
-#pragma unroll 4
-      for (int j = 0; j < cnt; ++j) {
-        const float w = __shfl(w_lane, j);
+      // four partitions per step, so that their loads are in flight together
+      for (int j0 = 0; j0 < cnt; j0 += 4) {
 #pragma unroll
-        for (int e = 0; e < PER; ++e) o[e] = __builtin_fmaf(w, po[(int64_t)(p0 + j) * D + e], o[e]);
+        for (int jj = 0; jj < 4; ++jj) {
+          const int j = j0 + jj;
+          const float w = __shfl(w_lane, j < cnt ? j : 0);
+          if (j < cnt) {
+#pragma unroll
+            for (int e = 0; e < PER; ++e)
+              o[e] = __builtin_fmaf(w, po[(int64_t)(p0 + j) * D + e], o[e]);
+          }
+        }
       }
     }
 #pragma unroll
