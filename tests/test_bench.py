@@ -1,0 +1,64 @@
+"""Host-side parts of bench.py (CPU): the algorithmic-byte accounting that the
+roofline divides by, the one-GPU guard, and the source hash that ties the
+committed HBM counters to the kernel they were taken on."""
+
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+import bench
+from workloads import make_config_case
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_c3_algorithmic_bytes_closed_form():
+    # 64 sequences x 8192 tokens, 4 KV heads of d 256 in BF16 (K and V), the
+    # BF16 query and float32 output of 16 heads, one int32 table entry per
+    # block of 32 tokens
+    c = make_config_case("c3_full_step", structure_only=True)
+    got = bench.decode_bytes(c.layout, 64, 16, 4, 256, 2)
+    kv = 2 * 64 * 8192 * 4 * 256 * 2
+    q, out, table = 64 * 16 * 256 * 2, 64 * 16 * 256 * 4, 64 * (8192 // 32) * 4
+    assert got == kv + q + out + table == 2_149_122_048
+
+
+def test_fp8_bytes_count_one_byte_per_element_and_the_scales():
+    c = make_config_case("c3_full_step", structure_only=True)
+    bf16 = bench.decode_bytes(c.layout, 64, 16, 4, 256, 2)
+    fp8 = bench.decode_bytes(c.layout, 64, 16, 4, 256, 2, kv_bytes=1)
+    kv_bf16 = 2 * 64 * 8192 * 4 * 256 * 2
+    assert fp8 == bf16 - kv_bf16 // 2 + 2 * 4 * 4
+
+
+def test_shared_prompt_blocks_count_once():
+    # 8 prompts of 4096 tokens, each shared by 16 rollouts whose private tails
+    # have their own blocks: unique K/V rows = 8 * 4096 + sum of the tails
+    c = make_config_case("c4_grpo_cow", structure_only=True)
+    lens = c.layout.context_lens.astype(np.int64)
+    per_token = 2 * 4 * 256 * 2
+    fixed = bench.decode_bytes(c.layout, 128, 16, 4, 256, 2) - int(lens.sum()) * per_token
+    unique = bench.decode_bytes(c.layout, 128, 16, 4, 256, 2, unique_blocks=True)
+    assert unique - fixed == (8 * 4096 + int((lens - 4096).sum())) * per_token
+    assert unique < bench.decode_bytes(c.layout, 128, 16, 4, 256, 2)
+
+
+def test_more_than_one_gpu_is_refused():
+    proc = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                          capture_output=True, text=True, timeout=120)
+    assert proc.returncode == 2
+    assert "one GPU" in proc.stderr
+    assert proc.stdout == ""
+
+
+def test_source_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    src = tmp_path / "k.hip"
+    src.write_text("int f(int x) { return x + 1; }  // add one\n")
+    h0 = bench.source_hash(["k.hip"])
+    src.write_text("/* a block\n comment */\nint f(int x) {\n  return x + 1;  // one more\n}\n")
+    assert bench.source_hash(["k.hip"]) == h0
+    src.write_text("int f(int x) { return x + 2; }\n")
+    assert bench.source_hash(["k.hip"]) != h0
