@@ -18,7 +18,11 @@ HIP kernels behind the C ABI in ``include/pa.h``:
                              and the device block copy it asks for;
 * ``pa_swap_out`` / ``pa_swap_in`` - batched block moves between the device
                              cache and a pinned host pool (preemption);
-* ``Scheduler``            - the iteration-level batching scheduler (C++).
+* ``Scheduler``            - the iteration-level batching scheduler (C++);
+* ``engine.Engine`` / ``engine.NativeEngine`` - step drivers that run the
+                             scheduler's plans on the GPU (the native one is
+                             the C++ driver of ``include/pa_engine.h``), with
+                             decode-only iterations replayed from a HIP graph.
 
 The Python functions below only marshal torch tensors to that ABI.
 """
