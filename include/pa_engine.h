@@ -66,6 +66,15 @@ typedef struct {
   float* const* out_pre;          /* device float32 [chunk_tokens, Hq, d] */
 } pa_engine_buffers;
 
+/* Creates the engine: its scheduler, index buffers, pinned staging and
+ * workspaces, and (use_graph) the captured decode-only graph. Returns
+ * PA_ERR_NULL for a NULL cfg, bufs, out or pointer array; PA_ERR_SHAPE for
+ * non-positive head counts or sizes, and the scheduler's own errors
+ * (pa_sched_create); PA_ERR_UNSUPPORTED when pa_decode has no kernel for the
+ * head shape or block size; PA_ERR_HIP when an allocation or the capture
+ * fails. The
+ * pointers in the arrays are not dereferenced here. *out is NULL on error
+ * and nothing stays allocated. */
 pa_status_t pa_engine_create(const pa_engine_config* cfg, const pa_engine_buffers* bufs,
                              const int32_t* prompt_lens, const int32_t* output_lens,
                              int32_t num_requests, void* stream, pa_engine** out);
@@ -74,11 +83,18 @@ void pa_engine_destroy(pa_engine* e);
 int32_t pa_engine_done(const pa_engine* e);
 
 /* Plan the next iteration (the scheduler's step). The plan's arrays stay
- * valid until the next pa_engine_plan. */
+ * valid until the next pa_engine_plan. PA_ERR_NULL for NULL arguments, else
+ * the status of pa_sched_step (PA_ERR_OUT_OF_BLOCKS: the host pool cannot
+ * take a preemption; the engine should then be destroyed). */
 pa_status_t pa_engine_plan(pa_engine* e, pa_step_plan* plan);
 
 /* Enqueue the device work of the last plan. Returns after enqueueing; it
- * waits only for the staging set it reuses (written two iterations ago). */
+ * waits only for the staging set it reuses (written two iterations ago).
+ * PA_ERR_NULL for NULL; PA_ERR_STATE when no plan is pending (each plan is
+ * executed once); PA_ERR_SHAPE when the plan exceeds the registered buffers
+ * (cannot happen with the engine's own scheduler); otherwise the first error
+ * of the entry points it calls (PA_ERR_HIP for a failed launch or copy), in
+ * which case part of the iteration may have been enqueued. */
 pa_status_t pa_engine_execute(pa_engine* e);
 
 /* Iterations executed so far and how many of them were graph launches. */
