@@ -72,9 +72,8 @@ typedef struct {
  * non-positive head counts or sizes, and the scheduler's own errors
  * (pa_sched_create); PA_ERR_UNSUPPORTED when pa_decode has no kernel for the
  * head shape or block size; PA_ERR_HIP when an allocation or the capture
- * fails. The
- * pointers in the arrays are not dereferenced here. *out is NULL on error
- * and nothing stays allocated. */
+ * fails. The pointers in the arrays are not dereferenced here. *out is NULL
+ * on error and nothing stays allocated. */
 pa_status_t pa_engine_create(const pa_engine_config* cfg, const pa_engine_buffers* bufs,
                              const int32_t* prompt_lens, const int32_t* output_lens,
                              int32_t num_requests, void* stream, pa_engine** out);
