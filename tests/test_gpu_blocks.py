@@ -11,7 +11,7 @@ import torch
 import oracle
 import paged_kv_cache_215_amd as pa
 from gpu_helpers import ATOL, max_abs_err, say
-from oracle.block_manager import BlockManagerRef, copy_blocks_ref
+from oracle.block_manager import BlockManagerRef, copy_blocks_ref, move_blocks_ref
 from workloads import to_numpy_bits
 
 pytestmark = pytest.mark.gpu
@@ -45,6 +45,39 @@ def test_copy_blocks_bit_exact(dtype, block_size, head_dim):
     want_k, want_v = copy_blocks_ref(kb, vb, valid)
     say(f"[copy] {dtype} bs{block_size} d{head_dim}: {len(valid)} pairs")
     pa.pa_copy_blocks(kc, vc, torch.from_numpy(pairs).to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(to_numpy_bits(kc).view(np.uint8), want_k.view(np.uint8))
+    assert np.array_equal(to_numpy_bits(vc).view(np.uint8), want_v.view(np.uint8))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32, torch.uint8])
+@pytest.mark.parametrize("block_size", [16, 32])
+def test_swap_round_trip_every_element_type(dtype, block_size):
+    # device -> pinned host pool -> other device blocks, bit for bit; pairs
+    # outside either pool are skipped
+    nb, nh, hkv, d = 96, 40, 4, 128
+    kc, vc = _pool(nb, hkv, block_size, d, dtype, seed=block_size + 1)
+    hk = torch.zeros((nh,) + tuple(kc.shape[1:]), dtype=dtype).pin_memory()
+    hv = torch.zeros((nh,) + tuple(kc.shape[1:]), dtype=dtype).pin_memory()
+    rng = np.random.default_rng(block_size)
+    src = rng.permutation(nb)[:30]
+    dst = rng.permutation(nh)[:30]
+    out_pairs = np.stack([src, dst], axis=1).astype(np.int64)
+    out_pairs = np.concatenate([out_pairs, [[nb, 1], [2, nh], [-3, 0]]])
+    kb, vb = to_numpy_bits(kc), to_numpy_bits(vc)
+    valid_out = [(int(a), int(b)) for a, b in out_pairs if 0 <= a < nb and 0 <= b < nh]
+    want_hk, want_hv = move_blocks_ref(kb, vb, to_numpy_bits(hk), to_numpy_bits(hv), valid_out)
+    say(f"[swap] {dtype} bs{block_size}: {len(valid_out)} blocks out")
+    pa.pa_swap_out(kc, vc, hk, hv, torch.from_numpy(out_pairs).to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(to_numpy_bits(hk).view(np.uint8), want_hk.view(np.uint8))
+    assert np.array_equal(to_numpy_bits(hv).view(np.uint8), want_hv.view(np.uint8))
+    back = rng.permutation(nb)[:30]
+    in_pairs = np.stack([dst, back], axis=1).astype(np.int64)
+    in_pairs = np.concatenate([in_pairs, [[nh, 0], [0, nb]]])
+    valid_in = [(int(a), int(b)) for a, b in in_pairs if 0 <= a < nh and 0 <= b < nb]
+    want_k, want_v = move_blocks_ref(want_hk, want_hv, kb, vb, valid_in)
+    pa.pa_swap_in(kc, vc, hk, hv, torch.from_numpy(in_pairs).pin_memory())
     torch.cuda.synchronize()
     assert np.array_equal(to_numpy_bits(kc).view(np.uint8), want_k.view(np.uint8))
     assert np.array_equal(to_numpy_bits(vc).view(np.uint8), want_v.view(np.uint8))
