@@ -545,6 +545,13 @@ def run_copy_swap(args):
     in_pairs = torch.from_numpy(np.stack([np.arange(n), perm[n:2 * n]], 1).astype(np.int64)).to(dev)
     out_ms = _event_ms(lambda: pa.pa_swap_out(kc, vc, hk, hv, out_pairs), 5, stream)
     in_ms = _event_ms(lambda: pa.pa_swap_in(kc, vc, hk, hv, in_pairs), 5, stream)
+    # context for the copy roofline: the runtime's own contiguous
+    # device-to-device copy of the same number of bytes (read + write)
+    flat_src = torch.empty(n * block_bytes // 2, dtype=torch.bfloat16, device=dev)
+    flat_dst = torch.empty_like(flat_src)
+    rt_ms = _event_ms(lambda: flat_dst.copy_(flat_src), 20, stream)
+    rt_gbs = 2 * flat_src.numel() * 2 / (rt_ms / 1e3) / 1e9
+    del flat_src, flat_dst
     moved = n * block_bytes
     res = {
         "metric": "KV block moves: copy-on-write copies (HBM GB/s) and swaps to/from pinned host "
@@ -556,7 +563,8 @@ def run_copy_swap(args):
         "copy_blocks": {"avg_call_us": round(copy_ms * 1e3, 2), "achieved": round(copy_gbs, 1),
                         "roofline": {"bound": "hbm", "achieved": round(copy_gbs, 1),
                                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                     "frac": round(copy_gbs / HBM_PEAK_GBS, 4), "traffic": None}},
+                                     "frac": round(copy_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                        "runtime_contiguous_copy_gbs": round(rt_gbs, 1)},
         "swap_out": {"avg_call_us": round(out_ms * 1e3, 2),
                      "achieved_gbs": round(moved / (out_ms / 1e3) / 1e9, 2)},
         "swap_in": {"avg_call_us": round(in_ms * 1e3, 2),
