@@ -46,6 +46,11 @@
 namespace pa {
 
 constexpr int kTile = 16;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 constexpr int kMaxPartBlocks = 512;  // table entries staged per partition
 
 constexpr int choose_k_lanes(int row_chunks, int group) {
@@ -718,6 +723,282 @@ __global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(DecodeArgs
   }
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core partition kernel for groups of 8 query heads over BF16 caches.
+//
+// With 8 query heads per KV head the VALU kernel spends 4 * 8 * d flops per
+// (token, KV head) against 4 d bytes of K and V: about 8 flops per byte,
+// enough to make it wait on its own arithmetic (about 61 % of the HBM rate at
+// d = 128). Here the contractions run on v_mfma instructions, with the G
+// heads as the 16 columns of a 16 x 16 product (8 of them padding):
+//   S^T[16 keys x 16] = K[16 keys x d] . Q^T[d x 16]   (16x16x32, d/32 steps)
+//     A = K rows straight from HBM: lane l reads 16 bytes of key l % 16 at
+//         dims 32 ks + 8 (l / 16) .. + 7, the A operand layout;
+//     B = Q^T: lane l holds head l % 16 at the same dims (registers).
+//   O^T[16 dims x 16] += V^T[16 dims x 16 keys] . P^T[16 keys x 16]  (16x16x16)
+//     B = P^T: lane l holds the weights of keys 4 (l / 16) .. + 3 for head
+//         l % 16, which is where the score product left those scores;
+//     A = V^T: the V tile goes through this wave's LDS region row-major and
+//         is read with ds_read_b64_tr_b16 (lane layout checked on the
+//         hardware): output lane i of a 16-lane group q gets V[4q + k][d0 + i]
+//         for k = 0..3 when lane j of the group supplies key row 4q + j/4 at
+//         dims d0 + 4 (j % 4).
+// The weights enter PV as BF16 hi + lo terms (16 significant bits), as in
+// the prefill kernel, and the running sum uses the same split values. The
+// plan, the work units, the persistent loop, the partials and the merge
+// kernel are those of the VALU kernel.
+template <int D, int NW>
+__global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeArgs a) {
+  constexpr int G = 8;
+  constexpr int kWaves = NW;
+  constexpr int kThreads = NW * kWave;
+  constexpr int DCH = D / 8;                   // 16-byte chunks per row
+  constexpr int KSTEPS = D / 32;               // k-steps of the score product
+  constexpr int DT = D / 16;                   // 16-dim tiles of the output
+  constexpr int SWZ = (DCH < 16 ? DCH : 16) - 1;
+  constexpr int VPL = kTile * DCH / kWave;     // V chunks per lane per tile
+  static_assert(VPL >= 1 && kTile * DCH % kWave == 0, "V tile shape");
+  // a wave's V tile (kTile rows of D bf16) and its share of the final merge
+  // (G heads of D floats) are both 32 D bytes; the merge reuses the region
+  static_assert(kTile * DCH * 16 == G * D * 4, "V tile and merge share a region");
+
+  __shared__ PlanLds s_plan;
+  __shared__ int s_bt[kMaxPartBlocks];
+  __shared__ __attribute__((aligned(16))) uint4 s_region[kWaves][kTile * DCH];
+  __shared__ float s_m[kWaves][G];
+  __shared__ float s_l[kWaves][G];
+
+  const int bs_log2 = a.block_size_log2;
+  const int bs = 1 << bs_log2;
+  const int tid = threadIdx.x;
+  build_plan<NW>(a, s_plan);
+  const int P = s_plan.part_tokens;
+  if (blockIdx.x == 0 && tid == 0) {  // for the merge kernel
+    a.plan->part_tokens = P;
+    a.plan->max_nparts = s_plan.max_nparts;
+  }
+
+  auto unit = [&](const int seq, const int kvh, const int part) {
+  const int n = s_plan.lens[seq];
+  const int start = part * P;
+  if (n == 0) {  // empty context: a zero row
+    for (int idx = tid; idx < G * D / 4; idx += kThreads)
+      reinterpret_cast<float4*>(a.out)[((int64_t)seq * a.num_q_heads + (int64_t)kvh * G) * (D / 4) + idx] =
+          make_float4(0.f, 0.f, 0.f, 0.f);
+    return;
+  }
+  if (start >= n) return;
+  const int end = min(start + P, n);
+  const int nparts = (n + P - 1) / P;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave;
+  const int col = lane % 16, grp = lane / 16;
+
+  // Q^T operand: head col of the group (zero for the padding columns)
+  bf16x8_t qop[KSTEPS];
+  {
+    const uint4* qb = reinterpret_cast<const uint4*>(a.query) +
+                      ((int64_t)seq * a.num_q_heads + (int64_t)kvh * G + (col < G ? col : 0)) * DCH;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const uint4 v = qb[4 * ks + grp];
+      qop[ks] = __builtin_bit_cast(bf16x8_t, col < G ? v : make_uint4(0, 0, 0, 0));
+    }
+  }
+
+  const int blk0 = start >> bs_log2;
+  const int nblk = ((end - start) + bs - 1) >> bs_log2;
+  for (int i = tid; i < nblk; i += kThreads) {
+    const int e = a.block_tables[(int64_t)seq * a.max_blocks_per_seq + blk0 + i];
+    s_bt[i] = (e >= 0 && (int64_t)e < a.num_blocks) ? e : -1;
+  }
+  __syncthreads();
+
+  const uint4* kcache = reinterpret_cast<const uint4*>(a.key_cache);
+  const uint4* vcache = reinterpret_cast<const uint4*>(a.value_cache);
+  const int64_t block_stride = (int64_t)a.num_kv_heads * bs * DCH;  // 16-byte chunks
+  const int64_t head_off = (int64_t)kvh * bs * DCH;
+  const int ntiles = (end - start + kTile - 1) / kTile;
+  uint4* vt = s_region[wave];
+
+  auto tile_block = [&](int t) -> int {
+    return __builtin_amdgcn_readfirstlane(s_bt[(t * kTile) >> bs_log2]);
+  };
+  auto tile_offset = [&](int t, int blk) -> int64_t {
+    return (int64_t)(blk < 0 ? 0 : blk) * block_stride + head_off +
+           (int64_t)((start + t * kTile) & (bs - 1)) * DCH;
+  };
+
+  f32x4_t acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;  // head col, log2 units (the same in the 4 lanes of a column)
+  float l_part = 0.f;       // sum of this lane's own weights
+
+  // K operand and V chunks of a tile, one tile ahead of the arithmetic
+  uint4 kop[KSTEPS];
+  uint4 vreg[VPL];
+  auto load_tile = [&](int64_t off) {
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) kop[ks] = load_stream(kcache + off + col * DCH + 4 * ks + grp);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int idx = lane + kWave * i;
+      vreg[i] = load_stream(vcache + off + (idx / DCH) * DCH + idx % DCH);
+    }
+  };
+
+  auto process = [&](int t, int blk, int64_t off_next, auto prefetch) {
+    constexpr bool kPrefetch = decltype(prefetch)::value;
+    const int tok0 = start + t * kTile;
+    const bool valid = blk >= 0;
+
+    // V rows of the tile into this wave's region (chunk c of row r at
+    // c ^ (r & SWZ)); rows past the context (or of an invalid block) are
+    // zeroed, they may hold anything, NaN included
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int idx = lane + kWave * i;
+      const int r = idx / DCH, c = idx % DCH;
+      const uint4 v = (valid && tok0 + r < n) ? vreg[i] : make_uint4(0, 0, 0, 0);
+      vt[r * DCH + (c ^ (r & SWZ))] = v;
+    }
+
+    // scores of keys tok0 + 4 grp + i for head col
+    f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop[ks]), qop[ks], sc,
+                                                  0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kPrefetch) load_tile(off_next);
+    __builtin_amdgcn_sched_barrier(0);
+
+    float sv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tok = tok0 + 4 * grp + i;
+      sv[i] = (valid && tok < n) ? sc[i] * a.scale_log2 : -INFINITY;
+    }
+    // online softmax per head: the column's 16 scores sit in lanes col,
+    // col + 16, col + 32, col + 48 (4 each)
+    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mx = pair_max<16>(mx);
+    mx = pair_max<32>(mx);
+    // rescale only when a head's maximum grew by more than 2^8 (weights of
+    // up to 2^8 stay far from float32 / BF16 overflow)
+    const float m_new = fmaxf(m_run, mx);
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run + 8.f) != 0) {
+      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+      l_part *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+      m_run = m_new;
+    }
+    const float moff = m_run == -INFINITY ? 0.f : m_run;
+    uint32_t ph[4], pl[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pf = fast_exp2(sv[i] - moff);
+      ph[i] = (uint32_t)__builtin_bit_cast(unsigned short, static_cast<__bf16>(pf));
+      const float hi = __uint_as_float(ph[i] << 16);
+      pl[i] = (uint32_t)__builtin_bit_cast(unsigned short, static_cast<__bf16>(pf - hi));
+      l_part += hi + __uint_as_float(pl[i] << 16);
+    }
+    const i16x4_t p_hi = __builtin_bit_cast(i16x4_t, make_uint2(ph[0] | (ph[1] << 16), ph[2] | (ph[3] << 16)));
+    const i16x4_t p_lo = __builtin_bit_cast(i16x4_t, make_uint2(pl[0] | (pl[1] << 16), pl[2] | (pl[3] << 16)));
+
+    // O^T += V^T P^T over the tile's 16 keys, 16 dims at a time
+    const int vrow = 4 * grp + col / 4;  // the key row this lane supplies
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int dim = 16 * dt + 4 * (col % 4);
+      const int c = dim / 8, half = (dim / 4) & 1;
+      const char* src = reinterpret_cast<const char*>(vt + vrow * DCH + (c ^ (vrow & SWZ))) + 8 * half;
+      const i16x4_t vop = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)src);
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, p_hi, acc[dt], 0, 0, 0);
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, p_lo, acc[dt], 0, 0, 0);
+    }
+  };
+
+  int t = wave;
+  if (t < ntiles) {
+    int blk = tile_block(t);
+    load_tile(tile_offset(t, blk));
+    for (; t + kWaves < ntiles; t += kWaves) {
+      const int blk_next = tile_block(t + kWaves);
+      process(t, blk, tile_offset(t + kWaves, blk_next), std::true_type{});
+      blk = blk_next;
+    }
+    process(t, blk, 0, std::false_type{});
+  }
+
+  // ---- wave totals per head, into this wave's region (its V rows are done)
+  float l_col = pair_sum<16>(l_part);
+  l_col = pair_sum<32>(l_col);
+  if (grp == 0 && col < G) {
+    s_m[wave][col] = m_run;
+    s_l[wave][col] = l_col;
+  }
+  float4* s_acc = reinterpret_cast<float4*>(vt);  // [G][D / 4]
+  if (col < G) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      s_acc[col * (D / 4) + 4 * dt + grp] = make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
+  }
+  __syncthreads();
+
+  // ---- merge the waves and write o (normalised), m, l
+  for (int idx = tid; idx < G * D / 4; idx += kThreads) {
+    const int g = idx / (D / 4), d4 = idx % (D / 4);
+    float M = s_m[0][g];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][g]);
+    float L = 0.f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float sw = fast_exp2(s_m[w][g] - M);
+      L += sw * s_l[w][g];
+      const float4 x = reinterpret_cast<const float4*>(s_region[w])[g * (D / 4) + d4];
+      o.x += sw * x.x; o.y += sw * x.y; o.z += sw * x.z; o.w += sw * x.w;
+    }
+    const float inv = 1.f / L;
+    o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
+    const int64_t head = (int64_t)seq * a.num_q_heads + (int64_t)kvh * G + g;
+    if (nparts == 1) {
+      reinterpret_cast<float4*>(a.out)[head * (D / 4) + d4] = o;
+    } else {
+      const int64_t slot = head * a.max_parts + part;
+      reinterpret_cast<float4*>(a.part_o)[slot * (D / 4) + d4] = o;
+      if (d4 == 0) {
+        a.part_ml[2 * slot] = M;
+        a.part_ml[2 * slot + 1] = L;
+      }
+    }
+  }
+  };  // unit
+
+  // persistent loop: as in the VALU kernel
+  const int n_full = s_plan.full_total * a.num_kv_heads;
+  const int n_units = (s_plan.full_total + a.num_seqs) * a.num_kv_heads;
+  for (int u = blockIdx.x; u < n_full; u += gridDim.x) {
+    const int2 e = plan_unit(s_plan, a.num_seqs, u / a.num_kv_heads);
+    unit(e.x, u % a.num_kv_heads, e.y);
+    __syncthreads();  // LDS is reused by the next unit
+  }
+  for (;;) {
+    if (tid == 0) s_plan.ticket = atomicAdd(&a.plan->ticket, 1);
+    __syncthreads();
+    const int u = n_full + s_plan.ticket;
+    __syncthreads();  // every thread has read the ticket before it is reused
+    if (u < n_full || u >= n_units) break;  // (below n_full: workspace never zero-filled)
+    const int2 e = plan_unit(s_plan, a.num_seqs, u / a.num_kv_heads);
+    unit(e.x, u % a.num_kv_heads, e.y);
+    __syncthreads();
+  }
+}
+
 // Merge of the per-partition partials of one (sequence, query head):
 // out = sum_p w_p o_p / sum_p w_p with w_p = l_p * 2^(m_p - max_p m_p).
 // Persistent over rows; when the plan gave every sequence one partition the
@@ -852,9 +1133,10 @@ int resident_per_cu(Kernel k, int threads) {
 
 }  // namespace
 
-template <typename T, int D, int G, int NW>
-static hipError_t launch_nw(const DecodeArgs& a, hipStream_t stream) {
-  static const int per_cu = resident_per_cu(decode_partition_kernel<T, D, G, NW>, NW * kWave);
+// Launch of a partition kernel (NW waves per workgroup) and the merge kernel.
+template <int D, int QueryBytes, int NW, auto Kernel>
+static hipError_t launch_kernel(const DecodeArgs& a, hipStream_t stream) {
+  static const int per_cu = resident_per_cu(Kernel, NW * kWave);
   const int cus = device_cus();
   // Batches above kPlanSeqs sequences run as consecutive launches of at most
   // kPlanSeqs sequences each, sharing the workspace in stream order.
@@ -862,7 +1144,7 @@ static hipError_t launch_nw(const DecodeArgs& a, hipStream_t stream) {
     DecodeArgs c = a;
     c.num_seqs = a.num_seqs - s0 < kPlanSeqs ? a.num_seqs - s0 : kPlanSeqs;
     c.out = a.out + (int64_t)s0 * a.num_q_heads * D;
-    c.query = static_cast<const char*>(a.query) + (int64_t)s0 * a.num_q_heads * D * T::Query::kBytes;
+    c.query = static_cast<const char*>(a.query) + (int64_t)s0 * a.num_q_heads * D * QueryBytes;
     c.block_tables = a.block_tables + (int64_t)s0 * a.max_blocks_per_seq;
     c.context_lens = a.context_lens + s0;
     c.plan_cus = cus;
@@ -870,8 +1152,7 @@ static hipError_t launch_nw(const DecodeArgs& a, hipStream_t stream) {
     const int64_t most_units = (int64_t)c.num_seqs * c.num_kv_heads * c.max_parts;
     const int64_t slots = (int64_t)cus * per_cu;
     const int64_t grid = most_units < slots ? most_units : slots;
-    hipLaunchKernelGGL((decode_partition_kernel<T, D, G, NW>), dim3((unsigned)grid),
-                       dim3(NW * kWave), 0, stream, c);
+    hipLaunchKernelGGL(Kernel, dim3((unsigned)grid), dim3(NW * kWave), 0, stream, c);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int64_t rows = (int64_t)c.num_seqs * c.num_q_heads;
@@ -885,18 +1166,31 @@ static hipError_t launch_nw(const DecodeArgs& a, hipStream_t stream) {
   return hipSuccess;
 }
 
+template <typename T, int D, int G, int NW>
+static hipError_t launch_nw(const DecodeArgs& a, hipStream_t stream) {
+  return launch_kernel<D, T::Query::kBytes, NW, decode_partition_kernel<T, D, G, NW>>(a, stream);
+}
+
 template <typename T, int D, int G>
 static hipError_t launch_t(const DecodeArgs& a, int waves, hipStream_t stream) {
-  // 8-wave workgroups are limited to 256 VGPRs per lane; the d = 256 shapes
-  // with 8 query heads per KV head or float32 data, float32 at d = 128 with 8
-  // query heads, and FP8 with 8 query heads per KV head (16 accumulators per
-  // head and lane) need more and use 4 waves.
-  constexpr bool kFits8 = !(D == 256 && (G == 8 || T::kBytes == 4)) &&
-                          !(D == 128 && G == 8 && T::kBytes == 4) && G * (16 / T::kBytes) <= 64;
-  if constexpr (kFits8) {
-    if (waves == 8) return launch_nw<T, D, G, 8>(a, stream);
+  if constexpr (G == 8 && std::is_same<T, BF16>::value) {
+    // groups of 8 query heads over BF16 caches run on the matrix cores; at
+    // d = 256 the operands and accumulators need more than the 256 VGPRs of
+    // 8-wave workgroups, so those use 4 waves
+    if constexpr (D > 128) return launch_kernel<D, 2, 4, decode_mfma_kernel<D, 4>>(a, stream);
+    else return launch_kernel<D, 2, 8, decode_mfma_kernel<D, 8>>(a, stream);
+  } else {
+    // 8-wave workgroups are limited to 256 VGPRs per lane; the d = 256 shapes
+    // with 8 query heads per KV head or float32 data, float32 at d = 128 with
+    // 8 query heads, and FP8 with 8 query heads per KV head (16 accumulators
+    // per head and lane) need more and use 4 waves.
+    constexpr bool kFits8 = !(D == 256 && (G == 8 || T::kBytes == 4)) &&
+                            !(D == 128 && G == 8 && T::kBytes == 4) && G * (16 / T::kBytes) <= 64;
+    if constexpr (kFits8) {
+      if (waves == 8) return launch_nw<T, D, G, 8>(a, stream);
+    }
+    return launch_nw<T, D, G, 4>(a, stream);
   }
-  return launch_nw<T, D, G, 4>(a, stream);
 }
 
 template <typename T, int D>
