@@ -19,8 +19,11 @@
 // the GQA group, the waves are merged in LDS, and the unit writes one
 // normalised partial (o, m, l) per query head. A sequence that needs one
 // partition writes its output directly; otherwise the merge kernel combines
-// the partials. Decode moves ~4 FLOP per byte of KV, far below the
-// matrix-core ridge, so the contractions stay on the VALU.
+// the partials. Decode moves ~4 FLOP per byte of KV for groups of up to 4
+// query heads, far below the matrix-core ridge, so those contractions stay on
+// the VALU; groups of 8 over BF16 caches (about 8 FLOP per byte, enough to
+// stall the VALU) run on the matrix cores in decode_mfma_kernel below, with
+// the same plan, units and merge.
 //
 // Register layout of a 16-token tile (per wave):
 //   K: each row (token) is spread over KL lanes that each hold KCH 16-byte
