@@ -727,18 +727,24 @@ __global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(DecodeArgs
 }
 
 // ---------------------------------------------------------------------------
-// Matrix-core partition kernel for groups of 8 query heads over BF16 caches.
+// Matrix-core partition kernel for groups of 8 query heads over BF16 caches,
+// and for groups of 4 and 8 over E4M3 caches.
 //
 // With 8 query heads per KV head the VALU kernel spends 4 * 8 * d flops per
 // (token, KV head) against 4 d bytes of K and V: about 8 flops per byte,
 // enough to make it wait on its own arithmetic (about 61 % of the HBM rate at
-// d = 128). Here the contractions run on v_mfma instructions, with the G
-// heads as the 16 columns of a 16 x 16 product (8 of them padding):
+// d = 128). An E4M3 cache halves the bytes for the same arithmetic and adds
+// the code conversions, so groups of 4 hit the same wall there. Here the
+// contractions run on v_mfma instructions, with the G heads as the first G
+// of the 16 columns of a 16 x 16 product (the rest are padding):
 //   S^T[16 keys x 16] = K[16 keys x d] . Q^T[d x 16]   (16x16x32, d/32 steps)
 //     A = K rows straight from HBM: lane l reads 16 bytes of key l % 16 at
-//         dims 32 ks + 8 (l / 16) .. + 7, the A operand layout;
+//         dims 32 ks + 8 (l / 16) .. + 7, the A operand layout (E4M3: 16
+//         codes at dims 16 (l / 16 + 4 j), converted exactly to BF16 and
+//         used as k-steps 2 j and 2 j + 1);
 //     B = Q^T: lane l holds head l % 16 at the same dims (registers).
-//   O^T[16 dims x 16] += V^T[16 dims x 16 keys] . P^T[16 keys x 16]  (16x16x16)
+//   O^T[16 dims x 16] += V^T[16 dims x 16 keys] . P^T[16 keys x 16]  (16x16x16;
+//     an E4M3 V tile is converted to BF16 as it is written to LDS)
 //     B = P^T: lane l holds the weights of keys 4 (l / 16) .. + 3 for head
 //         l % 16, which is where the score product left those scores;
 //     A = V^T: the V tile goes through this wave's LDS region row-major and
@@ -749,21 +755,26 @@ __global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(DecodeArgs
 // The weights enter PV as BF16 hi + lo terms (16 significant bits), as in
 // the prefill kernel, and the running sum uses the same split values. The
 // plan, the work units, the persistent loop, the partials and the merge
-// kernel are those of the VALU kernel.
-template <int D, int NW>
+// kernel are those of the VALU kernel. The per-head E4M3 scales fold into
+// the score scale (K) and the output normalisation (V).
+template <typename T, int D, int G, int NW>
 __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeArgs a) {
-  constexpr int G = 8;
+  constexpr bool kFp8 = std::is_same<T, FP8>::value;
+  static_assert(kFp8 || std::is_same<T, BF16>::value, "BF16 or E4M3 caches");
+  static_assert(G <= 16, "heads are columns of a 16-wide product");
   constexpr int kWaves = NW;
   constexpr int kThreads = NW * kWave;
-  constexpr int DCH = D / 8;                   // 16-byte chunks per row
+  constexpr int DCH = D / 8;                   // 16-byte BF16 chunks per row
+  constexpr int CCH = D * T::kBytes / 16;      // 16-byte chunks per cache row
   constexpr int KSTEPS = D / 32;               // k-steps of the score product
+  constexpr int KLD = kFp8 ? KSTEPS / 2 : KSTEPS;  // K loads per lane per tile
   constexpr int DT = D / 16;                   // 16-dim tiles of the output
   constexpr int SWZ = (DCH < 16 ? DCH : 16) - 1;
-  constexpr int VPL = kTile * DCH / kWave;     // V chunks per lane per tile
-  static_assert(VPL >= 1 && kTile * DCH % kWave == 0, "V tile shape");
+  constexpr int VPL = kTile * CCH / kWave;     // V cache chunks per lane per tile
+  static_assert(VPL >= 1 && kTile * CCH % kWave == 0 && KLD >= 1, "tile shape");
   // a wave's V tile (kTile rows of D bf16) and its share of the final merge
   // (G heads of D floats) are both 32 D bytes; the merge reuses the region
-  static_assert(kTile * DCH * 16 == G * D * 4, "V tile and merge share a region");
+  static_assert(kTile * DCH * 16 >= G * D * 4, "the merge fits the V region");
 
   __shared__ PlanLds s_plan;
   __shared__ int s_bt[kMaxPartBlocks];
@@ -794,20 +805,29 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeArgs a) {
   const int end = min(start + P, n);
   const int nparts = (n + P - 1) / P;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int lane = tid % kWave;
+  int lane = tid % kWave;
+  // E4M3: the lane's address offsets are recomputed in each unit rather than
+  // held across the whole kernel (28 VGPRs, which kept d = 256 above the 256
+  // of an 8-wave workgroup)
+  if constexpr (kFp8) asm volatile("" : "+v"(lane));
   const int col = lane % 16, grp = lane / 16;
 
   // Q^T operand: head col of the group (zero for the padding columns)
+  // (k-step ks covers BF16 chunk 4 ks + grp; for E4M3, k-steps 2 j + h cover
+  // chunk 2 (grp + 4 j) + h, the dims of the lane's 16 codes)
   bf16x8_t qop[KSTEPS];
   {
     const uint4* qb = reinterpret_cast<const uint4*>(a.query) +
                       ((int64_t)seq * a.num_q_heads + (int64_t)kvh * G + (col < G ? col : 0)) * DCH;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      const uint4 v = qb[4 * ks + grp];
+      const int chunk = kFp8 ? 2 * (grp + 4 * (ks / 2)) + ks % 2 : 4 * ks + grp;
+      const uint4 v = qb[chunk];
       qop[ks] = __builtin_bit_cast(bf16x8_t, col < G ? v : make_uint4(0, 0, 0, 0));
     }
   }
+  const float score_scale = kFp8 ? a.scale_log2 * a.k_scale[kvh] : a.scale_log2;
+  const float out_scale = kFp8 ? a.v_scale[kvh] : 1.f;
 
   const int blk0 = start >> bs_log2;
   const int nblk = ((end - start) + bs - 1) >> bs_log2;
@@ -819,8 +839,8 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeArgs a) {
 
   const uint4* kcache = reinterpret_cast<const uint4*>(a.key_cache);
   const uint4* vcache = reinterpret_cast<const uint4*>(a.value_cache);
-  const int64_t block_stride = (int64_t)a.num_kv_heads * bs * DCH;  // 16-byte chunks
-  const int64_t head_off = (int64_t)kvh * bs * DCH;
+  const int64_t block_stride = (int64_t)a.num_kv_heads * bs * CCH;  // 16-byte chunks
+  const int64_t head_off = (int64_t)kvh * bs * CCH;
   const int ntiles = (end - start + kTile - 1) / kTile;
   uint4* vt = s_region[wave];
 
@@ -829,7 +849,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeArgs a) {
   };
   auto tile_offset = [&](int t, int blk) -> int64_t {
     return (int64_t)(blk < 0 ? 0 : blk) * block_stride + head_off +
-           (int64_t)((start + t * kTile) & (bs - 1)) * DCH;
+           (int64_t)((start + t * kTile) & (bs - 1)) * CCH;
   };
 
   f32x4_t acc[DT];
@@ -839,15 +859,18 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeArgs a) {
   float l_part = 0.f;       // sum of this lane's own weights
 
   // K operand and V chunks of a tile, one tile ahead of the arithmetic
-  uint4 kop[KSTEPS];
+  uint4 kop[KLD];
   uint4 vreg[VPL];
-  auto load_tile = [&](int64_t off) {
+  auto load_k = [&](int64_t off) {
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) kop[ks] = load_stream(kcache + off + col * DCH + 4 * ks + grp);
+    for (int j = 0; j < KLD; ++j)
+      kop[j] = load_stream(kcache + off + col * CCH + (kFp8 ? grp + 4 * j : 4 * j + grp));
+  };
+  auto load_v = [&](int64_t off) {
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
       const int idx = lane + kWave * i;
-      vreg[i] = load_stream(vcache + off + (idx / DCH) * DCH + idx % DCH);
+      vreg[i] = load_stream(vcache + off + (idx / CCH) * CCH + idx % CCH);
     }
   };
 
@@ -862,26 +885,47 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
       const int idx = lane + kWave * i;
-      const int r = idx / DCH, c = idx % DCH;
+      const int r = idx / CCH, c = idx % CCH;
       const uint4 v = (valid && tok0 + r < n) ? vreg[i] : make_uint4(0, 0, 0, 0);
-      vt[r * DCH + (c ^ (r & SWZ))] = v;
+      if constexpr (kFp8) {  // 16 codes -> BF16 chunks 2c, 2c + 1 (exact), one chunk at a time
+        uint4 w[2];
+        k_as_query(FP8{}, v, w);
+        vt[r * DCH + ((2 * c) ^ (r & SWZ))] = w[0];
+        vt[r * DCH + ((2 * c + 1) ^ (r & SWZ))] = w[1];
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        vt[r * DCH + (c ^ (r & SWZ))] = v;
+      }
     }
 
     // scores of keys tok0 + 4 grp + i for head col
     f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop[ks]), qop[ks], sc,
-                                                  0, 0, 0);
+    for (int j = 0; j < KLD; ++j) {
+      if constexpr (kFp8) {
+        uint4 kq[2];
+        k_as_query(FP8{}, kop[j], kq);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kq[0]),
+                                                    qop[2 * j], sc, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kq[1]),
+                                                    qop[2 * j + 1], sc, 0, 0, 0);
+      } else {
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop[j]), qop[j],
+                                                    sc, 0, 0, 0);
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (kPrefetch) load_tile(off_next);
+    if constexpr (kPrefetch) {
+      load_k(off_next);
+      load_v(off_next);
+    }
     __builtin_amdgcn_sched_barrier(0);
 
     float sv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tok = tok0 + 4 * grp + i;
-      sv[i] = (valid && tok < n) ? sc[i] * a.scale_log2 : -INFINITY;
+      sv[i] = (valid && tok < n) ? sc[i] * score_scale : -INFINITY;
     }
     // online softmax per head: the column's 16 scores sit in lanes col,
     // col + 16, col + 32, col + 48 (4 each)
@@ -927,7 +971,8 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeArgs a) {
   int t = wave;
   if (t < ntiles) {
     int blk = tile_block(t);
-    load_tile(tile_offset(t, blk));
+    load_k(tile_offset(t, blk));
+    load_v(tile_offset(t, blk));
     for (; t + kWaves < ntiles; t += kWaves) {
       const int blk_next = tile_block(t + kWaves);
       process(t, blk, tile_offset(t + kWaves, blk_next), std::true_type{});
@@ -966,7 +1011,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeArgs a) {
       const float4 x = reinterpret_cast<const float4*>(s_region[w])[g * (D / 4) + d4];
       o.x += sw * x.x; o.y += sw * x.y; o.z += sw * x.z; o.w += sw * x.w;
     }
-    const float inv = 1.f / L;
+    const float inv = out_scale / L;
     o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
     const int64_t head = (int64_t)seq * a.num_q_heads + (int64_t)kvh * G + g;
     if (nparts == 1) {
@@ -1176,12 +1221,16 @@ static hipError_t launch_nw(const DecodeArgs& a, hipStream_t stream) {
 
 template <typename T, int D, int G>
 static hipError_t launch_t(const DecodeArgs& a, int waves, hipStream_t stream) {
-  if constexpr (G == 8 && std::is_same<T, BF16>::value) {
-    // groups of 8 query heads over BF16 caches run on the matrix cores; at
-    // d = 256 the operands and accumulators need more than the 256 VGPRs of
-    // 8-wave workgroups, so those use 4 waves
-    if constexpr (D > 128) return launch_kernel<D, 2, 4, decode_mfma_kernel<D, 4>>(a, stream);
-    else return launch_kernel<D, 2, 8, decode_mfma_kernel<D, 8>>(a, stream);
+  // Groups of 8 query heads over BF16 caches, and groups of 8 (and of 4 at
+  // d >= 128) over E4M3 caches, run on the matrix cores (their VALU forms
+  // wait on their own arithmetic). BF16 at d = 256 exceeds the 256 VGPRs of
+  // an 8-wave workgroup and uses 4 waves.
+  constexpr bool kFp8 = std::is_same<T, FP8>::value;
+  constexpr bool kMfma = (std::is_same<T, BF16>::value && G == 8) ||
+                         (kFp8 && (G == 8 || (G == 4 && D >= 128)));
+  if constexpr (kMfma) {
+    constexpr int kNw = (!kFp8 && D > 128) ? 4 : 8;
+    return launch_kernel<D, 2, kNw, decode_mfma_kernel<T, D, G, kNw>>(a, stream);
   } else {
     // 8-wave workgroups are limited to 256 VGPRs per lane; the d = 256 shapes
     // with 8 query heads per KV head or float32 data, float32 at d = 128 with
