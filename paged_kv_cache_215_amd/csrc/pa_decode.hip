@@ -23,7 +23,9 @@
 // query heads, far below the matrix-core ridge, so those contractions stay on
 // the VALU; groups of 8 over BF16 caches (about 8 FLOP per byte, enough to
 // stall the VALU) run on the matrix cores in decode_mfma_kernel below, with
-// the same plan, units and merge.
+// the same plan, units and merge. E4M3 caches, whose codes must be converted
+// before any arithmetic, take the matrix cores for groups of 8 and for groups
+// of 4 at d >= 128 as well.
 //
 // Register layout of a 16-token tile (per wave):
 //   K: each row (token) is spread over KL lanes that each hold KCH 16-byte
