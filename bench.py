@@ -46,6 +46,15 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def decode_kernel_name(fp8, group, head_dim, f32=False):
+    """The partition kernel pa_decode launches for a shape: groups of 8 query
+    heads over BF16 caches, and groups of 8 (and of 4 at d >= 128) over E4M3
+    caches, run on the matrix cores; every other shape on the VALU kernel."""
+    if not f32 and (group == 8 or (fp8 and group == 4 and head_dim >= 128)):
+        return "decode_mfma_kernel"
+    return "decode_partition_kernel"
+
+
 def decode_bytes(layout, num_decode, num_q_heads, num_kv_heads, head_dim, elem_bytes,
                  unique_blocks=False, kv_bytes=None):
     """Algorithmic bytes of one pa_decode call: K+V rows of every attended
@@ -314,7 +323,8 @@ def run(args):
         },
         "roofline": {
             "kernel": ("pa_decode_fp8" if fp8 else "pa_decode") +
-                      " (decode_partition_kernel + decode_merge_kernel)",
+                      f" ({decode_kernel_name(fp8, case.num_q_heads // case.num_kv_heads, case.head_dim, elem == 4)}"
+                      " + decode_merge_kernel)",
             "bound": "hbm",
             "achieved": round(achieved_gbs, 1),
             "peak": HBM_PEAK_GBS,

@@ -62,3 +62,13 @@ def test_source_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
     assert bench.source_hash(["k.hip"]) == h0
     src.write_text("int f(int x) { return x + 2; }\n")
     assert bench.source_hash(["k.hip"]) != h0
+
+
+def test_kernel_names_match_the_committed_kernel_traces():
+    # the kernel bench.py names in its roofline entry is the one the committed
+    # rocprofv3 summaries of the same workloads list first
+    for fp8, trace in ((False, "decode_c3_kernel_trace.md"), (True, "decode_fp8_c3_kernel_trace.md")):
+        name = bench.decode_kernel_name(fp8, 16 // 4, 256)
+        text = open(os.path.join(ROOT, "profiles", trace)).read()
+        first = [ln for ln in text.splitlines() if ln.startswith("| `pa::")][0]
+        assert f"pa::{name}<" in first, (trace, first)
