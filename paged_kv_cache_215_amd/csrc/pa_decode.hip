@@ -250,18 +250,24 @@ __device__ __forceinline__ int wave_scan(int x) {
   return x;
 }
 
+constexpr int kTailClasses = 16;  // size classes of the last partitions (P / 16 tokens each)
+
 struct PlanLds {
   int lens[kPlanSeqs];        // clamped context lengths
   int full_pre[kPlanSeqs];    // exclusive prefix of full-partition counts
+  unsigned short tail_order[kPlanSeqs];  // sequences by the size of their last partition
+  int cls_cnt[8][kTailClasses];          // per wave: last partitions of each size class
   long long red_sum[16];
   int red_a[16], red_b[16];
   int part_tokens, full_total, max_nparts;
+  int ranked;                 // tail_order holds the order (else: sequence order)
   int ticket;                 // this workgroup's current unit
 };
 
 // Fills the plan for the whole workgroup (NW waves); ends with a barrier.
 template <int NW>
 __device__ void build_plan(const DecodeArgs& a, PlanLds& pl) {
+  static_assert(NW <= 8 && kPlanSeqs <= 65536, "plan storage");
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int S = a.num_seqs;
   constexpr int kT = NW * kWave;
@@ -306,6 +312,7 @@ __device__ void build_plan(const DecodeArgs& a, PlanLds& pl) {
           if (p <= budget) P = p;
       }
       pl.part_tokens = P;
+      pl.ranked = mn != mx;  // equal lengths: equal last partitions, already in order
     }
   }
   __syncthreads();
@@ -338,13 +345,71 @@ __device__ void build_plan(const DecodeArgs& a, PlanLds& pl) {
     pl.full_pre[b] = run;
     run += max(1, (pl.lens[b] + P - 1) / P) - 1;
   }
+
+  // Order of the last partitions, which the ticket counter hands out: the
+  // longest first, so that the shortest ones fill the gaps at the end (longest
+  // processing time first). Lengths go into kTailClasses classes of P / 16
+  // tokens; within a class the order is the sequence order, so every
+  // workgroup derives the same permutation. Wave w ranks the sequences of
+  // its own contiguous range with ballots. A batch of equal lengths keeps the
+  // sequence order and skips this.
+  if (!pl.ranked) {
+    __syncthreads();
+    return;
+  }
+  const int per_wave = (S + NW - 1) / NW;
+  const int w0 = min(S, wave * per_wave), w1 = min(S, w0 + per_wave);
+  auto tail_class = [&](int b) {
+    const int n = pl.lens[b];
+    const int tail = n - (max(1, (n + P - 1) / P) - 1) * P;
+    return tail <= 0 ? 0 : (tail - 1) * kTailClasses / P;
+  };
+  int cnt = 0;  // lane k < kTailClasses: sequences of class k in this wave's range
+  for (int c0 = w0; c0 < w1; c0 += kWave) {
+    const int b = c0 + lane;
+    const int c = b < w1 ? tail_class(b) : -1;
+#pragma unroll
+    for (int k = 0; k < kTailClasses; ++k) {
+      const int m = __builtin_popcountll(__builtin_amdgcn_ballot_w64(c == k));
+      if (lane == k) cnt += m;
+    }
+  }
+  if (lane < kTailClasses) pl.cls_cnt[wave][lane] = cnt;
+  __syncthreads();
+  {  // lane k < kTailClasses: first position of (class k, this wave)
+    int total = 0, earlier = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int x = lane < kTailClasses ? pl.cls_cnt[w][lane] : 0;
+      total += x;
+      earlier += w < wave ? x : 0;
+    }
+    const int incl_cls = wave_scan(total);  // classes 0..k
+    const int all = __builtin_amdgcn_readlane(incl_cls, kTailClasses - 1);
+    cnt = all - incl_cls + earlier;  // larger classes, then this class in earlier waves
+  }
+  for (int c0 = w0; c0 < w1; c0 += kWave) {
+    const int b = c0 + lane;
+    const int c = b < w1 ? tail_class(b) : -1;
+    int pos = 0;
+#pragma unroll
+    for (int k = 0; k < kTailClasses; ++k) {
+      const unsigned long long m = __builtin_amdgcn_ballot_w64(c == k);
+      const int next = __builtin_amdgcn_readlane(cnt, k);
+      const int below = __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+      if (c == k) pos = next + below;
+      if (lane == k) cnt += __builtin_popcountll(m);
+    }
+    if (b < w1) pl.tail_order[pos] = (unsigned short)b;
+  }
   __syncthreads();
 }
 
 // Unit e of the plan -> (sequence, partition).
 __device__ __forceinline__ int2 plan_unit(const PlanLds& pl, int S, int e) {
   if (e >= pl.full_total) {
-    const int b = e - pl.full_total;
+    const int b = pl.ranked ? pl.tail_order[e - pl.full_total] : e - pl.full_total;
     const int P = pl.part_tokens;
     return make_int2(b, max(1, (pl.lens[b] + P - 1) / P) - 1);
   }

@@ -216,6 +216,18 @@ def test_large_batch_spans_several_launches():
     assert err <= ATOL
 
 
+@pytest.mark.parametrize("group", [4, 8])
+def test_ragged_batch_every_sequence(group):
+    # 1500 ragged sequences (empty ones included): each wave of the plan ranks
+    # several 64-sequence chunks when it orders the last partitions, longest
+    # first, for the ticket counter; every output row is checked, so a unit
+    # handed out twice or never shows up
+    lens = np.random.default_rng(25).integers(0, 700, size=1500)
+    case = make_case(name=f"ragged_1500_g{group}", seed=25 + group, context_lens=lens,
+                     num_q_heads=2 * group, num_kv_heads=2, head_dim=64, block_size=16, device=DEV)
+    _check(case)
+
+
 @pytest.mark.parametrize("kv_fp8", [False, True])
 def test_very_long_contexts(kv_fp8):
     # contexts far past one partition's staged block table (up to 128K
