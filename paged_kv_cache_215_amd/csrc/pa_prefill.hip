@@ -38,13 +38,12 @@ namespace pa {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kKeyTile = 32;      // keys per staged tile
-constexpr int kVtStride = 40;     // bf16 per V^T row in LDS (32 keys + 8 pad: 80-byte rows)
-
-// LDS column of key k (0..31) in a V^T row: keys 4q..4q+3 -> 8q..8q+3,
+// LDS column of key k of a tile in a V^T row. Each 32-key step of the PV
+// product keeps its own 32 columns, in which keys 4q..4q+3 -> 8q..8q+3 and
 // keys 16+4q..16+4q+3 -> 8q+4..8q+7.
 __device__ __forceinline__ int vt_slot(int k) {
-  return (k < 16) ? (8 * (k >> 2) + (k & 3)) : (8 * ((k - 16) >> 2) + 4 + (k & 3));
+  const int j = k & 31;
+  return (k & ~31) + ((j < 16) ? (8 * (j >> 2) + (j & 3)) : (8 * ((j - 16) >> 2) + 4 + (j & 3)));
 }
 
 __device__ __forceinline__ uint32_t pack_lo(uint32_t x, uint32_t y) {
@@ -58,8 +57,9 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
   return (uint32_t)__builtin_bit_cast(unsigned short, static_cast<__bf16>(f));
 }
 
-template <int D, int G, int HPW, int MW>
+template <int D, int G, int HPW, int MW, int KT>
 struct PrefillShape {
+  static_assert(KT == 32 || KT == 64, "key tile");
   static constexpr int HG = G / HPW;              // head groups (waves across heads)
   static constexpr int NW = HG >= MW ? HG : MW;   // waves per workgroup (at least MW)
   static constexpr int RT = NW / HG;              // 16-row sub-tiles per workgroup
@@ -69,21 +69,26 @@ struct PrefillShape {
   static constexpr int SWZ = (DCH < 16 ? DCH : 16) - 1;  // K chunk swizzle mask
   static constexpr int KSTEPS = D / 32;           // MFMA k-steps of QK^T
   static constexpr int DTILES = D / 16;           // 16-row tiles of O^T
-  static constexpr int KCHUNKS = kKeyTile * DCH;  // K chunks per tile
-  static constexpr int VJOBS = (kKeyTile / 4) * (D / 8);  // 4-key x 8-dim V jobs
+  static constexpr int QB = KT / 16;              // 16-key row blocks of S^T per tile
+  static constexpr int PSTEPS = KT / 32;          // 32-key k-steps of PV per tile
+  static constexpr int VT_STRIDE = KT + 8;        // bf16 per V^T row in LDS (8 pad)
+  static constexpr int KCHUNKS = KT * DCH;        // K chunks per tile
+  static constexpr int VJOBS = (KT / 4) * (D / 8);  // 4-key x 8-dim V jobs
   // K staging: TPR threads per key row, each loading KPT chunks of that row
-  static constexpr int TPR = (NT / kKeyTile) < DCH ? (NT / kKeyTile) : DCH;
+  static constexpr int TPR = (NT / KT) < DCH ? (NT / KT) : DCH;
   static constexpr int KPT = DCH / TPR;
   static constexpr int VPT = (VJOBS + NT - 1) / NT;       // V jobs per thread
 };
 
 constexpr int kPfMaxBlocks = 1024;  // table entries one context split may span
 
-template <int D, int G, int HPW, int MW>
-__global__ __launch_bounds__((PrefillShape<D, G, HPW, MW>::NT))
+template <int D, int G, int HPW, int MW, int KT>
+__global__ __launch_bounds__((PrefillShape<D, G, HPW, MW, KT>::NT))
 __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
-  using S = PrefillShape<D, G, HPW, MW>;
+  using S = PrefillShape<D, G, HPW, MW, KT>;
   constexpr int DCH = S::DCH;
+  constexpr int kKeyTile = KT;
+  constexpr int kVtStride = S::VT_STRIDE;
   __shared__ uint4 k_lds[2][kKeyTile * DCH];                          // swizzled K rows
   __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][D * kVtStride];  // V^T
   __shared__ int s_bt[kPfMaxBlocks];
@@ -268,13 +273,12 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
     const int buf = (kt - kt_begin) & 1;
     const bool has_next = kt + 1 < kt_end;
 
-    // ---- S^T = K Q^T for keys key0..key0+31 (two 16-key halves), per head
-    f32x4_t s0[HPW], s1[HPW];
+    // ---- S^T = K Q^T for keys key0..key0+KT-1 (16-key row blocks), per head
+    f32x4_t sc[HPW][S::QB];
 #pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) {
-      s0[hh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      s1[hh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+      for (int qb = 0; qb < S::QB; ++qb) sc[hh][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     // Waves raise their priority while they issue matrix products: of the
     // two waves sharing a SIMD, the one that reaches its products first
     // keeps the matrix unit while the other runs its softmax.
@@ -282,14 +286,13 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int ks = 0; ks < S::KSTEPS; ++ks) {
       const int c = 4 * ks + lq;
-      const bf16x8_t k0 =
-          __builtin_bit_cast(bf16x8_t, k_lds[buf][lrow * DCH + (c ^ (lrow & S::SWZ))]);
-      const bf16x8_t k1 =
-          __builtin_bit_cast(bf16x8_t, k_lds[buf][(16 + lrow) * DCH + (c ^ ((16 + lrow) & S::SWZ))]);
 #pragma unroll
-      for (int hh = 0; hh < HPW; ++hh) {
-        s0[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qop[hh][ks], s0[hh], 0, 0, 0);
-        s1[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qop[hh][ks], s1[hh], 0, 0, 0);
+      for (int qb = 0; qb < S::QB; ++qb) {
+        const int kr = 16 * qb + lrow;
+        const bf16x8_t kop = __builtin_bit_cast(bf16x8_t, k_lds[buf][kr * DCH + (c ^ (kr & S::SWZ))]);
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh)
+          sc[hh][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[hh][ks], sc[hh][qb], 0, 0, 0);
       }
     }
 
@@ -301,29 +304,29 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
 
     const int limit = base_pos + my_row;  // last key this row may see
     const bool diag = key0 + kKeyTile - 1 > base_pos + r0 || key0 + kKeyTile > n;
-    bf16x8_t pop_hi[HPW], pop_lo[HPW];
+    bf16x8_t pop_hi[HPW][S::PSTEPS], pop_lo[HPW][S::PSTEPS];
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
-      // ---- scale and causal / context mask (lane: keys 4lq+i and 16+4lq+i)
-      float sv[8];
+      // ---- scale and causal / context mask (lane: keys 16qb + 4lq + i)
+      float sv[4 * S::QB];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sv[i] = s0[hh][i] * a.scale_log2;
-        sv[4 + i] = s1[hh][i] * a.scale_log2;
-      }
+      for (int qb = 0; qb < S::QB; ++qb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[4 * qb + i] = sc[hh][qb][i] * a.scale_log2;
       if (diag) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int ka = key0 + 4 * lq + i, kb = key0 + 16 + 4 * lq + i;
-          sv[i] = (ka <= limit && ka < n) ? sv[i] : -INFINITY;
-          sv[4 + i] = (kb <= limit && kb < n) ? sv[4 + i] : -INFINITY;
-        }
+        for (int qb = 0; qb < S::QB; ++qb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int k = key0 + 16 * qb + 4 * lq + i;
+            sv[4 * qb + i] = (k <= limit && k < n) ? sv[4 * qb + i] : -INFINITY;
+          }
       }
 
       // ---- online softmax over this lane's query row
       float mx = sv[0];
 #pragma unroll
-      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+      for (int i = 1; i < 4 * S::QB; ++i) mx = fmaxf(mx, sv[i]);
       mx = pair_max<16>(mx);
       mx = pair_max<32>(mx);
       // Rescale only when some row's maximum grew by more than 2^8: the
@@ -342,39 +345,47 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
       // p_lo = RNE(p - p_hi)): 16 significant bits instead of 8, so the PV
       // product on the BF16 matrix cores keeps the weights' float32 accuracy
       // to about 2^-17 relative. The running sum uses the same p_hi + p_lo.
+      // PV step j takes the weights of row blocks 2j and 2j + 1.
       const float moff = m_run[hh] == -INFINITY ? 0.f : m_run[hh];
-      uint32_t ph[8], pl[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float pf = fast_exp2(sv[i] - moff);
-        ph[i] = bf16_bits_rne(pf);
-        const float hi = __uint_as_float(ph[i] << 16);
-        pl[i] = bf16_bits_rne(pf - hi);
-        l_part[hh] += hi + __uint_as_float(pl[i] << 16);
+      for (int j = 0; j < S::PSTEPS; ++j) {
+        uint32_t ph[8], pl[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float pf = fast_exp2(sv[8 * j + i] - moff);
+          ph[i] = bf16_bits_rne(pf);
+          const float hi = __uint_as_float(ph[i] << 16);
+          pl[i] = bf16_bits_rne(pf - hi);
+          l_part[hh] += hi + __uint_as_float(pl[i] << 16);
+        }
+        uint4 wh, wl;
+        wh.x = ph[0] | (ph[1] << 16);
+        wh.y = ph[2] | (ph[3] << 16);
+        wh.z = ph[4] | (ph[5] << 16);
+        wh.w = ph[6] | (ph[7] << 16);
+        wl.x = pl[0] | (pl[1] << 16);
+        wl.y = pl[2] | (pl[3] << 16);
+        wl.z = pl[4] | (pl[5] << 16);
+        wl.w = pl[6] | (pl[7] << 16);
+        pop_hi[hh][j] = __builtin_bit_cast(bf16x8_t, wh);
+        pop_lo[hh][j] = __builtin_bit_cast(bf16x8_t, wl);
       }
-      uint4 wh, wl;
-      wh.x = ph[0] | (ph[1] << 16);
-      wh.y = ph[2] | (ph[3] << 16);
-      wh.z = ph[4] | (ph[5] << 16);
-      wh.w = ph[6] | (ph[7] << 16);
-      wl.x = pl[0] | (pl[1] << 16);
-      wl.y = pl[2] | (pl[3] << 16);
-      wl.z = pl[4] | (pl[5] << 16);
-      wl.w = pl[6] | (pl[7] << 16);
-      pop_hi[hh] = __builtin_bit_cast(bf16x8_t, wh);
-      pop_lo[hh] = __builtin_bit_cast(bf16x8_t, wl);
     }
 
     // ---- O^T += V^T (P_hi + P_lo)^T, one V^T operand read for all heads
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int dt = 0; dt < S::DTILES; ++dt) {
-      const bf16x8_t vop = __builtin_bit_cast(
-          bf16x8_t, *reinterpret_cast<const uint4*>(&vt_lds[buf][(16 * dt + lrow) * kVtStride + 8 * lq]));
 #pragma unroll
-      for (int hh = 0; hh < HPW; ++hh) {
-        acc[hh][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_hi[hh], acc[hh][dt], 0, 0, 0);
-        acc[hh][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_lo[hh], acc[hh][dt], 0, 0, 0);
+      for (int j = 0; j < S::PSTEPS; ++j) {
+        const bf16x8_t vop = __builtin_bit_cast(
+            bf16x8_t,
+            *reinterpret_cast<const uint4*>(&vt_lds[buf][(16 * dt + lrow) * kVtStride + 32 * j + 8 * lq]));
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) {
+          acc[hh][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_hi[hh][j], acc[hh][dt], 0, 0, 0);
+          acc[hh][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_lo[hh][j], acc[hh][dt], 0, 0, 0);
+        }
       }
     }
     __builtin_amdgcn_s_setprio(0);
@@ -487,12 +498,28 @@ int prefill_rows_per_workgroup(int group, int head_dim) {
   return 16 * (nw / hg);
 }
 
+// Keys per staged tile: 64 for 8-wave workgroups of at most 2 heads per
+// wave (the per-tile barrier, softmax reductions and staging then serve twice
+// the matrix work), else 32: 4-wave workgroups would double their staging
+// registers, and 4 heads per wave would spill. The environment override
+// exists for tuning sweeps only.
+int prefill_key_tile(int group, int head_dim) {
+  static const int v = [] {
+    const char* s = std::getenv("PA_PREFILL_KEYTILE");
+    const int x = s ? std::atoi(s) : 0;
+    return x == 32 || x == 64 ? x : 0;
+  }();
+  if (prefill_min_waves(group) != 8 || prefill_group_heads_per_wave(group, head_dim) > 2) return 32;
+  return v ? v : 64;
+}
+
 int prefill_kv_splits(int num_seqs, int max_q_len, int num_q_heads, int num_kv_heads,
                       int head_dim, int max_context_len) {
   // Split the keys of each row tile until the launch has about 2048 waves
   // (two per SIMD on 256 CUs), keeping at least 8 key tiles per split.
   const int group = num_q_heads / num_kv_heads;
   const int rows = prefill_rows_per_workgroup(group, head_dim);
+  const int kt = prefill_key_tile(group, head_dim);
   const int64_t wgs = (int64_t)num_seqs * num_kv_heads * ((max_q_len + rows - 1) / rows);
   const int waves = (rows / 16) * (group / prefill_group_heads_per_wave(group, head_dim));
   static const int env_target = [] {
@@ -502,19 +529,18 @@ int prefill_kv_splits(int num_seqs, int max_q_len, int num_q_heads, int num_kv_h
   }();
   const int target = env_target ? env_target : 2048 / waves;
   int splits = 1;
-  while (splits < 8 && wgs * splits < target &&
-         (max_context_len / kKeyTile) / (2 * splits) >= 8)
+  while (splits < 8 && wgs * splits < target && (max_context_len / 32) / (2 * splits) >= 8)
     splits *= 2;
-  // each split's keys must fit the staged table: a split spans at most
-  // max_context_len / splits + 64 keys (tile rounding), i.e. at most
-  // (kPfMaxBlocks - 8) * 16 + 64 keys, which touch at most kPfMaxBlocks - 2
-  // blocks of 16 tokens
-  const int64_t span = (int64_t)(kPfMaxBlocks - 8) * 16;
+  // Each split's keys must fit the staged table. A split holds at most
+  // ceil(ntiles / splits) tiles of kt keys, starting on a tile boundary: at
+  // most max_context_len / splits + 2 * kt keys, i.e. at most
+  // max_context_len / (16 * splits) + 2 * kt / 16 + 1 blocks of 16 tokens.
+  const int64_t span = (int64_t)(kPfMaxBlocks - 2 * kt / 16 - 2) * 16;
   while ((int64_t)splits * span < max_context_len) ++splits;
   return splits;
 }
 
-template <int D, int G, int HPW, int MW>
+template <int D, int G, int HPW, int MW, int KT>
 static hipError_t launch_pf(const PrefillArgs& a_in, hipStream_t stream) {
   static const int remap = [] {
     const char* s = std::getenv("PA_PREFILL_XCD");
@@ -522,9 +548,9 @@ static hipError_t launch_pf(const PrefillArgs& a_in, hipStream_t stream) {
   }();
   PrefillArgs a = a_in;
   a.xcd_remap = remap;
-  using S = PrefillShape<D, G, HPW, MW>;
+  using S = PrefillShape<D, G, HPW, MW, KT>;
   dim3 grid((a.max_q_len + S::ROWS - 1) / S::ROWS, a.num_kv_heads, a.num_seqs * a.kv_splits);
-  hipLaunchKernelGGL((prefill_kernel<D, G, HPW, MW>), grid, dim3(S::NT), 0, stream, a);
+  hipLaunchKernelGGL((prefill_kernel<D, G, HPW, MW, KT>), grid, dim3(S::NT), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.kv_splits == 1) return err;
   hipLaunchKernelGGL((prefill_merge_kernel<D>), dim3(a.num_q_heads, a.total_q), dim3(kWave), 0,
@@ -532,16 +558,24 @@ static hipError_t launch_pf(const PrefillArgs& a_in, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D, int G, int HPW, int MW>
+static hipError_t launch_pk(const PrefillArgs& a, hipStream_t stream) {
+  if constexpr (MW == 8 && HPW <= 2) {
+    if (prefill_key_tile(G, D) == 64) return launch_pf<D, G, HPW, MW, 64>(a, stream);
+  }
+  return launch_pf<D, G, HPW, MW, 32>(a, stream);
+}
+
 template <int D, int G, int MW>
 static hipError_t launch_ph(const PrefillArgs& a, hipStream_t stream) {
   const int hpw = prefill_group_heads_per_wave(G, D);
   if constexpr (G >= 4 && D <= 128 && (MW == 4 || 4 * D <= 256)) {
-    if (hpw == 4) return launch_pf<D, G, 4, MW>(a, stream);
+    if (hpw == 4) return launch_pk<D, G, 4, MW>(a, stream);
   }
   if constexpr (G >= 2 && (MW == 4 || 2 * D <= 256)) {
-    if (hpw == 2) return launch_pf<D, G, 2, MW>(a, stream);
+    if (hpw == 2) return launch_pk<D, G, 2, MW>(a, stream);
   }
-  return launch_pf<D, G, 1, MW>(a, stream);
+  return launch_pk<D, G, 1, MW>(a, stream);
 }
 
 template <int D, int G>

@@ -16,6 +16,8 @@ SETTINGS = [
     {"PA_PREFILL_HPW": "4"},
     {"PA_PREFILL_WAVES": "4", "PA_PREFILL_HPW": "2"},
     {"PA_PREFILL_WAVES": "8"},
+    {"PA_PREFILL_KEYTILE": "32"},
+    {"PA_PREFILL_WAVES": "8", "PA_PREFILL_HPW": "2", "PA_PREFILL_KEYTILE": "64"},
     {"PA_PREFILL_TARGET_WGS": "64", "PA_PREFILL_XCD": "0"},
     {"PA_PREFILL_TARGET_WGS": "4096"},
     {"PA_DECODE_WAVES": "4"},
