@@ -22,8 +22,8 @@
 // With the accumulator layout of the 16x16 MFMA (lane l holds rows
 // 4*(l/16)+i of column l%16) both S^T and O^T keep a query row in the lanes
 // l%16 == row, so the online softmax is lane-local up to a 4-lane reduction.
-// P enters the PV product as two BF16 terms (hi + lo, 16 significant bits)
-// and the running sum uses the same split weights. The B operand of PV takes
+// P enters the PV product as two BF16 terms (hi + lo, 16 significant bits);
+// the running sum takes the float32 weights. The B operand of PV takes
 // the 8 weights a lane holds for
 // keys {4q..4q+3, 16+4q..16+4q+3} (q = l/16); V^T columns are stored in that
 // same key order, so the contraction pairs every weight with its key's row.
@@ -37,6 +37,8 @@ namespace pa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // LDS column of key k of a tile in a V^T row. Each 32-key step of the PV
 // product keeps its own 32 columns, in which keys 4q..4q+3 -> 8q..8q+3 and
@@ -53,9 +55,6 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t x, uint32_t y) {
   return __builtin_amdgcn_perm(y, x, 0x07060302u);  // hi16(x) | hi16(y) << 16
 }
 
-__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
-  return (uint32_t)__builtin_bit_cast(unsigned short, static_cast<__bf16>(f));
-}
 
 template <int D, int G, int HPW, int MW, int KT>
 struct PrefillShape {
@@ -126,15 +125,21 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
   const int my_row = r0 + rsub * 16 + lrow;          // chunk row of this lane's query
   const int qrow = my_row < L ? my_row : L - 1;       // clamp padding rows (not written)
 
-  // Q^T operands: query row my_row, dims 32*ks + 8*lq .. +8, per head
+  // Q^T operands: query row my_row, dims 32*ks + 8*lq .. +8, per head. The
+  // scores are scaled inside the exponent by c = |scale * log2(e)|; for a
+  // negative scale the query's sign bits are flipped instead (exact), and a
+  // zero scale becomes the smallest normal float, whose products with finite
+  // scores round the weights to exactly 1, as the zero scale would.
+  const uint32_t qflip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+  const float c_exp = fmaxf(fabsf(a.scale_log2), 1.17549435e-38f);
   bf16x8_t qop[HPW][S::KSTEPS];
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
-    const uint4* qp = reinterpret_cast<const uint4*>(a.query) +
-                      ((int64_t)(q0 + qrow) * a.num_q_heads + head0 + hh) * DCH;
+    const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(a.query) +
+                        ((int64_t)(q0 + qrow) * a.num_q_heads + head0 + hh) * DCH;
 #pragma unroll
     for (int ks = 0; ks < S::KSTEPS; ++ks)
-      qop[hh][ks] = __builtin_bit_cast(bf16x8_t, qp[4 * ks + lq]);
+      qop[hh][ks] = __builtin_bit_cast(bf16x8_t, qp[4 * ks + lq] ^ qflip);
   }
 
   // Key range of this split: keys visible to some row of the workgroup.
@@ -307,12 +312,12 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
     bf16x8_t pop_hi[HPW][S::PSTEPS], pop_lo[HPW][S::PSTEPS];
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
-      // ---- scale and causal / context mask (lane: keys 16qb + 4lq + i)
+      // ---- causal / context mask on the unscaled scores (lane: keys 16qb + 4lq + i)
       float sv[4 * S::QB];
 #pragma unroll
       for (int qb = 0; qb < S::QB; ++qb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sv[4 * qb + i] = sc[hh][qb][i] * a.scale_log2;
+        for (int i = 0; i < 4; ++i) sv[4 * qb + i] = sc[hh][qb][i];
       if (diag) {
 #pragma unroll
         for (int qb = 0; qb < S::QB; ++qb)
@@ -323,12 +328,14 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
           }
       }
 
-      // ---- online softmax over this lane's query row
+      // ---- online softmax over this lane's query row, in log2 units (c_exp > 0,
+      // so the largest scaled score is c_exp times the largest score)
       float mx = sv[0];
 #pragma unroll
       for (int i = 1; i < 4 * S::QB; ++i) mx = fmaxf(mx, sv[i]);
       mx = pair_max<16>(mx);
       mx = pair_max<32>(mx);
+      mx *= c_exp;
       // Rescale only when some row's maximum grew by more than 2^8: the
       // softmax does not depend on the offset subtracted, and weights of up
       // to 2^8 are far from float32 / BF16 overflow. This keeps the rescale
@@ -344,31 +351,27 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
       // Each weight p is carried as p_hi + p_lo, both BF16 (p_hi = RNE(p),
       // p_lo = RNE(p - p_hi)): 16 significant bits instead of 8, so the PV
       // product on the BF16 matrix cores keeps the weights' float32 accuracy
-      // to about 2^-17 relative. The running sum uses the same p_hi + p_lo.
-      // PV step j takes the weights of row blocks 2j and 2j + 1.
+      // to about 2^-17 relative; the running sum takes p itself. Weights are
+      // rounded in pairs (one packed conversion per pair). PV step j takes
+      // the weights of row blocks 2j and 2j + 1.
       const float moff = m_run[hh] == -INFINITY ? 0.f : m_run[hh];
 #pragma unroll
       for (int j = 0; j < S::PSTEPS; ++j) {
-        uint32_t ph[8], pl[8];
+        uint32_t wh[4], wl[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float pf = fast_exp2(sv[8 * j + i] - moff);
-          ph[i] = bf16_bits_rne(pf);
-          const float hi = __uint_as_float(ph[i] << 16);
-          pl[i] = bf16_bits_rne(pf - hi);
-          l_part[hh] += hi + __uint_as_float(pl[i] << 16);
+        for (int i = 0; i < 4; ++i) {
+          f32x2_t pf;
+          pf.x = fast_exp2(__builtin_fmaf(sv[8 * j + 2 * i], c_exp, -moff));
+          pf.y = fast_exp2(__builtin_fmaf(sv[8 * j + 2 * i + 1], c_exp, -moff));
+          wh[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pf, bf16x2_t));
+          f32x2_t r;
+          r.x = pf.x - __uint_as_float(wh[i] << 16);
+          r.y = pf.y - __uint_as_float(wh[i] & 0xffff0000u);
+          wl[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t));
+          l_part[hh] += pf.x + pf.y;
         }
-        uint4 wh, wl;
-        wh.x = ph[0] | (ph[1] << 16);
-        wh.y = ph[2] | (ph[3] << 16);
-        wh.z = ph[4] | (ph[5] << 16);
-        wh.w = ph[6] | (ph[7] << 16);
-        wl.x = pl[0] | (pl[1] << 16);
-        wl.y = pl[2] | (pl[3] << 16);
-        wl.z = pl[4] | (pl[5] << 16);
-        wl.w = pl[6] | (pl[7] << 16);
-        pop_hi[hh][j] = __builtin_bit_cast(bf16x8_t, wh);
-        pop_lo[hh][j] = __builtin_bit_cast(bf16x8_t, wl);
+        pop_hi[hh][j] = __builtin_bit_cast(bf16x8_t, make_uint4(wh[0], wh[1], wh[2], wh[3]));
+        pop_lo[hh][j] = __builtin_bit_cast(bf16x8_t, make_uint4(wl[0], wl[1], wl[2], wl[3]));
       }
     }
 

@@ -134,3 +134,15 @@ def test_long_prefix_spans_several_splits():
     err = max_abs_err(out.cpu().numpy()[rows], oracle_prefill_rows(case, 0, rows, kb, vb))
     say(f"[prefill] 30000-token prefix: sampled max-abs err {err:.3e}")
     assert np.all(np.isfinite(out.cpu().numpy())) and err <= ATOL
+
+
+@pytest.mark.parametrize("scale", [-0.0625, 0.0, 0.3])
+@pytest.mark.parametrize("group,head_dim", [(4, 256), (2, 128)])
+def test_scale_sign_and_zero(scale, group, head_dim):
+    # the kernel scales scores inside the exponent by |scale| and flips the
+    # query's sign for a negative scale; a zero scale gives uniform weights
+    case = make_case(name=f"pf_scale_{scale}_g{group}_d{head_dim}", seed=61, context_lens=[],
+                     num_q_heads=4 * group, num_kv_heads=4, head_dim=head_dim, block_size=16,
+                     device=DEV, prefill_chunks=[(90, 70)])
+    case.scale = scale
+    _full_check(case, tag=f"scale {scale}")
