@@ -283,6 +283,25 @@ def run(args):
     decode_ms = [a.elapsed_time(b) for a, b in dec_events]
     avg_decode_s = float(np.mean(decode_ms)) / 1e3
 
+    # Cold-cache decode calls (one-layer workloads): a 1 GiB write, more than
+    # the 256 MB last-level cache holds, goes between calls, outside the events,
+    # so every call reads its K/V from HBM. The full 16-layer step needs none:
+    # each layer's 2 GiB of K/V already exceeds that cache.
+    cold_ms = []
+    if L == 1 and args.cold_calls > 0:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        for i in range(args.cold_calls):
+            flush.fill_(i & 0xFF)
+            ev = []
+            timed(ev, lambda: attend(0))
+            torch.cuda.synchronize()
+            cold_ms.append(ev[0][0].elapsed_time(ev[0][1]))
+        del flush
+
+    def pctl(ms):
+        q = np.percentile(np.asarray(ms) * 1e3, [10, 50, 90])
+        return {"p10": round(float(q[0]), 2), "p50": round(float(q[1]), 2), "p90": round(float(q[2]), 2)}
+
     unique = args.workload == "c4_grpo_cow"
     bytes_call = decode_bytes(case.layout, S, case.num_q_heads, case.num_kv_heads, case.head_dim,
                               elem, unique_blocks=unique, kv_bytes=1 if fp8 else None)
@@ -333,9 +352,25 @@ def run(args):
             "traffic": traffic,
             "algorithmic_bytes_per_call": bytes_call,
             "avg_call_us": round(avg_decode_s * 1e6, 2),
+            "call_us": pctl(decode_ms),
         },
         "cpu_baseline": None,
     }
+    if unique:
+        # shared prompt blocks counted once per reader: the rate the call would
+        # need without prefix sharing (may exceed the HBM peak)
+        logical = decode_bytes(case.layout, S, case.num_q_heads, case.num_kv_heads, case.head_dim,
+                               elem, unique_blocks=False, kv_bytes=1 if fp8 else None)
+        result["roofline"]["logical_bytes_per_call"] = logical
+        result["roofline"]["effective_logical_gbs"] = round(logical / avg_decode_s / 1e9, 1)
+    if cold_ms:
+        cold_s = float(np.median(cold_ms)) / 1e3
+        result["roofline"]["cold_cache"] = {
+            "calls": len(cold_ms), "flush_bytes": 1 << 30, "call_us": pctl(cold_ms),
+            "achieved_at_p50": round(bytes_call / cold_s / 1e9, 1),
+            "frac_at_p50": round(bytes_call / cold_s / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"[bench] cold-cache pa_decode p50 {cold_s * 1e6:.1f} us, "
+            f"{bytes_call / cold_s / 1e9:.1f} GB/s")
     if pf is not None:
         pf_s = float(np.mean([a.elapsed_time(b) for a, b in pf_events])) / 1e3
         flop = 0
@@ -690,6 +725,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cold-calls", type=int, default=20,
+                    help="one-layer workloads: extra pa_decode calls timed after a 1 GiB cache "
+                         "flush each (reported under roofline.cold_cache)")
     ap.add_argument("--workload", default="c3_full_step",
                     choices=["c2_layer_decode", "c3_full_step", "c4_grpo_cow", "c5_mixed_step"])
     ap.add_argument("--component", choices=["engine", "copy_swap"], default=None,
