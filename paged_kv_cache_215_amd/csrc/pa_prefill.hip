@@ -56,6 +56,22 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t x, uint32_t y) {
 }
 
 
+// Schedule of a run of NR operand reads from LDS, each feeding M matrix
+// products: the first kAhead reads go out together and every read after
+// them follows the products of the read kAhead before it, so kAhead reads
+// are in flight while the products run.
+constexpr int kAhead = 4;
+template <int NR, int M>
+__device__ __forceinline__ void interleave_reads() {
+  __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);  // LDS reads
+#pragma unroll
+  for (int i = 0; i < NR - kAhead; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, M, 0);     // matrix products
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, M * kAhead, 0);
+}
+
 template <int D, int G, int HPW, int MW, int KT>
 struct PrefillShape {
   static_assert(KT == 32 || KT == 64, "key tile");
@@ -300,6 +316,7 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
           sc[hh][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[hh][ks], sc[hh][qb], 0, 0, 0);
       }
     }
+    interleave_reads<S::KSTEPS * S::QB, HPW>();
 
     __builtin_amdgcn_s_setprio(0);
     // The next tile's global loads go out once the score products have been
@@ -391,6 +408,7 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
         }
       }
     }
+    interleave_reads<S::DTILES * S::PSTEPS, 2 * HPW>();
     __builtin_amdgcn_s_setprio(0);
     if (has_next) store_lds(buf ^ 1);
     __syncthreads();  // next buffer complete; this one free for reuse
