@@ -427,10 +427,15 @@ PROFILE_COMMANDS = {
              "-d <out>/kt_c3 -o kt -- python3 <repo>/bench.py --steps 5 --warmup 1 --no-cpu-baseline",
     "kt_c5": "cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats --output-format csv "
              "-d <out>/kt_c5 -o kt -- python3 <repo>/bench.py --workload c5_mixed_step "
-             "--steps 5 --warmup 1 --no-cpu-baseline",
+             "--steps 5 --warmup 1 --cold-calls 0 --no-cpu-baseline",
     "kt_c3_fp8": "cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats --output-format csv "
                  "-d <out>/kt_c3_fp8 -o kt -- python3 <repo>/bench.py --kv fp8 --steps 5 "
                  "--warmup 1 --no-cpu-baseline",
+    "pmc_prefill_c5": "rocprofv3 --pmc SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU "
+                      "SQ_ACTIVE_INST_VALU SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_ACTIVE_INST_LDS "
+                      "SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE --output-format csv -d <out>/pmc_prefill_c5 "
+                      "-o p -- python3 <repo>/bench.py --workload c5_mixed_step --steps 2 --warmup 1 "
+                      "--cold-calls 0 --no-cpu-baseline",
     "pmc_fetch_c3": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/pmc_fetch_c3 -o p -- "
                     "python3 <repo>/bench.py --steps 2 --warmup 1 --no-cpu-baseline",
     "pmc_write_c3": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/pmc_write_c3 -o p -- "
@@ -471,6 +476,53 @@ def _counter_means(folder, counter):
     return {k: (len(v), sum(v) / len(v)) for k, v in out.items()}
 
 
+SIMDS, XCDS = 256 * 4, 8   # MI355X: 256 CUs of 4 SIMDs in 8 XCDs
+
+
+def _summarize_prefill_counters(folder, kt_folder, dst):
+    """Matrix-unit and VALU activity of the prefill kernel in the mixed step.
+    SQ_VALU_MFMA_BUSY_CYCLES sums the busy cycles of every SIMD's matrix
+    unit; GRBM_GUI_ACTIVE sums the GPU's busy cycles over the XCDs, so one
+    XCD's share is the kernel's length in cycles."""
+    names = ["SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU",
+             "SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_ACTIVE_INST_LDS", "SQ_LDS_BANK_CONFLICT",
+             "GRBM_GUI_ACTIVE"]
+    vals = {}
+    for c in names:
+        m = {k: v for k, v in _counter_means(folder, c).items() if "prefill_kernel" in k}
+        if m:
+            kname = next(iter(m))
+            vals[c] = m[kname][1]
+    if "GRBM_GUI_ACTIVE" not in vals or "SQ_VALU_MFMA_BUSY_CYCLES" not in vals:
+        return
+    cycles = vals["GRBM_GUI_ACTIVE"] / XCDS
+    lines = [f"# Counters of the prefill kernel in the mixed step (`{_short(kname)}`)", "",
+             "512-row causal chunk on a 3,584-token paged prefix, 16 query / 4 KV heads, d 256, "
+             "BF16; per dispatch, averaged over the profiled steps.", "",
+             "| counter | per dispatch |", "|---|---|"]
+    lines += [f"| {c} | {vals[c]:,.0f} |" for c in names if c in vals]
+    mfma_busy = vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (SIMDS * cycles)
+    lines += ["", f"Kernel length: {cycles:,.0f} cycles (GRBM_GUI_ACTIVE / {XCDS} XCDs).", "",
+              f"Matrix-unit busy: {mfma_busy * 100:.1f} % of the {SIMDS} SIMDs' cycles "
+              f"(SQ_VALU_MFMA_BUSY_CYCLES / ({SIMDS} x kernel cycles)); "
+              f"{vals['SQ_VALU_MFMA_BUSY_CYCLES'] / max(1.0, vals['SQ_INSTS_MFMA']):.1f} busy cycles "
+              "per matrix instruction."]
+    if "SQ_WAVE_CYCLES" in vals and "SQ_WAIT_ANY" in vals:
+        lines.append(f"Waves waiting: {vals['SQ_WAIT_ANY'] / vals['SQ_WAVE_CYCLES'] * 100:.1f} % of "
+                     f"their cycles; VALU issue: "
+                     f"{vals.get('SQ_ACTIVE_INST_VALU', 0) / vals['SQ_WAVE_CYCLES'] * 100:.1f} %.")
+    if os.path.isdir(kt_folder):
+        for r in _csv(_find(kt_folder, "kernel_stats.csv")):
+            if "prefill_kernel" in r["Name"]:
+                us = float(r["AverageNs"]) / 1e3
+                lines.append(f"Clock implied by the kernel trace's {us:.2f} us average: "
+                             f"{cycles / us / 1e3:.2f} GHz.")
+    lines += ["", "Command:", "", f"    {PROFILE_COMMANDS['pmc_prefill_c5']}"]
+    with open(os.path.join(dst, "prefill_c5_counters.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    log("wrote prefill_c5_counters.md")
+
+
 def summarize_profiles(src, dst):
     """Turn rocprofv3 CSV output (folders named as in PROFILE_COMMANDS) into
     the short text summaries kept under profiles/."""
@@ -500,6 +552,10 @@ def summarize_profiles(src, dst):
         with open(os.path.join(dst, name), "w") as f:
             f.write("\n".join(lines) + "\n")
         log(f"wrote {name}")
+
+    if os.path.isdir(os.path.join(src, "pmc_prefill_c5")):
+        _summarize_prefill_counters(os.path.join(src, "pmc_prefill_c5"),
+                                    os.path.join(src, "kt_c5"), dst)
 
     need = ["pmc_fetch_c3", "pmc_write_c3", "pmc_fetch_copy", "pmc_write_copy"]
     if not all(os.path.isdir(os.path.join(src, t)) for t in need):
