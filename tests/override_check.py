@@ -64,6 +64,8 @@ def main():
         for g in (4, 8):
             cases.append(lambda d=d, g=g: decode_case(d, g, [1, 17, 300, 1030, 2049, 4100],
                                                       d * g))
+    # equal lengths, one unit per CU: the plan's equal-length branch
+    cases.append(lambda: decode_case(256, 4, [1024] * 64, 11))
     worst = 0.0
     for run in cases:
         name, err = run()
