@@ -21,7 +21,7 @@ What the pages fix:
   physical blocks; a block is duplicated only when a sequence that shares it
   diverges, i.e. writes into it (copy-on-write, the same three sections).
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
 
 * The free pool is a stack: the most recently freed block is reused first;
   initially block 0 is taken first, then 1, 2, ...

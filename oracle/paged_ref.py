@@ -23,7 +23,7 @@ What the pages fix, and which passage each step follows:
   interleaved with decode tokens (vLLM architecture... deep dive, "Hardware-level
   optimizations"); a chunk row sees every cached key up to its own position.
 
-Readings where the pages are silent (each listed again in the design doc):
+Readings where the pages are silent:
 
 * cache layout ``[num_blocks, num_kv_heads, block_size, head_dim]``, K and V in
   separate tensors; slot = physical_block * block_size + offset; slot < 0 skips.

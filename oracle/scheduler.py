@@ -20,7 +20,7 @@ What the pages fix:
 * Long prompts are cut into chunks interleaved with decode tokens (vLLM
   architecture... deep dive, "Hardware-level optimizations").
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
 
 * Requests are served first come, first served; every request is present from
   iteration 0 (an offline batch); a request is (prompt_len, output_len) and
