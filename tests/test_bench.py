@@ -72,3 +72,30 @@ def test_kernel_names_match_the_committed_kernel_traces():
         text = open(os.path.join(ROOT, "profiles", trace)).read()
         first = [ln for ln in text.splitlines() if ln.startswith("| `pa::")][0]
         assert f"pa::{name}<" in first, (trace, first)
+
+
+def test_prefill_counter_summary(tmp_path):
+    # matrix-unit busy = busy cycles / (SIMDs x kernel cycles), with the kernel
+    # length taken as one XCD's share of GRBM_GUI_ACTIVE
+    pmc = tmp_path / "pmc_prefill_c5" / "run"
+    pmc.mkdir(parents=True)
+    name = "void pa::prefill_kernel<256, 4, 1, 8, 64>(pa::PrefillArgs)"
+    cycles = 100000
+    busy = bench.SIMDS * cycles // 4                        # a quarter of the SIMD cycles
+    values = {"SQ_INSTS_MFMA": busy // 16, "SQ_VALU_MFMA_BUSY_CYCLES": busy,
+              "SQ_WAVE_CYCLES": 1000, "SQ_WAIT_ANY": 300, "SQ_ACTIVE_INST_VALU": 200,
+              "GRBM_GUI_ACTIVE": cycles * bench.XCDS}
+    rows = ["Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value"]
+    for d in (1, 2):                                          # two dispatches, same values
+        rows += [f'{d},"{name}",{c},{v}' for c, v in values.items()]
+        rows.append(f'{d},"void pa::decode_merge_kernel<256>(pa::DecodeArgs)",SQ_INSTS_MFMA,7')
+    (pmc / "p_counter_collection.csv").write_text("\n".join(rows) + "\n")
+    out = tmp_path / "profiles"
+    out.mkdir()
+    bench._summarize_prefill_counters(str(tmp_path / "pmc_prefill_c5"), str(tmp_path / "kt_none"),
+                                      str(out))
+    text = (out / "prefill_c5_counters.md").read_text()
+    assert "Matrix-unit busy: 25.0 %" in text
+    assert "16.0 busy cycles per matrix instruction" in text
+    assert "Waves waiting: 30.0 %" in text and "VALU issue: 20.0 %" in text
+    assert f"Kernel length: {cycles:,} cycles" in text
