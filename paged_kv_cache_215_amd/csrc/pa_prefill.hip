@@ -12,21 +12,22 @@
 // Work decomposition. A workgroup owns (sequence, KV head, 16*R query rows,
 // context split); its NW = max(4, G) waves each take 16 query rows of one
 // query head of the group, so every K/V tile staged in LDS serves all G heads.
-// Per 32-key tile and wave:
-//   S^T[32 x 16] = K[32 x D] . Q^T[D x 16]   A = K rows (LDS, chunk-swizzled),
+// Per tile of KT keys (64 for 8-wave workgroups, else 32) and wave:
+//   S^T[KT x 16] = K[KT x D] . Q^T[D x 16]   A = K rows (LDS, chunk-swizzled),
 //                                             B = Q^T (this lane's query row,
 //                                             held in registers)
-//   O^T[D x 16] += V^T[D x 32] . P^T[32 x 16] A = V^T (LDS, transposed when the
+//   O^T[D x 16] += V^T[D x KT] . P^T[KT x 16] A = V^T (LDS, transposed when the
 //                                             tile is staged), B = P^T (this
 //                                             lane's own softmax weights)
 // With the accumulator layout of the 16x16 MFMA (lane l holds rows
 // 4*(l/16)+i of column l%16) both S^T and O^T keep a query row in the lanes
 // l%16 == row, so the online softmax is lane-local up to a 4-lane reduction.
 // P enters the PV product as two BF16 terms (hi + lo, 16 significant bits);
-// the running sum takes the float32 weights. The B operand of PV takes
-// the 8 weights a lane holds for
-// keys {4q..4q+3, 16+4q..16+4q+3} (q = l/16); V^T columns are stored in that
-// same key order, so the contraction pairs every weight with its key's row.
+// the running sum takes the float32 weights. In each 32-key step of PV the
+// B operand takes the 8 weights a lane holds for keys
+// {4q..4q+3, 16+4q..16+4q+3} (q = l/16) of that step; V^T columns are stored
+// in that same key order, so the contraction pairs every weight with its
+// key's row.
 
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
