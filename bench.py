@@ -139,6 +139,19 @@ def _cpu_worker(args):
     return oracle.decode_ref(q[b:b + 1], kc, vc, bt[b:b + 1], lens[b:b + 1], scale)
 
 
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), or the platform's name."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(case, layers, seq_layers_per_step):
     """Time the oracle on every sequence of the given layers; scale to the
     seconds of a full step (seq_layers_per_step sequence-layers)."""
@@ -396,6 +409,8 @@ def run(args):
             "value": round(S / cb["step_seconds"], 4),
             "unit": "tokens/s",
             "cores": cb["workers"],
+            "cpu": cpu_model(),
+            "effective_gbs": round(bytes_call * L / cb["step_seconds"] / 1e9, 3),
             "kind": "oracle",
             "sample": f"fp64 oracle {'decode_fp8_ref' if fp8 else 'decode_ref'} on all {S} "
                       f"sequences of {len(layers)} of the {L} "
