@@ -87,7 +87,10 @@ struct PrefillShape {
   static constexpr int DTILES = D / 16;           // 16-row tiles of O^T
   static constexpr int QB = KT / 16;              // 16-key row blocks of S^T per tile
   static constexpr int PSTEPS = KT / 32;          // 32-key k-steps of PV per tile
-  static constexpr int VT_STRIDE = KT + 8;        // bf16 per V^T row in LDS (8 pad)
+  // bf16 per V^T row in LDS: 64-key rows take 16 pad elements (8 left a
+  // nine-fold count of LDS bank conflicts); 32-key rows keep 8, so that two
+  // 4-wave workgroups still fit in a CU's LDS
+  static constexpr int VT_STRIDE = KT == 64 ? KT + 16 : KT + 8;
   static constexpr int KCHUNKS = KT * DCH;        // K chunks per tile
   static constexpr int VJOBS = (KT / 4) * (D / 8);  // 4-key x 8-dim V jobs
   // K staging: TPR threads per key row, each loading KPT chunks of that row
