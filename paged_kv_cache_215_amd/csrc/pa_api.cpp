@@ -180,6 +180,7 @@ pa_status_t decode_impl(float* out, const void* query, const void* key_cache,
   a.plan = reinterpret_cast<pa::DecodePlan*>(ws);
   a.plan_cus = 0;
   a.plan_units_per_cu = 0;
+  a.plan_units_unshared = 0;
   a.part_o = reinterpret_cast<float*>(ws + geo.part_o_off);
   a.part_ml = reinterpret_cast<float*>(ws + geo.part_ml_off);
   a.query = query;

@@ -258,7 +258,7 @@ struct PlanLds {
   unsigned short tail_order[kPlanSeqs];  // sequences by the size of their last partition
   int cls_cnt[8][kTailClasses];          // per wave: last partitions of each size class
   long long red_sum[16];
-  int red_a[16], red_b[16];
+  int red_a[16], red_b[16], red_c[16];
   int part_tokens, full_total, max_nparts;
   int ranked;                 // tail_order holds the order (else: sequence order)
   int ticket;                 // this workgroup's current unit
@@ -275,39 +275,59 @@ __device__ void build_plan(const DecodeArgs& a, PlanLds& pl) {
   const int b0 = min(S, tid * chunk), b1 = min(S, b0 + chunk);
   long long sum = 0;
   int mn = 0x7fffffff, mx = 0;
+  // shared: some sequence starts on the same physical block as the one before
+  // it (copy-on-write rollouts of one prompt are consecutive)
+  // (an entry is read whatever the length, so that its load does not wait on
+  // the length's; it counts only for a non-empty context)
+  int shared = 0;
+  int prev_first = -1;
+  if (b0 > 0 && b0 < b1) {
+    const int n = a.context_lens[b0 - 1];
+    const int e = a.block_tables[(int64_t)(b0 - 1) * a.max_blocks_per_seq];
+    if (n > 0 && a.ctx_limit > 0) prev_first = e;
+  }
   for (int b = b0; b < b1; ++b) {
     int n = a.context_lens[b];
+    const int e = a.block_tables[(int64_t)b * a.max_blocks_per_seq];
     n = n < 0 ? 0 : n;
     n = n > a.ctx_limit ? a.ctx_limit : n;
     pl.lens[b] = n;
     sum += n;
     mn = min(mn, n);
     mx = max(mx, n);
+    const int first = n > 0 ? e : -1;
+    shared |= first >= 0 && first == prev_first;
+    prev_first = first;
   }
   sum = wave_sum_ll(sum);
   mn = wave_min(mn);
   mx = wave_max(mx);
+  shared = wave_max(shared);
   if (lane == 0) {
     pl.red_sum[wave] = sum;
     pl.red_a[wave] = mn;
     pl.red_b[wave] = mx;
+    pl.red_c[wave] = shared;
   }
   __syncthreads();
   if (wave == 0) {
     sum = lane < NW ? pl.red_sum[lane] : 0;
     mn = lane < NW ? pl.red_a[lane] : 0x7fffffff;
     mx = lane < NW ? pl.red_b[lane] : 0;
+    shared = lane < NW ? pl.red_c[lane] : 0;
     sum = wave_sum_ll(sum);
     mn = wave_min(mn);
     mx = wave_max(mx);
+    shared = wave_max(shared);
     if (lane == 0) {
       int P = a.part_floor;
       if (mx > 0 && mn == mx) {
         for (int p = a.part_floor; p <= a.part_cap; p *= 2)
           if ((long long)S * a.num_kv_heads * ((mx + p - 1) / p) >= a.plan_cus) P = p;
       } else if (mx > 0) {
+        const int units = shared ? a.plan_units_per_cu : a.plan_units_unshared;
         const long long budget =
-            sum * a.num_kv_heads / ((long long)a.plan_cus * a.plan_units_per_cu);
+            sum * a.num_kv_heads / ((long long)a.plan_cus * units);
         for (int p = a.part_floor; p <= a.part_cap; p *= 2)
           if (p <= budget) P = p;
       }
@@ -1225,17 +1245,23 @@ int device_cus() {
 }
 
 // Work units per CU the plan aims for on ragged batches: fewer, larger
-// partitions cost less per unit, more give the ticketed tail finer grain; 2
-// measured best on the ragged, shared-prompt and mixed-step batches. The
-// environment override exists for tuning sweeps only.
-int units_per_cu() {
+// partitions cost less per unit, more give the ticketed tail finer grain.
+// Batches whose sequences share prompt blocks take 2 (with 1, every sequence
+// of the shared-prompt batch is a single ticketed unit, and rollouts no
+// longer read their shared blocks together: 170 -> 205 us); others take 1
+// (ragged 32-sequence layer 108.5 -> 106.5 us, E4M3 70.7 -> 66.7 us, mixed
+// step 305 -> 300 us). The environment override (both cases) exists for
+// tuning sweeps only.
+static int units_override() {
   static const int v = [] {
     const char* s = std::getenv("PA_DECODE_UNITS_PER_CU");
     const int x = s ? std::atoi(s) : 0;
-    return x > 0 ? x : 2;
+    return x > 0 ? x : 0;
   }();
   return v;
 }
+int units_per_cu() { return units_override() ? units_override() : 2; }
+int units_per_cu_unshared() { return units_override() ? units_override() : 1; }
 
 template <typename Kernel>
 int resident_per_cu(Kernel k, int threads) {
@@ -1264,6 +1290,7 @@ static hipError_t launch_kernel(const DecodeArgs& a, hipStream_t stream) {
     c.context_lens = a.context_lens + s0;
     c.plan_cus = cus;
     c.plan_units_per_cu = units_per_cu();
+    c.plan_units_unshared = units_per_cu_unshared();
     const int64_t most_units = (int64_t)c.num_seqs * c.num_kv_heads * c.max_parts;
     const int64_t slots = (int64_t)cus * per_cu;
     const int64_t grid = most_units < slots ? most_units : slots;

@@ -34,7 +34,8 @@ struct DecodeArgs {
   int ctx_limit;         // min(max_context_len, max_blocks_per_seq * block_size)
   DecodePlan* plan;      // workspace head: plan summary for the merge kernel
   int plan_cus;          // CUs of the device (sizes the plan)
-  int plan_units_per_cu; // target units per CU for ragged batches
+  int plan_units_per_cu; // target units per CU for ragged batches that share blocks
+  int plan_units_unshared; // the same when no two consecutive sequences share their first block
   int part_floor;        // smallest partition size the plan may choose
   int part_cap;          // largest partition size the plan may choose
   int waves;             // waves per partition workgroup (4 or 8)
