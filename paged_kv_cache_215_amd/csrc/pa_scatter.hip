@@ -68,59 +68,46 @@ __device__ __forceinline__ uint32_t pack4(float a, float b, float c, float d, fl
          (e4m3_code(__fdiv_rn(c, s)) << 16) | (e4m3_code(__fdiv_rn(d, s)) << 24);
 }
 
-// 16 source elements starting at element e of a row -> 16 codes.
-__device__ __forceinline__ uint4 quantize16(const void* src, int64_t e, bool bf16, float s) {
-  float x[16];
+// 4 source elements starting at element e of a row -> 4 codes in one word.
+__device__ __forceinline__ uint32_t quantize4(const void* src, int64_t e, bool bf16, float s) {
   if (bf16) {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + e);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint4 w = p[h];
-      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        x[8 * h + 2 * j] = bf16_lo(ws[j]);
-        x[8 * h + 2 * j + 1] = bf16_hi(ws[j]);
-      }
-    }
-  } else {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(src) + e);
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const float4 w = p[h];
-      x[4 * h] = w.x; x[4 * h + 1] = w.y; x[4 * h + 2] = w.z; x[4 * h + 3] = w.w;
-    }
+    const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(src) + e);
+    return pack4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y), s);
   }
-  return make_uint4(pack4(x[0], x[1], x[2], x[3], s), pack4(x[4], x[5], x[6], x[7], s),
-                    pack4(x[8], x[9], x[10], x[11], s), pack4(x[12], x[13], x[14], x[15], s));
+  const float4 w = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + e);
+  return pack4(w.x, w.y, w.z, w.w, s);
 }
 
-// One thread per 16-code chunk of a (token, KV head) row, K and V together.
+// One thread per 4 codes of a (token, KV head) row: the first half of the
+// threads write K, the second half V. (Each code takes an IEEE division, so
+// a thread's work is a serial chain; short chains on many threads finish
+// sooner than 32 divisions on each of a few.)
 __global__ __launch_bounds__(256) void scatter_fp8_kernel(ScatterFp8Args a) {
-  const int row_chunks = a.head_dim / 16;
-  const int64_t per_token = (int64_t)a.num_kv_heads * row_chunks;
-  const int64_t total = (int64_t)a.num_tokens * per_token;
-  uint4* kc = reinterpret_cast<uint4*>(a.key_cache);
-  uint4* vc = reinterpret_cast<uint4*>(a.value_cache);
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+  const int row_words = a.head_dim / 4;
+  const int64_t per_token = (int64_t)a.num_kv_heads * row_words;
+  const int64_t total = (int64_t)a.num_tokens * per_token;  // words per cache
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < 2 * total;
        i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t t = i / per_token;
-    const int64_t rest = i - t * per_token;  // head * row_chunks + chunk
+    const bool is_v = i >= total;
+    const int64_t j = is_v ? i - total : i;
+    const int64_t t = j / per_token;
+    const int64_t rest = j - t * per_token;  // head * row_words + word
     const int64_t slot = a.slot_mapping[t];
     if (slot < 0 || slot >= a.num_slots) continue;  // skipped or out of range
     const int64_t blk = slot / a.block_size;
     const int64_t off = slot - blk * a.block_size;
-    const int64_t head = rest / row_chunks;
-    const int64_t chunk = rest - head * row_chunks;
-    const int64_t dst = ((blk * a.num_kv_heads + head) * a.block_size + off) * row_chunks + chunk;
-    const int64_t e = i * 16;  // first source element of this chunk
-    kc[dst] = quantize16(a.key, e, a.src_bf16, a.k_scale[head]);
-    vc[dst] = quantize16(a.value, e, a.src_bf16, a.v_scale[head]);
+    const int64_t head = rest / row_words;
+    const int64_t word = rest - head * row_words;
+    const int64_t dst = ((blk * a.num_kv_heads + head) * a.block_size + off) * row_words + word;
+    const int64_t e = j * 4;  // first source element of this word
+    uint32_t* cache = static_cast<uint32_t*>(is_v ? a.value_cache : a.key_cache);
+    cache[dst] = quantize4(is_v ? a.value : a.key, e, a.src_bf16,
+                           is_v ? a.v_scale[head] : a.k_scale[head]);
   }
 }
 
 hipError_t launch_scatter_fp8(const ScatterFp8Args& a, hipStream_t stream) {
-  const int64_t total = (int64_t)a.num_tokens * a.num_kv_heads * (a.head_dim / 16);
+  const int64_t total = 2 * (int64_t)a.num_tokens * a.num_kv_heads * (a.head_dim / 4);
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65535) blocks = 65535;
   hipLaunchKernelGGL(scatter_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
