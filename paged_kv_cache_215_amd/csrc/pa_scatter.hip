@@ -23,14 +23,18 @@ __global__ __launch_bounds__(256) void scatter_kernel(ScatterArgs a) {
     const int64_t t = i / per_token;
     const int64_t rest = i - t * per_token;          // head * row_chunks + chunk
     const int64_t slot = a.slot_mapping[t];
+    // the rows are read before the slot is tested, so that their loads and
+    // the slot's are in flight together
+    const uint4 kv = key[i];
+    const uint4 vv = value[i];
     if (slot < 0 || slot >= a.num_slots) continue;   // skipped or out of range
     const int64_t blk = slot / a.block_size;
     const int64_t off = slot - blk * a.block_size;
     const int64_t head = rest / a.row_chunks;
     const int64_t chunk = rest - head * a.row_chunks;
     const int64_t dst = ((blk * a.num_kv_heads + head) * a.block_size + off) * a.row_chunks + chunk;
-    kc[dst] = key[i];
-    vc[dst] = value[i];
+    kc[dst] = kv;
+    vc[dst] = vv;
   }
 }
 
@@ -93,16 +97,17 @@ __global__ __launch_bounds__(256) void scatter_fp8_kernel(ScatterFp8Args a) {
     const int64_t t = j / per_token;
     const int64_t rest = j - t * per_token;  // head * row_words + word
     const int64_t slot = a.slot_mapping[t];
+    const int64_t head = rest / row_words;
+    const int64_t word = rest - head * row_words;
+    // the codes are formed before the slot is tested, so that the source
+    // loads and the slot's are in flight together
+    const uint32_t codes = quantize4(is_v ? a.value : a.key, j * 4, a.src_bf16,
+                                     is_v ? a.v_scale[head] : a.k_scale[head]);
     if (slot < 0 || slot >= a.num_slots) continue;  // skipped or out of range
     const int64_t blk = slot / a.block_size;
     const int64_t off = slot - blk * a.block_size;
-    const int64_t head = rest / row_words;
-    const int64_t word = rest - head * row_words;
     const int64_t dst = ((blk * a.num_kv_heads + head) * a.block_size + off) * row_words + word;
-    const int64_t e = j * 4;  // first source element of this word
-    uint32_t* cache = static_cast<uint32_t*>(is_v ? a.value_cache : a.key_cache);
-    cache[dst] = quantize4(is_v ? a.value : a.key, e, a.src_bf16,
-                           is_v ? a.v_scale[head] : a.k_scale[head]);
+    static_cast<uint32_t*>(is_v ? a.value_cache : a.key_cache)[dst] = codes;
   }
 }
 
