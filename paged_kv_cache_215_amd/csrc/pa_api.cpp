@@ -14,17 +14,6 @@
 
 namespace pa {
 
-int decode_target_workgroups() {
-  // Workgroups the decode launch aims for (a few times the CU count). The
-  // environment override exists for tuning sweeps only.
-  static const int target = [] {
-    const char* s = std::getenv("PA_DECODE_TARGET_WGS");
-    const int v = s ? std::atoi(s) : 0;
-    return v > 0 ? v : 1024;
-  }();
-  return target;
-}
-
 int decode_waves_per_workgroup() {
   static const int waves = [] {
     const char* s = std::getenv("PA_DECODE_WAVES");

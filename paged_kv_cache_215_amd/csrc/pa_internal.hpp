@@ -120,7 +120,6 @@ struct DecodeLaunch {
   int waves;
 };
 
-int decode_target_workgroups();
 int decode_waves_per_workgroup();
 DecodeLaunch decode_launch_shape(int num_seqs, int num_kv_heads, int block_size,
                                  int max_context_len);
