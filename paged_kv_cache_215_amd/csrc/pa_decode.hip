@@ -192,7 +192,7 @@ __device__ __forceinline__ float reduce_neutral(float x) {
   return x;
 }
 
-template <typename Shape>
+template <typename Shape, bool Keep>
 __device__ __forceinline__ void load_k(const uint4* __restrict__ kbase, int lane,
                                        uint4 (&kb)[Shape::NGK][Shape::KCH]) {
   constexpr int RC = Shape::RC, KL = Shape::KL, RK = Shape::RK;
@@ -201,10 +201,10 @@ __device__ __forceinline__ void load_k(const uint4* __restrict__ kbase, int lane
   for (int gk = 0; gk < Shape::NGK; ++gk)
 #pragma unroll
     for (int i = 0; i < Shape::KCH; ++i)
-      kb[gk][i] = load_stream(kbase + (gk * RK + krow) * RC + kc + KL * i);
+      kb[gk][i] = load_kv<Keep>(kbase + (gk * RK + krow) * RC + kc + KL * i);
 }
 
-template <typename Shape>
+template <typename Shape, bool Keep>
 __device__ __forceinline__ void load_v(const uint4* __restrict__ vbase, int lane,
                                        typename Shape::VChunk (&vb)[Shape::NGV]) {
   using VC = typename Shape::VChunk;
@@ -212,7 +212,7 @@ __device__ __forceinline__ void load_v(const uint4* __restrict__ vbase, int lane
   const VC* base = reinterpret_cast<const VC*>(vbase);
   const int vrow = lane / VL, vc = lane % VL;
 #pragma unroll
-  for (int gv = 0; gv < Shape::NGV; ++gv) vb[gv] = load_stream(base + (gv * RV + vrow) * VL + vc);
+  for (int gv = 0; gv < Shape::NGV; ++gv) vb[gv] = load_kv<Keep>(base + (gv * RV + vrow) * VL + vc);
 }
 
 // ---------------------------------------------------------------------------
@@ -261,6 +261,7 @@ struct PlanLds {
   int red_a[16], red_b[16], red_c[16];
   int part_tokens, full_total, max_nparts;
   int ranked;                 // tail_order holds the order (else: sequence order)
+  int shared;                 // some sequence starts on the block of the one before
   int ticket;                 // this workgroup's current unit
 };
 
@@ -333,6 +334,7 @@ __device__ void build_plan(const DecodeArgs& a, PlanLds& pl) {
       }
       pl.part_tokens = P;
       pl.ranked = mn != mx;  // equal lengths: equal last partitions, already in order
+      pl.shared = shared;
     }
   }
   __syncthreads();
@@ -461,13 +463,16 @@ __global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(DecodeArgs
   const int tid = threadIdx.x;
   build_plan<NW>(a, s_plan);
   const int P = s_plan.part_tokens;
+  // blocks shared between sequences: K/V through ordinary loads (see load_kv)
+  const bool keep = __builtin_amdgcn_readfirstlane(s_plan.shared) != 0;
   if (blockIdx.x == 0 && tid == 0) {  // for the merge kernel
     a.plan->part_tokens = P;
     a.plan->max_nparts = s_plan.max_nparts;
   }
 
   // One work unit: (sequence, KV head, partition) of the plan.
-  auto unit = [&](const int seq, const int kvh, const int part) {
+  auto unit = [&](const int seq, const int kvh, const int part, auto keep_tag) {
+  constexpr bool kKeep = decltype(keep_tag)::value;
   const int n = s_plan.lens[seq];
   const int start = part * P;
   if (n == 0) {  // empty context: a zero row
@@ -590,7 +595,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(DecodeArgs
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (kPrefetch) load_k<S>(kcache + off_next, lane, kb);
+    if constexpr (kPrefetch) load_k<S, kKeep>(kcache + off_next, lane, kb);
     __builtin_amdgcn_sched_barrier(0);
     transpose_reduce<NV, KL / 2>(sc);
 
@@ -693,7 +698,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(DecodeArgs
         for (int e = 0; e < E; ++e) acc[g][e] = __builtin_fmaf(pw[g], v[e], acc[g][e]);
     }
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (kPrefetch) load_v<S>(vcache + off_next, lane, vb);
+    if constexpr (kPrefetch) load_v<S, kKeep>(vcache + off_next, lane, vb);
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -701,8 +706,8 @@ __global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(DecodeArgs
   if (t < ntiles) {
     int blk = tile_block(t);
     const int64_t off = tile_offset(t, blk);
-    load_k<S>(kcache + off, lane, kb);
-    load_v<S>(vcache + off, lane, vb);
+    load_k<S, kKeep>(kcache + off, lane, kb);
+    load_v<S, kKeep>(vcache + off, lane, vb);
     for (; t + kWaves < ntiles; t += kWaves) {
       const int blk_next = tile_block(t + kWaves);
       process(t, blk, tile_offset(t + kWaves, blk_next), std::true_type{});
@@ -798,7 +803,8 @@ __global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(DecodeArgs
   const int n_units = (s_plan.full_total + a.num_seqs) * a.num_kv_heads;
   for (int u = blockIdx.x; u < n_full; u += gridDim.x) {
     const int2 e = plan_unit(s_plan, a.num_seqs, u / a.num_kv_heads);
-    unit(e.x, u % a.num_kv_heads, e.y);
+    if (keep) unit(e.x, u % a.num_kv_heads, e.y, std::true_type{});
+    else unit(e.x, u % a.num_kv_heads, e.y, std::false_type{});
     __syncthreads();  // LDS is reused by the next unit
   }
   for (;;) {
@@ -808,7 +814,8 @@ __global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(DecodeArgs
     __syncthreads();  // every thread has read the ticket before it is reused
     if (u < n_full || u >= n_units) break;  // (below n_full: workspace never zero-filled)
     const int2 e = plan_unit(s_plan, a.num_seqs, u / a.num_kv_heads);
-    unit(e.x, u % a.num_kv_heads, e.y);
+    if (keep) unit(e.x, u % a.num_kv_heads, e.y, std::true_type{});
+    else unit(e.x, u % a.num_kv_heads, e.y, std::false_type{});
     __syncthreads();
   }
 }
@@ -874,12 +881,15 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeArgs a) {
   const int tid = threadIdx.x;
   build_plan<NW>(a, s_plan);
   const int P = s_plan.part_tokens;
+  // blocks shared between sequences: K/V through ordinary loads (see load_kv)
+  const bool keep = __builtin_amdgcn_readfirstlane(s_plan.shared) != 0;
   if (blockIdx.x == 0 && tid == 0) {  // for the merge kernel
     a.plan->part_tokens = P;
     a.plan->max_nparts = s_plan.max_nparts;
   }
 
-  auto unit = [&](const int seq, const int kvh, const int part) {
+  auto unit = [&](const int seq, const int kvh, const int part, auto keep_tag) {
+  constexpr bool kKeep = decltype(keep_tag)::value;
   const int n = s_plan.lens[seq];
   const int start = part * P;
   if (n == 0) {  // empty context: a zero row
@@ -951,13 +961,13 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeArgs a) {
   auto load_k = [&](int64_t off) {
 #pragma unroll
     for (int j = 0; j < KLD; ++j)
-      kop[j] = load_stream(kcache + off + col * CCH + (kFp8 ? grp + 4 * j : 4 * j + grp));
+      kop[j] = load_kv<kKeep>(kcache + off + col * CCH + (kFp8 ? grp + 4 * j : 4 * j + grp));
   };
   auto load_v = [&](int64_t off) {
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
       const int idx = lane + kWave * i;
-      vreg[i] = load_stream(vcache + off + (idx / CCH) * CCH + idx % CCH);
+      vreg[i] = load_kv<kKeep>(vcache + off + (idx / CCH) * CCH + idx % CCH);
     }
   };
 
@@ -1119,7 +1129,8 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeArgs a) {
   const int n_units = (s_plan.full_total + a.num_seqs) * a.num_kv_heads;
   for (int u = blockIdx.x; u < n_full; u += gridDim.x) {
     const int2 e = plan_unit(s_plan, a.num_seqs, u / a.num_kv_heads);
-    unit(e.x, u % a.num_kv_heads, e.y);
+    if (keep) unit(e.x, u % a.num_kv_heads, e.y, std::true_type{});
+    else unit(e.x, u % a.num_kv_heads, e.y, std::false_type{});
     __syncthreads();  // LDS is reused by the next unit
   }
   for (;;) {
@@ -1129,7 +1140,8 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeArgs a) {
     __syncthreads();  // every thread has read the ticket before it is reused
     if (u < n_full || u >= n_units) break;  // (below n_full: workspace never zero-filled)
     const int2 e = plan_unit(s_plan, a.num_seqs, u / a.num_kv_heads);
-    unit(e.x, u % a.num_kv_heads, e.y);
+    if (keep) unit(e.x, u % a.num_kv_heads, e.y, std::true_type{});
+    else unit(e.x, u % a.num_kv_heads, e.y, std::false_type{});
     __syncthreads();
   }
 }

@@ -40,6 +40,19 @@ __device__ __forceinline__ uint2 load_stream(const uint2* p) {
   const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
   return make_uint2(v.x, v.y);
 }
+// The load of a K/V chunk a work unit uses: nontemporal (each byte is read
+// once), or ordinary when the blocks are shared between sequences (rollouts
+// of one prompt), where the caches' reuse across work units matters. The
+// choice is a template argument: two forms in one function body get merged
+// by the compiler into the ordinary one.
+template <bool Keep, typename C>
+__device__ __forceinline__ C load_kv(const C* p) {
+  if constexpr (Keep) {
+    return *p;
+  } else {
+    return load_stream(p);
+  }
+}
 __device__ __forceinline__ void zero_chunk(uint4& v) { v = make_uint4(0, 0, 0, 0); }
 __device__ __forceinline__ void zero_chunk(uint2& v) { v = make_uint2(0, 0); }
 
