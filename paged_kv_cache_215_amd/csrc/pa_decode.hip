@@ -28,9 +28,10 @@
 // of 4 at d >= 128 as well.
 //
 // The plan also tests whether consecutive sequences start on the same
-// physical block (copy-on-write rollouts of one prompt). If none do, it aims
+// physical block (copy-on-write rollouts of one prompt). If fewer than half
+// of the live sequences do, it aims
 // at one unit per CU and the K/V loads are nontemporal: each byte is read
-// once. If some do, it aims at two units per CU, dealt in lockstep, and the
+// once. Otherwise it aims at two units per CU, dealt in lockstep, and the
 // dealt partitions (the shared prompt) use ordinary loads so that the
 // rollouts reading the same blocks find them in the caches.
 //
@@ -265,7 +266,7 @@ struct PlanLds {
   unsigned short tail_order[kPlanSeqs];  // sequences by the size of their last partition
   int cls_cnt[8][kTailClasses];          // per wave: last partitions of each size class
   long long red_sum[16];
-  int red_a[16], red_b[16], red_c[16];
+  int red_a[16], red_b[16], red_c[16], red_d[16];
   int part_tokens, full_total, max_nparts;
   int ranked;                 // tail_order holds the order (else: sequence order)
   int shared;                 // some sequence starts on the block of the one before
@@ -283,11 +284,13 @@ __device__ void build_plan(const DecodeArgs& a, PlanLds& pl) {
   const int b0 = min(S, tid * chunk), b1 = min(S, b0 + chunk);
   long long sum = 0;
   int mn = 0x7fffffff, mx = 0;
-  // shared: some sequence starts on the same physical block as the one before
-  // it (copy-on-write rollouts of one prompt are consecutive)
+  // shared: sequences that start on the same physical block as the one
+  // before them (copy-on-write rollouts of one prompt are consecutive);
+  // live: sequences with a non-empty context. The batch counts as sharing
+  // blocks when at least half of its live sequences do.
   // (an entry is read whatever the length, so that its load does not wait on
   // the length's; it counts only for a non-empty context)
-  int shared = 0;
+  int shared = 0, live = 0;
   int prev_first = -1;
   if (b0 > 0 && b0 < b1) {
     const int n = a.context_lens[b0 - 1];
@@ -304,18 +307,21 @@ __device__ void build_plan(const DecodeArgs& a, PlanLds& pl) {
     mn = min(mn, n);
     mx = max(mx, n);
     const int first = n > 0 ? e : -1;
-    shared |= first >= 0 && first == prev_first;
+    shared += first >= 0 && first == prev_first;
+    live += n > 0;
     prev_first = first;
   }
   sum = wave_sum_ll(sum);
   mn = wave_min(mn);
   mx = wave_max(mx);
-  shared = wave_max(shared);
+  shared = (int)wave_sum_ll(shared);
+  live = (int)wave_sum_ll(live);
   if (lane == 0) {
     pl.red_sum[wave] = sum;
     pl.red_a[wave] = mn;
     pl.red_b[wave] = mx;
     pl.red_c[wave] = shared;
+    pl.red_d[wave] = live;
   }
   __syncthreads();
   if (wave == 0) {
@@ -323,10 +329,13 @@ __device__ void build_plan(const DecodeArgs& a, PlanLds& pl) {
     mn = lane < NW ? pl.red_a[lane] : 0x7fffffff;
     mx = lane < NW ? pl.red_b[lane] : 0;
     shared = lane < NW ? pl.red_c[lane] : 0;
+    live = lane < NW ? pl.red_d[lane] : 0;
     sum = wave_sum_ll(sum);
     mn = wave_min(mn);
     mx = wave_max(mx);
-    shared = wave_max(shared);
+    shared = (int)wave_sum_ll(shared);
+    live = (int)wave_sum_ll(live);
+    shared = live > 0 && 2 * shared >= live;
     if (lane == 0) {
       int P = a.part_floor;
       if (mx > 0 && mn == mx) {
