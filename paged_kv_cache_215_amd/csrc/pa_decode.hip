@@ -29,11 +29,11 @@
 //
 // The plan also tests whether consecutive sequences start on the same
 // physical block (copy-on-write rollouts of one prompt). If fewer than half
-// of the live sequences do, it aims
-// at one unit per CU and the K/V loads are nontemporal: each byte is read
-// once. Otherwise it aims at two units per CU, dealt in lockstep, and the
-// dealt partitions (the shared prompt) use ordinary loads so that the
-// rollouts reading the same blocks find them in the caches.
+// of the live sequences do, it aims at one unit per CU and the K/V loads are
+// nontemporal: each byte is read once. Otherwise it aims at two units per
+// CU, dealt in lockstep, and the dealt partitions (the shared prompt) use
+// ordinary loads so that the rollouts reading the same blocks find them in
+// the caches.
 //
 // Register layout of a 16-token tile (per wave):
 //   K: each row (token) is spread over KL lanes that each hold KCH 16-byte
