@@ -84,7 +84,9 @@ typedef enum {
   PA_ERR_WORKSPACE = 5,
   PA_ERR_HIP = 6,
   PA_ERR_OUT_OF_BLOCKS = 7,  /* block manager: the pool lacks the blocks asked for */
-  PA_ERR_STATE = 8           /* block manager: unknown or duplicate sequence id */
+  PA_ERR_STATE = 8,          /* block manager: unknown or duplicate sequence id */
+  PA_ERR_NOMEM = 9           /* host side: an allocation failed (no C++ exception
+                                ever crosses this ABI; see pa_blocks.h) */
 } pa_status_t;
 
 /*

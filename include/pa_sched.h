@@ -84,8 +84,10 @@ typedef struct {
   const int64_t* resumed;
 } pa_step_plan;
 
-/* PA_ERR_SHAPE for non-positive sizes or a request with prompt_len < 1 or
- * output_len < 1; *out is NULL on error. */
+/* PA_ERR_SHAPE for non-positive sizes, num_host_blocks above 2^31 - 1, or a
+ * request with prompt_len < 1 or output_len < 1; PA_ERR_NOMEM if host memory
+ * runs out (nothing is leaked); *out is NULL on error. Host swap blocks are
+ * handed out lazily, so creation costs no memory per host block. */
 pa_status_t pa_sched_create(const pa_sched_config* cfg, const int32_t* prompt_lens,
                             const int32_t* output_lens, int32_t num_requests,
                             pa_scheduler** out);
@@ -96,7 +98,9 @@ int32_t pa_sched_done(const pa_scheduler* s);
 
 /* Plan the next iteration. PA_ERR_OUT_OF_BLOCKS if a preemption needs more
  * host blocks than are free (the plan is then incomplete and the scheduler
- * should be discarded). */
+ * should be discarded). PA_ERR_NOMEM if host memory runs out half way: the
+ * scheduler is then unusable and every later step returns PA_ERR_STATE
+ * (destroy it). No C++ exception leaves any pa_sched_* call. */
 pa_status_t pa_sched_step(pa_scheduler* s, pa_step_plan* plan);
 
 /* The device pool's manager, for block tables (pa_bm_tables) and queries. */

@@ -24,7 +24,7 @@ PA_DTYPE_FP8_E4M3 = 2
 STATUS_NAMES = {
     0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED",
     4: "PA_ERR_ALIGN", 5: "PA_ERR_WORKSPACE", 6: "PA_ERR_HIP", 7: "PA_ERR_OUT_OF_BLOCKS",
-    8: "PA_ERR_STATE",
+    8: "PA_ERR_STATE", 9: "PA_ERR_NOMEM",
 }
 
 # Exported symbols and their C signatures (mirrors include/pa.h).

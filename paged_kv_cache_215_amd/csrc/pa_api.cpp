@@ -445,7 +445,8 @@ const char* pa_status_string(pa_status_t status) {
     case PA_ERR_WORKSPACE: return "workspace too small";
     case PA_ERR_HIP: return "HIP launch failed";
     case PA_ERR_OUT_OF_BLOCKS: return "the block pool lacks the blocks asked for";
-    case PA_ERR_STATE: return "unknown or duplicate sequence id";
+    case PA_ERR_STATE: return "unknown or duplicate sequence id, or an object left unusable";
+    case PA_ERR_NOMEM: return "host memory could not be allocated";
   }
   return "unknown status";
 }

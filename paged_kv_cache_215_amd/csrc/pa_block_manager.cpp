@@ -11,13 +11,25 @@
 //
 // Every operation is O(tokens touched + blocks touched); an append first
 // counts the blocks it needs, so a failing call leaves the state unchanged.
+//
+// The pool is held lazily, so that creating a manager costs O(1) memory
+// whatever num_blocks is: blocks that were never handed out are the range
+// [fresh, num_blocks), taken in increasing order, and only returned blocks
+// sit on an explicit stack above it. That is the same order as a stack
+// initialised to num_blocks - 1 .. 0 (top = 0). Reference counts exist for
+// blocks below `fresh` only.
+//
+// No C++ exception leaves this file: every entry point catches them and
+// returns PA_ERR_NOMEM. Each mutating call reserves the memory it may need
+// before it changes anything, so a failed allocation leaves the manager as it
+// was.
 
 #include "pa_blocks.h"
 
 #include <algorithm>
 #include <cstdint>
+#include <new>
 #include <unordered_map>
-#include <unordered_set>
 #include <vector>
 
 struct pa_block_manager {
@@ -28,16 +40,25 @@ struct pa_block_manager {
   int64_t num_blocks = 0;
   int32_t block_size = 0;
   int32_t capacity = 0;
-  std::vector<int32_t> free_stack;  // top = back
-  std::vector<int32_t> refcount;
+  int64_t fresh = 0;                // blocks [fresh, num_blocks) were never taken
+  std::vector<int32_t> free_stack;  // returned blocks, top = back
+  std::vector<int32_t> refcount;    // [fresh]
   std::unordered_map<int64_t, Seq> seqs;
   std::vector<int64_t> copies;      // queued (src, dst) pairs, flattened
   size_t copies_head = 0;           // first pair not yet taken (in pairs)
 
+  int64_t num_free() const { return (int64_t)free_stack.size() + (num_blocks - fresh); }
+
+  // Needs refcount capacity for one more fresh block (reserved by the caller).
   int32_t take() {
-    const int32_t b = free_stack.back();
-    free_stack.pop_back();
-    refcount[b] = 1;
+    if (!free_stack.empty()) {
+      const int32_t b = free_stack.back();
+      free_stack.pop_back();
+      refcount[(size_t)b] = 1;
+      return b;
+    }
+    const int32_t b = (int32_t)fresh++;
+    refcount.push_back(1);
     return b;
   }
 
@@ -46,11 +67,32 @@ struct pa_block_manager {
     const int64_t n = s.length, bs = block_size;
     // positions p in [n, n + k) with p % bs == 0
     const int64_t first = (n + bs - 1) / bs * bs;
-    const int64_t fresh = first < n + k ? (n + k - 1 - first) / bs + 1 : 0;
-    const bool cow = (n % bs) != 0 && refcount[s.blocks.back()] > 1;
-    return fresh + (cow ? 1 : 0);
+    const int64_t fresh_blocks = first < n + k ? (n + k - 1 - first) / bs + 1 : 0;
+    const bool cow = (n % bs) != 0 && refcount[(size_t)s.blocks.back()] > 1;
+    return fresh_blocks + (cow ? 1 : 0);
   }
 };
+
+namespace {
+
+// Capacity for n elements, growing geometrically (so that reserving before
+// every mutation keeps appends amortised O(1)); may throw.
+template <typename V>
+void room_for(V& v, size_t n) {
+  if (v.capacity() < n) v.reserve(std::max(n, 2 * v.capacity()));
+}
+
+// Runs f and turns any C++ exception into a status (none crosses the C ABI).
+template <typename F>
+pa_status_t guarded(F&& f) noexcept {
+  try {
+    return f();
+  } catch (...) {
+    return PA_ERR_NOMEM;
+  }
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -60,78 +102,92 @@ pa_status_t pa_bm_create(int64_t num_blocks, int32_t block_size, int32_t max_blo
   *out = nullptr;
   if (num_blocks <= 0 || num_blocks > INT32_MAX || block_size <= 0 || max_blocks_per_seq <= 0)
     return PA_ERR_SHAPE;
-  auto* bm = new pa_block_manager();
-  bm->num_blocks = num_blocks;
-  bm->block_size = block_size;
-  bm->capacity = max_blocks_per_seq;
-  bm->free_stack.resize((size_t)num_blocks);
-  for (int64_t i = 0; i < num_blocks; ++i) bm->free_stack[(size_t)i] = (int32_t)(num_blocks - 1 - i);
-  bm->refcount.assign((size_t)num_blocks, 0);
-  *out = bm;
-  return PA_OK;
+  return guarded([&] {
+    auto* bm = new pa_block_manager();
+    bm->num_blocks = num_blocks;
+    bm->block_size = block_size;
+    bm->capacity = max_blocks_per_seq;
+    *out = bm;
+    return PA_OK;
+  });
 }
 
 void pa_bm_destroy(pa_block_manager* bm) { delete bm; }
 
 pa_status_t pa_bm_add(pa_block_manager* bm, int64_t seq) {
   if (!bm) return PA_ERR_NULL;
-  if (bm->seqs.count(seq)) return PA_ERR_STATE;
-  bm->seqs.emplace(seq, pa_block_manager::Seq{});
-  return PA_OK;
+  return guarded([&] {
+    if (bm->seqs.count(seq)) return PA_ERR_STATE;
+    bm->seqs.emplace(seq, pa_block_manager::Seq{});  // unchanged if it throws
+    return PA_OK;
+  });
 }
 
 pa_status_t pa_bm_fork(pa_block_manager* bm, int64_t parent, int64_t child) {
   if (!bm) return PA_ERR_NULL;
-  auto it = bm->seqs.find(parent);
-  if (it == bm->seqs.end() || bm->seqs.count(child)) return PA_ERR_STATE;
-  pa_block_manager::Seq copy = it->second;
-  for (int32_t b : copy.blocks) ++bm->refcount[(size_t)b];
-  bm->seqs.emplace(child, std::move(copy));
-  return PA_OK;
+  return guarded([&] {
+    auto it = bm->seqs.find(parent);
+    if (it == bm->seqs.end() || bm->seqs.count(child)) return PA_ERR_STATE;
+    pa_block_manager::Seq copy = it->second;
+    // insert first (it may throw), then count the references (it cannot)
+    auto& added = bm->seqs.emplace(child, std::move(copy)).first->second;
+    for (int32_t b : added.blocks) ++bm->refcount[(size_t)b];
+    return PA_OK;
+  });
 }
 
 pa_status_t pa_bm_append(pa_block_manager* bm, int64_t seq, int32_t num_tokens, int64_t* slots) {
   if (!bm) return PA_ERR_NULL;
-  auto it = bm->seqs.find(seq);
-  if (it == bm->seqs.end()) return PA_ERR_STATE;
-  if (num_tokens < 0) return PA_ERR_SHAPE;
-  if (num_tokens == 0) return PA_OK;
-  if (!slots) return PA_ERR_NULL;
-  auto& s = it->second;
-  const int64_t bs = bm->block_size;
-  const int64_t n = s.length, end = n + num_tokens;
-  if ((end + bs - 1) / bs > bm->capacity) return PA_ERR_SHAPE;
-  if (bm->needed(s, num_tokens) > (int64_t)bm->free_stack.size()) return PA_ERR_OUT_OF_BLOCKS;
-  if (n % bs != 0 && bm->refcount[(size_t)s.blocks.back()] > 1) {  // copy-on-write
-    const int32_t src = s.blocks.back();
-    const int32_t dst = bm->take();
-    --bm->refcount[(size_t)src];
-    s.blocks.back() = dst;
-    bm->copies.push_back(src);
-    bm->copies.push_back(dst);
-  }
-  for (int64_t p = n; p < end; ++p) {
-    if (p % bs == 0) s.blocks.push_back(bm->take());
-    slots[p - n] = (int64_t)s.blocks[(size_t)(p / bs)] * bs + p % bs;
-  }
-  s.length = end;
-  return PA_OK;
+  return guarded([&] {
+    auto it = bm->seqs.find(seq);
+    if (it == bm->seqs.end()) return PA_ERR_STATE;
+    if (num_tokens < 0) return PA_ERR_SHAPE;
+    if (num_tokens == 0) return PA_OK;
+    if (!slots) return PA_ERR_NULL;
+    auto& s = it->second;
+    const int64_t bs = bm->block_size;
+    const int64_t n = s.length, end = n + num_tokens;
+    const int64_t nb_end = (end + bs - 1) / bs;
+    if (nb_end > bm->capacity) return PA_ERR_SHAPE;
+    const int64_t need = bm->needed(s, num_tokens);
+    if (need > bm->num_free()) return PA_ERR_OUT_OF_BLOCKS;
+    const bool cow = n % bs != 0 && bm->refcount[(size_t)s.blocks.back()] > 1;
+    // everything that may allocate, before anything changes
+    room_for(s.blocks, (size_t)nb_end);
+    room_for(bm->refcount, (size_t)(bm->fresh + need));
+    if (cow) room_for(bm->copies, bm->copies.size() + 2);
+    if (cow) {  // copy-on-write of the shared, partly filled last block
+      const int32_t src = s.blocks.back();
+      const int32_t dst = bm->take();
+      --bm->refcount[(size_t)src];
+      s.blocks.back() = dst;
+      bm->copies.push_back(src);
+      bm->copies.push_back(dst);
+    }
+    for (int64_t p = n; p < end; ++p) {
+      if (p % bs == 0) s.blocks.push_back(bm->take());
+      slots[p - n] = (int64_t)s.blocks[(size_t)(p / bs)] * bs + p % bs;
+    }
+    s.length = end;
+    return PA_OK;
+  });
 }
 
 pa_status_t pa_bm_free(pa_block_manager* bm, int64_t seq) {
   if (!bm) return PA_ERR_NULL;
-  auto it = bm->seqs.find(seq);
-  if (it == bm->seqs.end()) return PA_ERR_STATE;
-  const auto& blocks = it->second.blocks;
-  for (auto b = blocks.rbegin(); b != blocks.rend(); ++b)
-    if (--bm->refcount[(size_t)*b] == 0) bm->free_stack.push_back(*b);
-  bm->seqs.erase(it);
-  return PA_OK;
+  return guarded([&] {
+    auto it = bm->seqs.find(seq);
+    if (it == bm->seqs.end()) return PA_ERR_STATE;
+    const auto& blocks = it->second.blocks;
+    room_for(bm->free_stack, bm->free_stack.size() + blocks.size());
+    for (auto b = blocks.rbegin(); b != blocks.rend(); ++b)
+      if (--bm->refcount[(size_t)*b] == 0) bm->free_stack.push_back(*b);
+    bm->seqs.erase(it);
+    return PA_OK;
+  });
 }
 
-int64_t pa_bm_num_free(const pa_block_manager* bm) {
-  return bm ? (int64_t)bm->free_stack.size() : -1;
-}
+int64_t pa_bm_num_free(const pa_block_manager* bm) { return bm ? bm->num_free() : -1; }
 
 int64_t pa_bm_length(const pa_block_manager* bm, int64_t seq) {
   if (!bm) return -1;
@@ -147,7 +203,7 @@ int64_t pa_bm_blocks_needed(const pa_block_manager* bm, int64_t seq, int32_t num
 
 int32_t pa_bm_refcount(const pa_block_manager* bm, int64_t block) {
   if (!bm || block < 0 || block >= bm->num_blocks) return -1;
-  return bm->refcount[(size_t)block];
+  return block < bm->fresh ? bm->refcount[(size_t)block] : 0;
 }
 
 int32_t pa_bm_table(const pa_block_manager* bm, int64_t seq, int32_t* out, int32_t capacity) {
@@ -169,9 +225,9 @@ pa_status_t pa_bm_tables(const pa_block_manager* bm, const int64_t* seqs, int32_
   if (num_seqs == 0) return PA_OK;
   if (!seqs || !tables || !context_lens) return PA_ERR_NULL;
   for (int32_t i = 0; i < num_seqs; ++i)
-    if (!bm->seqs.count(seqs[i])) return PA_ERR_STATE;
+    if (bm->seqs.find(seqs[i]) == bm->seqs.end()) return PA_ERR_STATE;
   for (int32_t i = 0; i < num_seqs; ++i) {
-    const auto& s = bm->seqs.at(seqs[i]);
+    const auto& s = bm->seqs.find(seqs[i])->second;
     int32_t* row = tables + (int64_t)i * row_stride;
     const size_t nb = s.blocks.size();
     std::copy(s.blocks.begin(), s.blocks.end(), row);
@@ -183,14 +239,20 @@ pa_status_t pa_bm_tables(const pa_block_manager* bm, const int64_t* seqs, int32_
 
 int64_t pa_bm_take_copies(pa_block_manager* bm, int64_t* pairs, int64_t max_pairs) {
   if (!bm || !pairs || max_pairs <= 0) return 0;
-  std::unordered_set<int64_t> written, read;
+  // The run's earlier pairs are in pairs[] already; a pair joins the run only
+  // if it neither reads nor writes a block an earlier pair writes, and does
+  // not write a block an earlier pair reads. (A linear scan: runs are as long
+  // as one step's copy-on-write events, and nothing here allocates.)
   int64_t taken = 0;
   size_t i = bm->copies_head;
   while (i + 1 < bm->copies.size() && taken < max_pairs) {
     const int64_t src = bm->copies[i], dst = bm->copies[i + 1];
-    if (written.count(src) || written.count(dst) || read.count(dst)) break;
-    written.insert(dst);
-    read.insert(src);
+    bool clash = false;
+    for (int64_t k = 0; k < taken && !clash; ++k) {
+      const int64_t rs = pairs[2 * k], wd = pairs[2 * k + 1];
+      clash = src == wd || dst == wd || dst == rs;
+    }
+    if (clash) break;
     pairs[2 * taken] = src;
     pairs[2 * taken + 1] = dst;
     ++taken;

@@ -1,7 +1,8 @@
 // Continuous-batching step driver (declared in include/pa_engine.h): plans an
 // iteration with the native scheduler and enqueues its device work through
 // the library's own entry points; decode-only iterations are one launch of a
-// captured HIP graph.
+// captured HIP graph. No C++ exception leaves an entry point: a failed host
+// allocation is PA_ERR_NOMEM.
 
 #include "pa_engine.h"
 
@@ -114,16 +115,10 @@ void release(pa_engine* e) {
   if (e->sched) pa_sched_destroy(e->sched);
 }
 
-}  // namespace
-
-extern "C" {
-
-pa_status_t pa_engine_create(const pa_engine_config* cfg, const pa_engine_buffers* b,
-                             const int32_t* prompt_lens, const int32_t* output_lens,
-                             int32_t num_requests, void* stream, pa_engine** out) {
-  if (!out) return PA_ERR_NULL;
-  *out = nullptr;
-  if (!cfg || !b) return PA_ERR_NULL;
+// Fills a new engine e; on failure the caller releases and deletes it.
+pa_status_t create_impl(const pa_engine_config* cfg, const pa_engine_buffers* b,
+                        const int32_t* prompt_lens, const int32_t* output_lens,
+                        int32_t num_requests, void* stream, pa_engine* e) {
   const int L = cfg->num_layers;
   if (L <= 0 || cfg->num_q_heads <= 0 || cfg->num_kv_heads <= 0 || cfg->head_dim <= 0)
     return PA_ERR_SHAPE;
@@ -131,7 +126,6 @@ pa_status_t pa_engine_create(const pa_engine_config* cfg, const pa_engine_buffer
                          b->k_dec, b->v_dec, b->q_pre, b->k_pre, b->v_pre})
     if (!a) return PA_ERR_NULL;
   if (!b->out_dec || !b->out_pre) return PA_ERR_NULL;
-  auto* e = new pa_engine();
   e->cfg = *cfg;
   e->stream = static_cast<hipStream_t>(stream);
   auto take = [L](void* const* a, std::vector<void*>& v) { v.assign(a, a + L); };
@@ -149,10 +143,7 @@ pa_status_t pa_engine_create(const pa_engine_config* cfg, const pa_engine_buffer
   e->op.assign(b->out_pre, b->out_pre + L);
   const pa_sched_config& s = cfg->sched;
   pa_status_t status = pa_sched_create(&s, prompt_lens, output_lens, num_requests, &e->sched);
-  if (status != PA_OK) {
-    delete e;
-    return status;
-  }
+  if (status != PA_OK) return status;
   e->B = s.max_batch;
   e->MB = s.max_blocks_per_seq;
   e->C = s.chunk_tokens;
@@ -196,38 +187,12 @@ pa_status_t pa_engine_create(const pa_engine_config* cfg, const pa_engine_buffer
     if (status == PA_OK) status = capture(e);
   }
   if (status == PA_OK) status = hip_ok(hipStreamSynchronize(e->stream));
-  if (status != PA_OK) {
-    release(e);
-    delete e;
-    return status;
-  }
-  *out = e;
-  return PA_OK;
+  return status;
 }
 
-void pa_engine_destroy(pa_engine* e) {
-  if (!e) return;
-  (void)hipStreamSynchronize(e->stream);
-  release(e);
-  delete e;
-}
 
-int32_t pa_engine_done(const pa_engine* e) { return e ? pa_sched_done(e->sched) : 0; }
-int64_t pa_engine_iterations(const pa_engine* e) { return e ? e->iterations : -1; }
-int64_t pa_engine_graph_launches(const pa_engine* e) { return e ? e->graph_launches : -1; }
-
-pa_status_t pa_engine_plan(pa_engine* e, pa_step_plan* plan) {
-  if (!e || !plan) return PA_ERR_NULL;
-  PA_TRY(pa_sched_step(e->sched, &e->plan));
-  e->planned = true;
-  *plan = e->plan;
-  return PA_OK;
-}
-
-pa_status_t pa_engine_execute(pa_engine* e) {
-  if (!e) return PA_ERR_NULL;
-  if (!e->planned) return PA_ERR_STATE;
-  e->planned = false;
+// The device work of the pending plan.
+pa_status_t execute_impl(pa_engine* e) {
   const pa_step_plan& p = e->plan;
   const auto& c = e->cfg;
   const auto& s = c.sched;
@@ -344,6 +309,66 @@ pa_status_t pa_engine_execute(pa_engine* e) {
   st.used = true;
   ++e->iterations;
   return PA_OK;
+}
+
+
+}  // namespace
+
+extern "C" {
+
+pa_status_t pa_engine_create(const pa_engine_config* cfg, const pa_engine_buffers* b,
+                             const int32_t* prompt_lens, const int32_t* output_lens,
+                             int32_t num_requests, void* stream, pa_engine** out) {
+  if (!out) return PA_ERR_NULL;
+  *out = nullptr;
+  if (!cfg || !b) return PA_ERR_NULL;
+  pa_engine* e = nullptr;
+  pa_status_t status = PA_OK;
+  try {
+    e = new pa_engine();
+    status = create_impl(cfg, b, prompt_lens, output_lens, num_requests, stream, e);
+  } catch (...) {
+    status = PA_ERR_NOMEM;
+  }
+  if (status != PA_OK) {
+    if (e) {
+      release(e);
+      delete e;
+    }
+    return status;
+  }
+  *out = e;
+  return PA_OK;
+}
+
+void pa_engine_destroy(pa_engine* e) {
+  if (!e) return;
+  (void)hipStreamSynchronize(e->stream);
+  release(e);
+  delete e;
+}
+
+int32_t pa_engine_done(const pa_engine* e) { return e ? pa_sched_done(e->sched) : 0; }
+int64_t pa_engine_iterations(const pa_engine* e) { return e ? e->iterations : -1; }
+int64_t pa_engine_graph_launches(const pa_engine* e) { return e ? e->graph_launches : -1; }
+
+pa_status_t pa_engine_plan(pa_engine* e, pa_step_plan* plan) {
+  if (!e || !plan) return PA_ERR_NULL;
+  PA_TRY(pa_sched_step(e->sched, &e->plan));
+  e->planned = true;
+  *plan = e->plan;
+  return PA_OK;
+}
+
+pa_status_t pa_engine_execute(pa_engine* e) {
+  if (!e) return PA_ERR_NULL;
+  if (!e->planned) return PA_ERR_STATE;
+  e->planned = false;
+  try {
+    return execute_impl(e);
+  } catch (...) {
+    return PA_ERR_NOMEM;
+  }
 }
 
 }  // extern "C"

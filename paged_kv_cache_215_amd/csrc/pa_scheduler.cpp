@@ -3,6 +3,13 @@
 // for the device pool and a stack of host blocks for the swap space, and
 // writes each iteration's plan (decode batch, prefill chunks, swap copies)
 // into buffers it owns.
+//
+// The host swap space is held lazily, like the block manager's pool: blocks
+// [host_fresh, num_host_blocks) were never handed out and are taken in
+// increasing order, below the stack of returned ones. No C++ exception leaves
+// this file: an allocation that fails inside pa_sched_step leaves the
+// scheduler unusable (every later step returns PA_ERR_STATE), and one inside
+// pa_sched_create frees what was made; both return PA_ERR_NOMEM.
 
 #include "pa_sched.h"
 
@@ -25,10 +32,12 @@ struct pa_scheduler {
   std::vector<int64_t> batch;                 // admission order
   std::deque<int64_t> swapped;                // oldest preemption first
   std::vector<std::vector<int64_t>> host_of;  // host blocks of a swapped sequence
-  std::vector<int64_t> host_free;             // stack, top = back
+  std::vector<int64_t> host_free;             // returned host blocks, top = back
+  int64_t host_fresh = 0;                     // host blocks [host_fresh, num_host_blocks) never used
   int64_t next_waiting = 0;
   int64_t finished_count = 0;
   int32_t iteration = 0;
+  bool broken = false;                        // a step failed half way
   std::vector<int32_t> table_buf;
 
   // plan buffers
@@ -38,10 +47,34 @@ struct pa_scheduler {
   int64_t blocks_for(int64_t tokens) const {
     return (tokens + cfg.block_size - 1) / cfg.block_size;
   }
+  int64_t host_free_count() const {
+    return (int64_t)host_free.size() + (cfg.num_host_blocks - host_fresh);
+  }
+  int64_t take_host() {
+    if (host_free.empty()) return host_fresh++;
+    const int64_t h = host_free.back();
+    host_free.pop_back();
+    return h;
+  }
+  // seq's table in table_buf (grown to the table's length); its block count
   int32_t table(int64_t seq) {
+    const int32_t nb = pa_bm_table(bm, seq, nullptr, 0);
+    if (nb > (int32_t)table_buf.size()) table_buf.resize((size_t)nb);
     return pa_bm_table(bm, seq, table_buf.data(), (int32_t)table_buf.size());
   }
 };
+
+namespace {
+
+// A block-manager call the plan relies on. The scheduler's own checks rule
+// out every failure but a failed allocation; any failure abandons the step.
+void must(pa_status_t st) {
+  if (st != PA_OK) throw st;
+}
+
+pa_status_t step_impl(pa_scheduler* s, pa_step_plan* plan);
+
+}  // namespace
 
 extern "C" {
 
@@ -52,30 +85,32 @@ pa_status_t pa_sched_create(const pa_sched_config* cfg, const int32_t* prompt_le
   *out = nullptr;
   if (!cfg) return PA_ERR_NULL;
   if (num_requests < 0 || cfg->num_blocks <= 0 || cfg->num_host_blocks < 0 ||
-      cfg->block_size <= 0 || cfg->max_blocks_per_seq <= 0 || cfg->max_batch <= 0 ||
-      cfg->chunk_tokens <= 0)
+      cfg->num_host_blocks > INT32_MAX || cfg->block_size <= 0 || cfg->max_blocks_per_seq <= 0 ||
+      cfg->max_batch <= 0 || cfg->chunk_tokens <= 0)
     return PA_ERR_SHAPE;
   if (num_requests > 0 && (!prompt_lens || !output_lens)) return PA_ERR_NULL;
   for (int32_t i = 0; i < num_requests; ++i)
     if (prompt_lens[i] < 1 || output_lens[i] < 1) return PA_ERR_SHAPE;
-  auto* s = new pa_scheduler();
-  s->cfg = *cfg;
-  const pa_status_t st =
-      pa_bm_create(cfg->num_blocks, cfg->block_size, cfg->max_blocks_per_seq, &s->bm);
-  if (st != PA_OK) {
-    delete s;
-    return st;
+  pa_scheduler* s = nullptr;
+  try {
+    s = new pa_scheduler();
+    s->cfg = *cfg;
+    const pa_status_t st =
+        pa_bm_create(cfg->num_blocks, cfg->block_size, cfg->max_blocks_per_seq, &s->bm);
+    if (st != PA_OK) {
+      delete s;
+      return st;
+    }
+    s->prompt.assign(prompt_lens, prompt_lens + num_requests);
+    s->output.assign(output_lens, output_lens + num_requests);
+    s->prefilled.assign((size_t)num_requests, 0);
+    s->generated.assign((size_t)num_requests, 0);
+    s->state.assign((size_t)num_requests, State::Waiting);
+    s->host_of.resize((size_t)num_requests);
+  } catch (...) {
+    pa_sched_destroy(s);
+    return PA_ERR_NOMEM;
   }
-  s->prompt.assign(prompt_lens, prompt_lens + num_requests);
-  s->output.assign(output_lens, output_lens + num_requests);
-  s->prefilled.assign((size_t)num_requests, 0);
-  s->generated.assign((size_t)num_requests, 0);
-  s->state.assign((size_t)num_requests, State::Waiting);
-  s->host_of.resize((size_t)num_requests);
-  s->host_free.resize((size_t)cfg->num_host_blocks);
-  for (int64_t i = 0; i < cfg->num_host_blocks; ++i)
-    s->host_free[(size_t)i] = cfg->num_host_blocks - 1 - i;
-  s->table_buf.resize((size_t)cfg->max_blocks_per_seq);
   *out = s;
   return PA_OK;
 }
@@ -94,6 +129,23 @@ const pa_block_manager* pa_sched_blocks(const pa_scheduler* s) { return s ? s->b
 
 pa_status_t pa_sched_step(pa_scheduler* s, pa_step_plan* plan) {
   if (!s || !plan) return PA_ERR_NULL;
+  if (s->broken) return PA_ERR_STATE;
+  try {
+    return step_impl(s, plan);
+  } catch (pa_status_t st) {
+    s->broken = true;
+    return st;
+  } catch (...) {
+    s->broken = true;
+    return PA_ERR_NOMEM;
+  }
+}
+
+}  // extern "C"
+
+namespace {
+
+pa_status_t step_impl(pa_scheduler* s, pa_step_plan* plan) {
   for (auto* v : {&s->d_seqs, &s->d_slots, &s->p_seqs, &s->p_slots, &s->s_out, &s->s_in,
                   &s->fin, &s->adm, &s->pre, &s->res})
     v->clear();
@@ -108,7 +160,7 @@ pa_status_t pa_sched_step(pa_scheduler* s, pa_step_plan* plan) {
   for (size_t i = 0; i < s->batch.size();) {
     const int64_t q = s->batch[i];
     if (s->state[q] == State::Running && s->generated[q] == s->output[q]) {
-      pa_bm_free(bm, q);
+      must(pa_bm_free(bm, q));
       s->state[q] = State::Finished;
       ++s->finished_count;
       s->fin.push_back(q);
@@ -125,9 +177,9 @@ pa_status_t pa_sched_step(pa_scheduler* s, pa_step_plan* plan) {
     const int64_t length = (int64_t)s->prompt[q] + s->generated[q];
     if (pa_bm_num_free(bm) < s->blocks_for(length) + 1) break;
     s->swapped.pop_front();
-    pa_bm_add(bm, q);
+    must(pa_bm_add(bm, q));
     slots_tmp.resize((size_t)length);
-    pa_bm_append(bm, q, (int32_t)length, slots_tmp.data());
+    must(pa_bm_append(bm, q, (int32_t)length, slots_tmp.data()));
     const int32_t nb = s->table(q);
     auto& hosts = s->host_of[q];
     for (int32_t j = 0; j < nb; ++j) {
@@ -146,9 +198,9 @@ pa_status_t pa_sched_step(pa_scheduler* s, pa_step_plan* plan) {
          (int64_t)s->batch.size() < s->cfg.max_batch) {
     const int64_t q = s->next_waiting;
     if (pa_bm_num_free(bm) < s->blocks_for((int64_t)s->prompt[q] + 1)) break;
-    pa_bm_add(bm, q);
+    must(pa_bm_add(bm, q));
     slots_tmp.resize((size_t)s->prompt[q]);
-    pa_bm_append(bm, q, s->prompt[q], slots_tmp.data());
+    must(pa_bm_append(bm, q, s->prompt[q], slots_tmp.data()));
     s->state[q] = State::Prefilling;
     s->batch.push_back(q);
     ++s->next_waiting;
@@ -188,19 +240,18 @@ pa_status_t pa_sched_step(pa_scheduler* s, pa_step_plan* plan) {
     const int64_t v = runners.back();
     runners.pop_back();
     const int32_t nb = s->table(v);
-    if ((int64_t)s->host_free.size() < nb) {
+    if (s->host_free_count() < nb) {
       status = PA_ERR_OUT_OF_BLOCKS;
       break;
     }
     auto& hosts = s->host_of[v];
     for (int32_t j = 0; j < nb; ++j) {
-      const int64_t h = s->host_free.back();
-      s->host_free.pop_back();
+      const int64_t h = s->take_host();
       hosts.push_back(h);
       s->s_out.push_back(s->table_buf[(size_t)j]);
       s->s_out.push_back(h);
     }
-    pa_bm_free(bm, v);
+    must(pa_bm_free(bm, v));
     s->state[v] = State::Swapped;
     s->batch.erase(std::find(s->batch.begin(), s->batch.end(), v));
     s->swapped.push_back(v);
@@ -209,7 +260,7 @@ pa_status_t pa_sched_step(pa_scheduler* s, pa_step_plan* plan) {
   if (status == PA_OK) {
     for (const int64_t q : runners) {
       int64_t slot = 0;
-      pa_bm_append(bm, q, 1, &slot);
+      must(pa_bm_append(bm, q, 1, &slot));
       ++s->generated[q];
       s->d_seqs.push_back(q);
       s->d_slots.push_back(slot);
@@ -243,4 +294,4 @@ pa_status_t pa_sched_step(pa_scheduler* s, pa_step_plan* plan) {
   return status;
 }
 
-}  // extern "C"
+}  // namespace
