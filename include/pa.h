@@ -110,20 +110,27 @@ pa_status_t pa_reshape_and_cache(const void* key, const void* value,
                                  void* stream);
 
 /*
- * Bytes of device workspace pa_decode needs for these sizes (a small header
- * holding the work-queue counter, then split-context partial results).
- * Depends only on the arguments; 0 never occurs for positive sizes. Returns 0
- * for arguments pa_decode would reject.
+ * Bytes of device workspace pa_decode needs for these sizes: a 256-byte head
+ * (plan summary and work-queue counters), then split-context partial results.
+ * The partials are bounded by the batch, not by max_context_len alone: about
+ * one slot per sequence plus a fixed spare of 2048 (per query head, head_dim
+ * + 2 floats each), unless the largest partitions (8192 tokens) need more;
+ * capped by the slots of 256-token partitions. Depends only on the
+ * arguments; 0 never occurs for positive sizes. Returns 0 for arguments
+ * pa_decode would reject.
  */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                 int32_t num_kv_heads, int32_t head_dim,
                                 int32_t block_size, int32_t max_context_len);
 
 /*
- * Zero-fills a decode workspace on `stream` (a fill kernel, so it can be
- * captured in a graph). A workspace must be zero-filled once before its first
- * pa_decode; every pa_decode leaves it ready for the next call. Any zero fill
- * (for example a buffer allocated zeroed) serves equally.
+ * Zero-fills the head of a decode workspace (its first 256 bytes, or all of
+ * it if smaller) on `stream`, with a fill kernel so that it can be captured
+ * in a graph. A workspace must be initialised once before its first
+ * pa_decode; every pa_decode leaves the head at zero again (the last
+ * partition workgroup resets the counters), whatever happens to later
+ * launches. Any zero fill (for example a buffer allocated zeroed) serves
+ * equally.
  */
 pa_status_t pa_decode_workspace_init(void* workspace, size_t workspace_bytes,
                                      void* stream);
@@ -140,10 +147,13 @@ pa_status_t pa_decode_workspace_init(void* workspace, size_t workspace_bytes,
  * float32; out is float32 and fully overwritten (never read).
  *   query           [num_seqs, num_q_heads, head_dim], element type dtype
  *   workspace       device buffer of at least pa_decode_workspace_size(...)
- *                   bytes, zero-filled before its first use (see
+ *                   bytes, initialised before its first use (see
  *                   pa_decode_workspace_init) and then left to the library
- *                   between calls. A workspace that was never zero-filled
- *                   gives wrong results but no out-of-bounds access.
+ *                   between calls. Its head holds a work-queue counter that
+ *                   the call takes with atomics and sets back to zero, so two
+ *                   calls that overlap on one workspace race (stream order
+ *                   is fine). A workspace that was never initialised gives
+ *                   wrong results but no out-of-bounds access.
  *   max_context_len upper bound of context_lens (sizes the launch grid).
  * dtype: PA_DTYPE_F32 or PA_DTYPE_BF16 for query and both caches.
  */

@@ -49,6 +49,7 @@ int32_t ctx_limit(int32_t max_ctx, int32_t max_blocks, int32_t bs) {
 
 struct DecodeGeometry {
   pa::DecodeLaunch launch;
+  size_t full_pre_off;
   size_t part_o_off;
   size_t part_ml_off;
   size_t bytes;
@@ -56,15 +57,19 @@ struct DecodeGeometry {
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Workspace: plan summary | partial outputs | partial (m, l). Launches of at
-// most 4096 sequences each reuse it in stream order.
+// Workspace: plan summary and work-queue counters (256 bytes) | first slot of
+// each sequence's partitions | partial outputs | partial (m, l). Launches of
+// at most 4096 sequences each reuse it in stream order.
+constexpr size_t kDecodeHeadBytes = 256;
+
 DecodeGeometry decode_geometry(int32_t num_seqs, int32_t hq, int32_t hkv, int32_t d, int32_t bs,
                                int32_t max_ctx) {
   DecodeGeometry g;
   g.launch = pa::decode_launch_shape(num_seqs, hkv, bs, max_ctx);
   const size_t seqs = num_seqs < 4096 ? (size_t)num_seqs : 4096;
-  const size_t rows = seqs * hq * g.launch.max_parts;
-  g.part_o_off = 256;
+  const size_t rows = (size_t)g.launch.unit_slots * hq;
+  g.full_pre_off = kDecodeHeadBytes;
+  g.part_o_off = round_up(g.full_pre_off + seqs * sizeof(int32_t), 256);
   g.part_ml_off = round_up(g.part_o_off + rows * d * sizeof(float), 256);
   g.bytes = round_up(g.part_ml_off + rows * 2 * sizeof(float), 256);
   return g;
@@ -156,7 +161,8 @@ pa_status_t decode_impl(float* out, const void* query, const void* key_cache,
       !supported_group(num_q_heads, num_kv_heads) || !type_ok)
     return PA_ERR_UNSUPPORTED;
   if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) ||
-      !aligned(value_cache, 16) || !aligned(workspace, 16) || !aligned(block_tables, 4) ||
+      !aligned(value_cache, 16) || !aligned(workspace, 16) ||
+      !aligned(block_tables, 4) ||
       !aligned(context_lens, 4) || (scaled && (!aligned(k_scale, 4) || !aligned(v_scale, 4))))
     return PA_ERR_ALIGN;
   const DecodeGeometry geo = decode_geometry(num_seqs, num_q_heads, num_kv_heads, head_dim,
@@ -172,6 +178,7 @@ pa_status_t decode_impl(float* out, const void* query, const void* key_cache,
   a.plan_units_unshared = 0;
   a.part_o = reinterpret_cast<float*>(ws + geo.part_o_off);
   a.part_ml = reinterpret_cast<float*>(ws + geo.part_ml_off);
+  a.full_pre = reinterpret_cast<int*>(ws + geo.full_pre_off);
   a.query = query;
   a.key_cache = key_cache;
   a.value_cache = value_cache;
@@ -280,7 +287,10 @@ pa_status_t pa_decode_workspace_init(void* workspace, size_t workspace_bytes, vo
   if (workspace_bytes == 0) return PA_OK;
   if (!workspace) return PA_ERR_NULL;
   if (!aligned(workspace, 16)) return PA_ERR_ALIGN;
-  return from_hip(pa::launch_zero_fill(workspace, workspace_bytes & ~(size_t)15,
+  // only the head (the work-queue counters) has to start at zero: partials are
+  // always written before they are read
+  const size_t n = workspace_bytes < kDecodeHeadBytes ? workspace_bytes : kDecodeHeadBytes;
+  return from_hip(pa::launch_zero_fill(workspace, n & ~(size_t)15,
                                        static_cast<hipStream_t>(stream)));
 }
 

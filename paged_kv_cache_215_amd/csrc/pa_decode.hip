@@ -269,7 +269,8 @@ struct PlanLds {
   int red_a[16], red_b[16], red_c[16], red_d[16];
   int part_tokens, full_total, max_nparts;
   int ranked;                 // tail_order holds the order (else: sequence order)
-  int shared;                 // some sequence starts on the block of the one before
+  int shared;                 // at least half of the live sequences start on their
+                              // predecessor's first block (copy-on-write rollouts)
   int ticket;                 // this workgroup's current unit
 };
 
@@ -459,6 +460,76 @@ __device__ __forceinline__ int2 plan_unit(const PlanLds& pl, int S, int e) {
   return make_int2(lo, e - pl.full_pre[lo]);
 }
 
+// The plan summary the merge kernel needs, written by workgroup 0: partition
+// size, largest partition count, and (only when some sequence has several
+// partitions) where each sequence's partial slots start.
+template <int NT>
+__device__ __forceinline__ void publish_plan(const DecodeArgs& a, const PlanLds& pl) {
+  if (blockIdx.x != 0) return;
+  if (threadIdx.x == 0) {
+    a.plan->part_tokens = pl.part_tokens;
+    a.plan->max_nparts = pl.max_nparts;
+    a.plan->full_total = pl.full_total;
+  }
+  if (pl.max_nparts > 1)
+    for (int b = threadIdx.x; b < a.num_seqs; b += NT) a.full_pre[b] = pl.full_pre[b];
+}
+
+// Partial slot of (sequence, partition, query head): full partitions take
+// slots [0, full_total) in plan order, a sequence's last partition slot
+// full_total + seq; each slot holds one row per query head.
+__device__ __forceinline__ int64_t partial_slot(const DecodeArgs& a, const PlanLds& pl, int seq,
+                                                int part, int nparts, int head) {
+  const int e = part < nparts - 1 ? pl.full_pre[seq] + part : pl.full_total + seq;
+  return (int64_t)e * a.num_q_heads + head;
+}
+
+// Persistent loop over the plan's units, shared by the partition kernels.
+// Full partitions (all of one size) go round-robin, so the grid walks them in
+// lockstep rounds: sequences that share prompt blocks (copy-on-write rollouts
+// are consecutive) read those blocks at about the same time. The last
+// partitions, whose sizes are ragged, are then taken from the ticket counter
+// in the workspace head so that they balance across CUs. The last workgroup
+// to leave the queue sets the counters back to zero for the next call (every
+// other workgroup has taken its last ticket by then), so a workspace is left
+// ready whatever happens to later launches. `keep` selects ordinary rather
+// than nontemporal K/V loads for a batch that shares blocks;
+// unit(seq, kvh, part, tag) runs one unit with the load kind as a type tag.
+template <int KvBytes, typename Unit>
+__device__ __forceinline__ void run_units(const DecodeArgs& a, PlanLds& pl, bool keep,
+                                          Unit&& unit) {
+  const int tid = threadIdx.x;
+  const int n_full = pl.full_total * a.num_kv_heads;
+  const int n_units = (pl.full_total + a.num_seqs) * a.num_kv_heads;
+  for (int u = blockIdx.x; u < n_full; u += gridDim.x) {
+    const int2 e = plan_unit(pl, a.num_seqs, u / a.num_kv_heads);
+    if (keep) unit(e.x, u % a.num_kv_heads, e.y, std::true_type{});
+    else unit(e.x, u % a.num_kv_heads, e.y, std::false_type{});
+    __syncthreads();  // LDS is reused by the next unit
+  }
+  for (;;) {
+    if (tid == 0) pl.ticket = atomicAdd(&a.plan->ticket, 1);
+    __syncthreads();
+    const int u = n_full + pl.ticket;
+    __syncthreads();  // every thread has read the ticket before it is reused
+    if (u < n_full || u >= n_units) break;  // (below n_full: workspace never zero-filled)
+    const int2 e = plan_unit(pl, a.num_seqs, u / a.num_kv_heads);
+    // last partitions are private tails even in a shared batch: nontemporal
+    // for BF16 / float32 caches (shared-prompt batch 245 -> 231 us), ordinary
+    // for E4M3 ones, which measured faster that way (146 vs 154 us)
+    if (KvBytes == 1 && keep) unit(e.x, u % a.num_kv_heads, e.y, std::true_type{});
+    else unit(e.x, u % a.num_kv_heads, e.y, std::false_type{});
+    __syncthreads();
+  }
+  if (tid == 0) {
+    __threadfence();  // this workgroup's last ticket is taken before it counts itself out
+    if (atomicAdd(&a.plan->done, 1) == (int)gridDim.x - 1) {
+      atomicExch(&a.plan->ticket, 0);
+      atomicExch(&a.plan->done, 0);
+    }
+  }
+}
+
 template <typename T, int D, int G, int NW>
 __global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(DecodeArgs a) {
   using S = DecodeShape<T, D, G>;
@@ -481,10 +552,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(DecodeArgs
   const int P = s_plan.part_tokens;
   // blocks shared between sequences: K/V through ordinary loads (see load_kv)
   const bool keep = __builtin_amdgcn_readfirstlane(s_plan.shared) != 0;
-  if (blockIdx.x == 0 && tid == 0) {  // for the merge kernel
-    a.plan->part_tokens = P;
-    a.plan->max_nparts = s_plan.max_nparts;
-  }
+  publish_plan<kThreads>(a, s_plan);
 
   // One work unit: (sequence, KV head, partition) of the plan.
   auto unit = [&](const int seq, const int kvh, const int part, auto keep_tag) {
@@ -799,7 +867,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(DecodeArgs
     if (nparts == 1) {
       reinterpret_cast<float4*>(a.out)[head * (D / 4) + d4] = o;
     } else {
-      const int64_t slot = head * a.max_parts + part;
+      const int64_t slot = partial_slot(a, s_plan, seq, part, nparts, kvh * G + g);
       reinterpret_cast<float4*>(a.part_o)[slot * (D / 4) + d4] = o;
       if (d4 == 0) {
         a.part_ml[2 * slot] = M;
@@ -809,34 +877,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(DecodeArgs
   }
   };  // unit
 
-  // Persistent loop. Full partitions (all of one size) go round-robin, so the
-  // grid walks them in lockstep rounds: sequences that share prompt blocks
-  // (copy-on-write rollouts are consecutive) read those blocks at about the
-  // same time. The last partitions, whose sizes are ragged, are then taken
-  // from the ticket counter in the workspace head so they balance across CUs;
-  // the merge kernel, which follows in stream order, resets the counter.
-  const int n_full = s_plan.full_total * a.num_kv_heads;
-  const int n_units = (s_plan.full_total + a.num_seqs) * a.num_kv_heads;
-  for (int u = blockIdx.x; u < n_full; u += gridDim.x) {
-    const int2 e = plan_unit(s_plan, a.num_seqs, u / a.num_kv_heads);
-    if (keep) unit(e.x, u % a.num_kv_heads, e.y, std::true_type{});
-    else unit(e.x, u % a.num_kv_heads, e.y, std::false_type{});
-    __syncthreads();  // LDS is reused by the next unit
-  }
-  for (;;) {
-    if (tid == 0) s_plan.ticket = atomicAdd(&a.plan->ticket, 1);
-    __syncthreads();
-    const int u = n_full + s_plan.ticket;
-    __syncthreads();  // every thread has read the ticket before it is reused
-    if (u < n_full || u >= n_units) break;  // (below n_full: workspace never zero-filled)
-    const int2 e = plan_unit(s_plan, a.num_seqs, u / a.num_kv_heads);
-    // last partitions are private tails even in a shared batch: nontemporal
-    // for BF16 / float32 caches (shared-prompt batch 245 -> 231 us), ordinary
-    // for E4M3 ones, which measured faster that way (146 vs 154 us)
-    if (T::kBytes == 1 && keep) unit(e.x, u % a.num_kv_heads, e.y, std::true_type{});
-    else unit(e.x, u % a.num_kv_heads, e.y, std::false_type{});
-    __syncthreads();
-  }
+  run_units<T::kBytes>(a, s_plan, keep, unit);
 }
 
 // ---------------------------------------------------------------------------
@@ -902,10 +943,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeArgs a) {
   const int P = s_plan.part_tokens;
   // blocks shared between sequences: K/V through ordinary loads (see load_kv)
   const bool keep = __builtin_amdgcn_readfirstlane(s_plan.shared) != 0;
-  if (blockIdx.x == 0 && tid == 0) {  // for the merge kernel
-    a.plan->part_tokens = P;
-    a.plan->max_nparts = s_plan.max_nparts;
-  }
+  publish_plan<kThreads>(a, s_plan);
 
   auto unit = [&](const int seq, const int kvh, const int part, auto keep_tag) {
   constexpr bool kKeep = decltype(keep_tag)::value;
@@ -1133,7 +1171,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeArgs a) {
     if (nparts == 1) {
       reinterpret_cast<float4*>(a.out)[head * (D / 4) + d4] = o;
     } else {
-      const int64_t slot = head * a.max_parts + part;
+      const int64_t slot = partial_slot(a, s_plan, seq, part, nparts, kvh * G + g);
       reinterpret_cast<float4*>(a.part_o)[slot * (D / 4) + d4] = o;
       if (d4 == 0) {
         a.part_ml[2 * slot] = M;
@@ -1143,66 +1181,47 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeArgs a) {
   }
   };  // unit
 
-  // persistent loop: as in the VALU kernel
-  const int n_full = s_plan.full_total * a.num_kv_heads;
-  const int n_units = (s_plan.full_total + a.num_seqs) * a.num_kv_heads;
-  for (int u = blockIdx.x; u < n_full; u += gridDim.x) {
-    const int2 e = plan_unit(s_plan, a.num_seqs, u / a.num_kv_heads);
-    if (keep) unit(e.x, u % a.num_kv_heads, e.y, std::true_type{});
-    else unit(e.x, u % a.num_kv_heads, e.y, std::false_type{});
-    __syncthreads();  // LDS is reused by the next unit
-  }
-  for (;;) {
-    if (tid == 0) s_plan.ticket = atomicAdd(&a.plan->ticket, 1);
-    __syncthreads();
-    const int u = n_full + s_plan.ticket;
-    __syncthreads();  // every thread has read the ticket before it is reused
-    if (u < n_full || u >= n_units) break;  // (below n_full: workspace never zero-filled)
-    const int2 e = plan_unit(s_plan, a.num_seqs, u / a.num_kv_heads);
-    // last partitions are private tails even in a shared batch: nontemporal
-    // for BF16 / float32 caches (shared-prompt batch 245 -> 231 us), ordinary
-    // for E4M3 ones, which measured faster that way (146 vs 154 us)
-    if (T::kBytes == 1 && keep) unit(e.x, u % a.num_kv_heads, e.y, std::true_type{});
-    else unit(e.x, u % a.num_kv_heads, e.y, std::false_type{});
-    __syncthreads();
-  }
+  run_units<T::kBytes>(a, s_plan, keep, unit);
 }
 
 // Merge of the per-partition partials of one (sequence, query head):
 // out = sum_p w_p o_p / sum_p w_p with w_p = l_p * 2^(m_p - max_p m_p).
 // Persistent over rows; when the plan gave every sequence one partition the
-// partition kernel already wrote every row and the launch ends at once. It
-// also resets the partition kernel's ticket counter for the next call.
+// partition kernel already wrote every row and the launch ends at once.
 template <int D>
 __global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeArgs a) {
   constexpr int PER = D / kWave;  // 1, 2 or 4 floats per lane
-  if (blockIdx.x == 0 && threadIdx.x == 0) a.plan->ticket = 0;  // ready for the next call
   const int P = a.plan->part_tokens;
   if (a.plan->max_nparts <= 1) return;
+  const int full_total = a.plan->full_total;
   const int rows = a.num_seqs * a.num_q_heads;
   const int lane = threadIdx.x;
   for (int row = blockIdx.x; row < rows; row += gridDim.x) {
-    const int seq = row / a.num_q_heads;
+    const int seq = row / a.num_q_heads, h = row % a.num_q_heads;
     int n = a.context_lens[seq];
     n = n < 0 ? 0 : n;
     n = n > a.ctx_limit ? a.ctx_limit : n;
     const int nparts = (n + P - 1) / P;
     if (nparts <= 1) continue;  // written by the partition kernel (zeros if empty)
-    const int64_t head = row;
-    const float* ml = a.part_ml + 2 * head * a.max_parts;
+    const int first = a.full_pre[seq];
+    // slot of partition p (rows of Hq query heads per slot)
+    auto slot = [&](int p) -> int64_t {
+      const int e = p < nparts - 1 ? first + p : full_total + seq;
+      return (int64_t)e * a.num_q_heads + h;
+    };
     // lane p holds partition p's (m, l), 64 partitions per pass
     float M = -INFINITY;
-    for (int p = lane; p < nparts; p += kWave) M = fmaxf(M, ml[2 * p]);
+    for (int p = lane; p < nparts; p += kWave) M = fmaxf(M, a.part_ml[2 * slot(p)]);
 #pragma unroll
     for (int m = 1; m < kWave; m <<= 1) M = fmaxf(M, __shfl_xor(M, m));
     float o[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) o[e] = 0.f;
     float L = 0.f;
-    const float* po = a.part_o + head * a.max_parts * D + lane * PER;
     for (int p0 = 0; p0 < nparts; p0 += kWave) {
       const int p = p0 + lane;
-      const float w_lane = p < nparts ? ml[2 * p + 1] * fast_exp2(ml[2 * p] - M) : 0.f;
+      const float w_lane =
+          p < nparts ? a.part_ml[2 * slot(p) + 1] * fast_exp2(a.part_ml[2 * slot(p)] - M) : 0.f;
       L += w_lane;
       const int cnt = nparts - p0 < kWave ? nparts - p0 : kWave;
       // four partitions per step, so that their loads are in flight together
@@ -1212,9 +1231,9 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeArgs a) {
           const int j = j0 + jj;
           const float w = __shfl(w_lane, j < cnt ? j : 0);
           if (j < cnt) {
+            const float* po = a.part_o + slot(p0 + j) * D + lane * PER;
 #pragma unroll
-            for (int e = 0; e < PER; ++e)
-              o[e] = __builtin_fmaf(w, po[(int64_t)(p0 + j) * D + e], o[e]);
+            for (int e = 0; e < PER; ++e) o[e] = __builtin_fmaf(w, po[e], o[e]);
           }
         }
       }
@@ -1222,7 +1241,7 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeArgs a) {
 #pragma unroll
     for (int m = 1; m < kWave; m <<= 1) L += __shfl_xor(L, m);
     const float inv = 1.f / L;
-    float* out = a.out + head * D + lane * PER;
+    float* out = a.out + (int64_t)row * D + lane * PER;
 #pragma unroll
     for (int e = 0; e < PER; ++e) out[e] = o[e] * inv;
   }
@@ -1249,16 +1268,34 @@ hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t stream) {
 // ---------------------------------------------------------------------------
 // Host side.
 
+// Partial slots a workspace holds beyond one per sequence. The plan aims at
+// one or two units per CU; the partitions it makes stay below this many more
+// than one per sequence for any batch (and far below for 256 CUs).
+constexpr int64_t kSpareSlots = 2048;
+
 DecodeLaunch decode_launch_shape(int num_seqs, int num_kv_heads, int block_size,
                                  int max_context_len) {
-  // The plan kernel picks the partition size per call between part_floor and
-  // part_cap; the workspace is laid out for part_floor (the most partitions).
+  // The plan picks the partition size per call between part_floor and
+  // part_cap. The workspace holds unit_slots partial slots; part_floor is the
+  // smallest size (a power-of-two multiple of 256) at which every batch
+  // within max_context_len fits them: a sequence of n tokens takes
+  // max(1, ceil(n / P)) slots. unit_slots is the partition count at 256
+  // tokens, capped at a modest figure unless the largest partitions need more.
+  (void)num_kv_heads;
   DecodeLaunch r;
   r.waves = decode_waves_per_workgroup();
-  r.part_floor = 256;                                   // a multiple of 16 * 8 waves
   r.part_cap = kMaxPartBlocks * block_size < 8192 ? kMaxPartBlocks * block_size : 8192;
-  r.max_parts = (max_context_len + r.part_floor - 1) / r.part_floor;
-  if (r.max_parts < 1) r.max_parts = 1;
+  const int64_t seqs = num_seqs < kPlanSeqs ? num_seqs : kPlanSeqs;
+  const int64_t ctx = max_context_len > 1 ? max_context_len : 1;
+  auto parts_at = [&](int64_t p) { return seqs * ((ctx + p - 1) / p); };
+  const int64_t at_cap = parts_at(r.part_cap);
+  int64_t slots = seqs + kSpareSlots > at_cap ? seqs + kSpareSlots : at_cap;
+  if (parts_at(256) < slots) slots = parts_at(256);
+  r.unit_slots = slots;
+  int p = 256;  // a multiple of 16 * 8 waves
+  while (p < r.part_cap && parts_at(p) > slots) p *= 2;
+  r.part_floor = p;
+  r.max_parts = (int)((ctx + p - 1) / p);
   return r;
 }
 

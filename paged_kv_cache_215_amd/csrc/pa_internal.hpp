@@ -6,19 +6,24 @@
 
 namespace pa {
 
-// Plan summary of one decode launch, written by the partition kernel into the
-// head of the workspace for the merge kernel.
+// Head of a decode workspace: the plan summary the partition kernel writes for
+// the merge kernel, and the work-queue counters. The counters are zero between
+// calls: the last partition workgroup to leave the queue resets them.
 struct DecodePlan {
   int part_tokens;   // tokens per partition chosen for this batch
   int max_nparts;    // largest partition count of any sequence
-  int ticket;        // next unit to take; 0 between calls
-  int pad;
+  int ticket;        // next ticketed unit; 0 between calls
+  int done;          // workgroups that have left the queue; 0 between calls
+  int full_total;    // full partitions of the plan (their slots come first)
+  int pad[3];
 };
 
 struct DecodeArgs {
   float* out;            // [S, Hq, D] float32
-  float* part_o;         // [S, Hq, max_parts, D] normalised partial outputs
-  float* part_ml;        // [S, Hq, max_parts, 2] (max in log2 units, sum)
+  float* part_o;         // [unit_slots, Hq, D] normalised partial outputs
+  float* part_ml;        // [unit_slots, Hq, 2] (max in log2 units, sum)
+  int* full_pre;         // [S] first slot of each sequence's full partitions
+                         // (its last partition's slot is full_total + seq)
   const void* query;     // [S, Hq, D]
   const void* key_cache;    // [num_blocks, Hkv, bs, D]
   const void* value_cache;
@@ -39,7 +44,7 @@ struct DecodeArgs {
   int part_floor;        // smallest partition size the plan may choose
   int part_cap;          // largest partition size the plan may choose
   int waves;             // waves per partition workgroup (4 or 8)
-  int max_parts;         // ceil(max_context_len / part_floor): workspace layout
+  int max_parts;         // ceil(max_context_len / part_floor): most partitions of a sequence
   float scale_log2;      // softmax scale * log2(e)
   const float* k_scale;  // [Hkv] FP8 cache: K = code value * k_scale (else null)
   const float* v_scale;  // [Hkv] FP8 cache: V = code value * v_scale (else null)
@@ -114,10 +119,12 @@ struct PrefillArgs {
 };
 
 struct DecodeLaunch {
-  int part_floor;
+  int part_floor;        // smallest partition size: one that keeps the plan's
+                         // partitions within unit_slots
   int part_cap;
   int max_parts;
   int waves;
+  int64_t unit_slots;    // partition slots of the workspace (per query head)
 };
 
 int decode_waves_per_workgroup();

@@ -91,6 +91,14 @@ def test_decode_workspace_size(lib):
     # grows with the context
     assert lib.pa_decode_workspace_size(8, 16, 4, 256, 16, 8192) >= \
         lib.pa_decode_workspace_size(8, 16, 4, 256, 16, 1024)
+    # bounded by the batch, not by the longest context alone: 1024 x 128K
+    # tokens needs the slots of 8192-token partitions (16 per sequence), 4096 x
+    # 128K likewise; a 64-sequence batch keeps one 256-token slot per 256 tokens
+    row = 16 * (256 + 2) * 4
+    assert lib.pa_decode_workspace_size(1024, 16, 4, 256, 16, 131072) <= 1024 * 16 * row + (1 << 20)
+    assert lib.pa_decode_workspace_size(4096, 16, 4, 256, 16, 131072) <= 4096 * 16 * row + (1 << 20)
+    assert lib.pa_decode_workspace_size(64, 16, 4, 256, 32, 8192) >= 64 * 32 * row
+    assert lib.pa_decode_workspace_size(64, 16, 4, 256, 32, 8192) <= 64 * 32 * row + (1 << 20)
 
 
 def scatter_args(**over):
