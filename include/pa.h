@@ -168,6 +168,33 @@ pa_status_t pa_decode(float* out, const void* query,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode without a workspace, for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). Same arguments, result and errors as pa_decode, less
+ * the workspace: the split-context partials and the work-queue counters live
+ * in a static device array of pa_decode_noalloc_max_bytes() bytes (64 MiB)
+ * inside the library, one per GPU, held until the process ends. Sizes whose
+ * pa_decode_workspace_size exceeds it return PA_ERR_WORKSPACE before any HIP
+ * call (64 sequences x 8192 tokens at 16 query heads, d 256, fit: 32.3 MiB).
+ * Each call first clears the array's head (a fill kernel) and then runs the
+ * decode kernels on it; it calls no allocating routine. Every call on one GPU
+ * shares the array, so calls that overlap on one GPU (other streams, other
+ * threads) race; calls in one stream's order are fine.
+ */
+pa_status_t pa_decode_noalloc(float* out, const void* query,
+                              const void* key_cache, const void* value_cache,
+                              const int32_t* block_tables,
+                              const int32_t* context_lens, int32_t num_seqs,
+                              int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size,
+                              int32_t max_blocks_per_seq, int64_t num_blocks,
+                              int32_t max_context_len, float scale,
+                              pa_dtype_t dtype, void* stream);
+
+/* Size of pa_decode_noalloc's static scratch, in bytes. */
+size_t pa_decode_noalloc_max_bytes(void);
+
+/*
  * FP8 KV cache. Quantizing the cache to FP8 halves the bytes every decode
  * step re-reads, which the pages count as doubling the effective memory
  * bandwidth (vLLM architecture, memory and benchmarks deep dive,

@@ -10,6 +10,8 @@ HIP kernels behind the C ABI in ``include/pa.h``:
                              separate merge kernel;
 * ``pa_prefill_chunk``     - a causal query chunk against the paged cache on
                              the matrix cores;
+* ``pa_decode_noalloc``    - ``pa_decode`` on a static scratch inside the
+                             library, for callers that cannot allocate;
 * ``pa_reshape_and_cache_fp8`` / ``pa_decode_fp8`` - the same scatter and
                              decode over an FP8 (E4M3) cache with one scale
                              per KV head for K and for V;
@@ -43,6 +45,7 @@ from ._lib import (  # noqa: F401
     pa_swap_out,
     pa_decode,
     pa_decode_fp8,
+    pa_decode_noalloc,
     pa_decode_workspace_init,
     pa_decode_workspace_size,
     pa_prefill_chunk,

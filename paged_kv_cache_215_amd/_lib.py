@@ -35,6 +35,9 @@ SIGNATURES = {
     "pa_decode_workspace_init": (_i32, [_vp, _sz, _vp]),
     "pa_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
                          _i32, _f32, _i32, _vp, _sz, _vp]),
+    "pa_decode_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                 _i32, _i64, _i32, _f32, _i32, _vp]),
+    "pa_decode_noalloc_max_bytes": (_sz, []),
     "pa_reshape_and_cache_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                         _i64, _i32, _vp]),
     "pa_decode_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
@@ -199,6 +202,23 @@ def pa_decode(query, key_cache, value_cache, block_tables, context_lens, scale,
         _ptr(context_lens), num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
         block_tables.shape[1], num_blocks, int(max_context_len), float(scale),
         _dtype_code(query), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return out
+
+
+def pa_decode_noalloc(query, key_cache, value_cache, block_tables, context_lens, scale,
+                      max_context_len, out):
+    """pa_decode on the library's static scratch: no workspace, nothing
+    allocated (``out``, float32 [S, Hq, d], is the caller's)."""
+    dev = _dev(query, key_cache, value_cache, block_tables, context_lens, out)
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    num_seqs, num_q_heads, head_dim = query.shape
+    num_blocks, num_kv_heads, block_size, _ = key_cache.shape
+    _check("pa_decode_noalloc", lib().pa_decode_noalloc(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        _ptr(context_lens), num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+        block_tables.shape[1], num_blocks, int(max_context_len), float(scale),
+        _dtype_code(query), _stream(dev)))
     return out
 
 

@@ -7,6 +7,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdlib>
 
@@ -24,6 +25,14 @@ int decode_waves_per_workgroup() {
 }
 
 }  // namespace pa
+
+// Decode scratch for pa_decode_noalloc: a fixed device array that every call
+// on a GPU shares (each GPU the library runs on holds its own copy until the
+// process ends). In host code `scratch` only names the symbol: its device
+// address comes from hipGetSymbolAddress, once per device, and only that
+// address is ever passed to a kernel or a fill.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -136,22 +145,47 @@ pa_status_t swap_impl(const void* key_cache, const void* value_cache, const void
   return from_hip(pa::launch_copy_blocks(a, static_cast<hipStream_t>(stream)));
 }
 
+constexpr int kMaxDevices = 64;
+std::atomic<void*> scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device, looked up on the first
+// call there (nullptr if the lookup fails; its error is cleared).
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  void* p = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  scratch_ptr[dev].store(p, std::memory_order_release);  // the same value on every race
+  return p;
+}
+
 // Validation (NULL -> SHAPE -> UNSUPPORTED -> ALIGN -> WORKSPACE) and launch of
 // a decode over a cache of type kv. type_ok is the caller's check of its
 // element types (reported as UNSUPPORTED); an FP8 cache also needs its two
-// scale arrays.
+// scale arrays. With use_scratch the decode runs on the static scratch
+// instead of a caller's workspace (workspace and workspace_bytes are then
+// ignored): the sizes must fit kScratchBytes, and the scratch head is cleared
+// with a fill kernel before the launch.
 pa_status_t decode_impl(float* out, const void* query, const void* key_cache,
                         const void* value_cache, const float* k_scale, const float* v_scale,
                         const int32_t* block_tables, const int32_t* context_lens,
                         int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                         int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                         int64_t num_blocks, int32_t max_context_len, float scale, pa::KvType kv,
-                        bool type_ok, void* workspace, size_t workspace_bytes, void* stream) {
+                        bool type_ok, void* workspace, size_t workspace_bytes, void* stream,
+                        bool use_scratch = false) {
   const bool scaled = kv == pa::KvType::FP8;
   if (num_seqs < 0) return PA_ERR_SHAPE;
   if (num_seqs == 0) return PA_OK;
   if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens ||
-      !workspace || (scaled && (!k_scale || !v_scale)))
+      (!workspace && !use_scratch) || (scaled && (!k_scale || !v_scale)))
     return PA_ERR_NULL;
   if (num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
       max_blocks_per_seq <= 0 || num_blocks <= 0 || max_context_len < 0 ||
@@ -161,13 +195,20 @@ pa_status_t decode_impl(float* out, const void* query, const void* key_cache,
       !supported_group(num_q_heads, num_kv_heads) || !type_ok)
     return PA_ERR_UNSUPPORTED;
   if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) ||
-      !aligned(value_cache, 16) || !aligned(workspace, 16) ||
+      !aligned(value_cache, 16) || (!use_scratch && !aligned(workspace, 16)) ||
       !aligned(block_tables, 4) ||
       !aligned(context_lens, 4) || (scaled && (!aligned(k_scale, 4) || !aligned(v_scale, 4))))
     return PA_ERR_ALIGN;
   const DecodeGeometry geo = decode_geometry(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                              block_size, max_context_len);
-  if (workspace_bytes < geo.bytes) return PA_ERR_WORKSPACE;
+  if ((use_scratch ? kScratchBytes : workspace_bytes) < geo.bytes) return PA_ERR_WORKSPACE;
+  if (use_scratch) {
+    workspace = scratch_on_current_device();
+    if (!workspace) return PA_ERR_HIP;
+    if (pa::launch_zero_fill(workspace, kDecodeHeadBytes, static_cast<hipStream_t>(stream)) !=
+        hipSuccess)
+      return PA_ERR_HIP;
+  }
 
   pa::DecodeArgs a;
   char* ws = static_cast<char*>(workspace);
@@ -308,6 +349,23 @@ pa_status_t pa_decode(float* out, const void* query, const void* key_cache,
                      dtype == PA_DTYPE_BF16 ? pa::KvType::BF16 : pa::KvType::F32, type_ok,
                      workspace, workspace_bytes, stream);
 }
+
+pa_status_t pa_decode_noalloc(float* out, const void* query, const void* key_cache,
+                              const void* value_cache, const int32_t* block_tables,
+                              const int32_t* context_lens, int32_t num_seqs,
+                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int32_t max_blocks_per_seq,
+                              int64_t num_blocks, int32_t max_context_len, float scale,
+                              pa_dtype_t dtype, void* stream) {
+  const bool type_ok = dtype == PA_DTYPE_F32 || dtype == PA_DTYPE_BF16;
+  return decode_impl(out, query, key_cache, value_cache, nullptr, nullptr, block_tables,
+                     context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                     max_blocks_per_seq, num_blocks, max_context_len, scale,
+                     dtype == PA_DTYPE_BF16 ? pa::KvType::BF16 : pa::KvType::F32, type_ok,
+                     nullptr, 0, stream, /*use_scratch=*/true);
+}
+
+size_t pa_decode_noalloc_max_bytes(void) { return kScratchBytes; }
 
 pa_status_t pa_decode_fp8(float* out, const void* query, const void* key_cache,
                           const void* value_cache, const float* k_scale, const float* v_scale,
