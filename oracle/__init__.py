@@ -28,8 +28,8 @@ definitions state:
                                         preemption by swapping to host blocks.
 * ``fp8``                             - E4M3 code values, the saturating
                                         round-to-nearest-even quantizer with
-                                        per-head scales, FP8 scatter and decode
-                                        on the dequantized cache.
+                                        per-head scales, FP8 scatter, decode and
+                                        chunked prefill on the dequantized cache.
 
 Pins (checked by ``tests/test_oracle*.py`` with ``-m "not gpu"``): dense
 brute force, closed forms (n = 1, uniform keys, two-token softmax, GQA head

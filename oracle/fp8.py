@@ -21,6 +21,9 @@ They give no format, scale or rounding; the readings taken here:
   kept); the sign of zero is kept.
 * dequantized value = value(code) * s, exact in float64.
 
+Decode and chunked prefill over an FP8 cache are the BF16 definitions applied
+to the dequantized values.
+
 The quantizer below rounds by searching the table of the 127 non-negative
 finite code values for the nearest one; it shares nothing with the device's
 bit-level rounding.
@@ -145,3 +148,18 @@ def decode_fp8_ref(query, key_codes, value_codes, k_scale, v_scale, block_tables
 
     return decode_ref(to_f64(query), _DequantizedView(key_codes, k_scale),
                       _DequantizedView(value_codes, v_scale), block_tables, context_lens, scale)
+
+
+def prefill_chunk_fp8_ref(query, key_codes, value_codes, k_scale, v_scale, block_tables,
+                          context_lens, cu_q_lens, scale):
+    """Causal chunk attention over an FP8 cache: the attention of
+    ``prefill_chunk_ref`` on the dequantized K and V (float64 output). The
+    pages name FP8 caches and chunked prefill side by side as levers of the
+    same serving step (vLLM architecture, memory and benchmarks deep dive,
+    "Hardware-level optimizations"); quantizing changes the values K and V
+    hold, not what the chunk attends to."""
+    from .paged_ref import prefill_chunk_ref
+
+    return prefill_chunk_ref(to_f64(query), _DequantizedView(key_codes, k_scale),
+                             _DequantizedView(value_codes, v_scale), block_tables, context_lens,
+                             cu_q_lens, scale)

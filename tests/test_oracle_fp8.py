@@ -9,7 +9,8 @@ import pytest
 import torch
 
 from oracle import fp8
-from oracle.paged_ref import decode_ref
+from oracle.dense_ref import dense_attention_ref
+from oracle.paged_ref import decode_ref, prefill_chunk_ref
 from oracle_helpers import lay_out
 
 
@@ -193,6 +194,66 @@ def test_decode_on_representable_cache_equals_plain_decode():
     assert np.array_equal(got, want)
 
 
+def _representable_case(rng, lens, hkv, d, bs, ks_h, vs_h):
+    """Contiguous K/V drawn as s_h * value(code) (random finite codes), laid
+    into a shuffled pool; returns code caches, value caches and tables."""
+    kcodes = [rng.integers(0, 0x7E, size=(n, hkv, d)) | (rng.integers(0, 2, (n, hkv, d)) << 7)
+              for n in lens]
+    vcodes = [rng.integers(0, 0x7E, size=(n, hkv, d)) | (rng.integers(0, 2, (n, hkv, d)) << 7)
+              for n in lens]
+    kvals = [(fp8.e4m3_value(c) * ks_h[None, :, None]).astype(np.float32) for c in kcodes]
+    vvals = [(fp8.e4m3_value(c) * vs_h[None, :, None]).astype(np.float32) for c in vcodes]
+    kc, vc, bt = lay_out(kvals, vvals, bs, np.random.default_rng(1), fill=0.0)
+    kq = fp8.quantize_rows(kc.transpose(0, 2, 1, 3), ks_h).transpose(0, 2, 1, 3)
+    vq = fp8.quantize_rows(vc.transpose(0, 2, 1, 3), vs_h).transpose(0, 2, 1, 3)
+    return kq, vq, kc, vc, bt, kvals, vvals
+
+
+def test_prefill_on_representable_cache_equals_plain_prefill():
+    # exact dequantization: the FP8 chunk must equal the plain chunk oracle on
+    # the same values, for chunks with and without a cached prefix
+    rng = np.random.default_rng(19)
+    lens, q_lens, hkv, d, bs = [40, 23, 9], [7, 23, 1], 2, 16, 16
+    ks_h = np.array([0.25, 0.0625], dtype=np.float32)
+    vs_h = np.array([4.0, 0.125], dtype=np.float32)
+    kq, vq, kc, vc, bt, _, _ = _representable_case(rng, lens, hkv, d, bs, ks_h, vs_h)
+    cu = np.concatenate([[0], np.cumsum(q_lens)])
+    q = rng.standard_normal((int(cu[-1]), 4, d)).astype(np.float32)
+    got = fp8.prefill_chunk_fp8_ref(q, kq, vq, ks_h, vs_h, bt, np.array(lens), cu, 0.3)
+    want = prefill_chunk_ref(q, kc, vc, bt, np.array(lens), cu, 0.3)
+    assert np.array_equal(got, want)
+
+
+def test_prefill_fp8_matches_dense_causal_attention():
+    # brute force on the contiguous dequantized K/V (no table walk): the
+    # bottom-right causal chunk of each sequence
+    rng = np.random.default_rng(21)
+    lens, q_lens, hkv, d, bs = [37, 16], [5, 16], 2, 8, 16
+    ks_h = np.array([0.5, 0.125], dtype=np.float32)
+    vs_h = np.array([0.25, 2.0], dtype=np.float32)
+    kq, vq, _, _, bt, kvals, vvals = _representable_case(rng, lens, hkv, d, bs, ks_h, vs_h)
+    cu = np.concatenate([[0], np.cumsum(q_lens)])
+    q = rng.standard_normal((int(cu[-1]), 4, d)).astype(np.float32)
+    got = fp8.prefill_chunk_fp8_ref(q, kq, vq, ks_h, vs_h, bt, np.array(lens), cu, 0.35)
+    for b in range(len(lens)):
+        want = dense_attention_ref(q[cu[b]:cu[b + 1]], kvals[b], vvals[b], 0.35, causal=True)
+        assert np.max(np.abs(got[cu[b]:cu[b + 1]] - want)) < 1e-12
+
+
+def test_prefill_fp8_single_row_equals_fp8_decode():
+    # a one-row chunk at the end of its context is a decode query
+    rng = np.random.default_rng(23)
+    lens, hkv, d, bs = [50, 1, 16], 1, 8, 16
+    ks_h = np.array([0.5], dtype=np.float32)
+    vs_h = np.array([0.75], dtype=np.float32)
+    kq, vq, _, _, bt, _, _ = _representable_case(rng, lens, hkv, d, bs, ks_h, vs_h)
+    q = rng.standard_normal((len(lens), 2, d)).astype(np.float32)
+    cu = np.arange(len(lens) + 1)
+    got = fp8.prefill_chunk_fp8_ref(q, kq, vq, ks_h, vs_h, bt, np.array(lens), cu, 0.5)
+    want = fp8.decode_fp8_ref(q, kq, vq, ks_h, vs_h, bt, np.array(lens), 0.5)
+    assert np.array_equal(got, want)
+
+
 def test_dequantize_closed_form():
     codes = np.array([0x38, 0x40, 0xB8, 0x01], dtype=np.uint8).reshape(1, 2, 1, 2)
     got = fp8.dequantize(codes, np.array([3.0, 0.5], dtype=np.float32))
@@ -264,6 +325,9 @@ PINS = [
     test_bf16_sources_widen_exactly,
     test_scatter_writes_only_mapped_slots,
     test_decode_on_representable_cache_equals_plain_decode,
+    test_prefill_on_representable_cache_equals_plain_prefill,
+    test_prefill_fp8_matches_dense_causal_attention,
+    test_prefill_fp8_single_row_equals_fp8_decode,
     test_dequantize_closed_form,
 ]
 
@@ -277,8 +341,26 @@ def _some_pin_fails():
     return False
 
 
+def _prefill_v_with_k_scale(query, key_codes, value_codes, k_scale, v_scale, block_tables,
+                            context_lens, cu_q_lens, scale):
+    from oracle.paged_ref import prefill_chunk_ref as plain
+    return plain(query, fp8._DequantizedView(key_codes, k_scale),
+                 fp8._DequantizedView(value_codes, k_scale), block_tables, context_lens,
+                 cu_q_lens, scale)
+
+
+def _prefill_unscaled_k(query, key_codes, value_codes, k_scale, v_scale, block_tables,
+                        context_lens, cu_q_lens, scale):
+    from oracle.paged_ref import prefill_chunk_ref as plain
+    ones = np.ones_like(np.asarray(k_scale, dtype=np.float32))
+    return plain(query, fp8._DequantizedView(key_codes, ones),
+                 fp8._DequantizedView(value_codes, v_scale), block_tables, context_lens,
+                 cu_q_lens, scale)
+
+
 @pytest.mark.parametrize("mutation", ["ties_away", "no_saturation", "truncate", "bias8",
-                                      "scale_multiplies", "one_scale_for_all_heads"])
+                                      "scale_multiplies", "one_scale_for_all_heads",
+                                      "prefill_v_with_k_scale", "prefill_unscaled_k"])
 def test_planted_fp8_mistake_fails_a_pin(monkeypatch, mutation):
     monkeypatch.setitem(fp8.__dict__, "_orig_quantize", fp8.quantize_e4m3)
     if mutation == "ties_away":
@@ -292,6 +374,10 @@ def test_planted_fp8_mistake_fails_a_pin(monkeypatch, mutation):
         monkeypatch.setattr(fp8, "_VALUES", _value_bias8(fp8._CODES))
     elif mutation == "scale_multiplies":
         monkeypatch.setattr(fp8, "quantize_rows", _quantize_rows_multiply)
+    elif mutation == "prefill_v_with_k_scale":
+        monkeypatch.setattr(fp8, "prefill_chunk_fp8_ref", _prefill_v_with_k_scale)
+    elif mutation == "prefill_unscaled_k":
+        monkeypatch.setattr(fp8, "prefill_chunk_fp8_ref", _prefill_unscaled_k)
     else:
         monkeypatch.setattr(fp8, "quantize_rows", _quantize_rows_first_head)
     assert _some_pin_fails()
