@@ -289,6 +289,33 @@ pa_status_t pa_prefill_chunk(float* out, const void* query,
                              void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/*
+ * pa_prefill_chunk over an FP8 cache (codes and per-head scales as for
+ * pa_decode_fp8): the causal chunk attention of pa_prefill_chunk with k_j and
+ * v_j the dequantized rows. The pages name the FP8 cache and chunked prefill
+ * together as levers of one serving step (vLLM architecture, memory and
+ * benchmarks deep dive, "Hardware-level optimizations"). The codes are
+ * converted exactly to BF16 as the K/V tiles are staged for the matrix cores;
+ * the K scale folds into the softmax scale and the V scale into the output.
+ * The workspace is the one pa_prefill_chunk_workspace_size describes for the
+ * same sizes.
+ * query_dtype: PA_DTYPE_BF16 only.
+ */
+pa_status_t pa_prefill_chunk_fp8(float* out, const void* query,
+                                 const void* key_cache, const void* value_cache,
+                                 const float* k_scale, const float* v_scale,
+                                 const int32_t* block_tables,
+                                 const int32_t* context_lens,
+                                 const int32_t* cu_q_lens,
+                                 int32_t num_seqs, int32_t total_q,
+                                 int32_t max_q_len, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t max_blocks_per_seq,
+                                 int64_t num_blocks, int32_t max_context_len,
+                                 float scale, pa_dtype_t query_dtype,
+                                 void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* pa_status_string(pa_status_t status);
 

@@ -12,9 +12,10 @@ HIP kernels behind the C ABI in ``include/pa.h``:
                              the matrix cores;
 * ``pa_decode_noalloc``    - ``pa_decode`` on a static scratch inside the
                              library, for callers that cannot allocate;
-* ``pa_reshape_and_cache_fp8`` / ``pa_decode_fp8`` - the same scatter and
-                             decode over an FP8 (E4M3) cache with one scale
-                             per KV head for K and for V;
+* ``pa_reshape_and_cache_fp8`` / ``pa_decode_fp8`` / ``pa_prefill_chunk_fp8``
+                           - the same scatter, decode and prefill chunk over
+                             an FP8 (E4M3) cache with one scale per KV head
+                             for K and for V;
 * ``BlockManager`` / ``pa_copy_blocks`` - the host block manager (on-demand
                              blocks, reference-counted sharing, copy-on-write)
                              and the device block copy it asks for;
@@ -49,6 +50,7 @@ from ._lib import (  # noqa: F401
     pa_decode_workspace_init,
     pa_decode_workspace_size,
     pa_prefill_chunk,
+    pa_prefill_chunk_fp8,
     pa_prefill_chunk_workspace_size,
     pa_reshape_and_cache,
     pa_reshape_and_cache_fp8,

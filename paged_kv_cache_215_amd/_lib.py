@@ -45,6 +45,9 @@ SIGNATURES = {
     "pa_prefill_chunk_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_prefill_chunk": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                 _i32, _i32, _i32, _i64, _i32, _f32, _i32, _vp, _sz, _vp]),
+    "pa_prefill_chunk_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                    _i32, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _f32, _i32,
+                                    _vp, _sz, _vp]),
     "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i32, _vp]),
     "pa_bm_create": (_i32, [_i64, _i32, _i32, ctypes.POINTER(_vp)]),
     "pa_bm_destroy": (None, [_vp]),
@@ -308,6 +311,38 @@ def pa_prefill_chunk(query, key_cache, value_cache, block_tables, context_lens, 
         _ptr(context_lens), _ptr(cu_q_lens), num_seqs, total_q, int(max_q_len), num_q_heads,
         num_kv_heads, head_dim, block_size, block_tables.shape[1], num_blocks,
         int(max_context_len), float(scale), _dtype_code(query), _ptr(workspace),
+        workspace.numel() if workspace is not None else 0, _stream(dev)))
+    return out
+
+
+def pa_prefill_chunk_fp8(query, key_cache, value_cache, k_scale, v_scale, block_tables,
+                         context_lens, cu_q_lens, max_q_len, scale, max_context_len, out=None,
+                         workspace=None):
+    """Causal chunk attention over an FP8 (E4M3) paged cache; returns float32
+    [total_q, Hq, d]."""
+    dev = _dev(query, key_cache, value_cache, k_scale, v_scale, block_tables, context_lens,
+               cu_q_lens)
+    if cu_q_lens.dtype != torch.int32:
+        raise TypeError("cu_q_lens must be int32")
+    _fp8_cache(key_cache)
+    _fp8_cache(value_cache)
+    _scales(k_scale, v_scale)
+    total_q, num_q_heads, head_dim = query.shape
+    num_blocks, num_kv_heads, block_size, _ = key_cache.shape
+    if k_scale.numel() != num_kv_heads or v_scale.numel() != num_kv_heads:
+        raise ValueError("one scale per KV head")
+    num_seqs = cu_q_lens.numel() - 1
+    if out is None:
+        out = torch.empty((total_q, num_q_heads, head_dim), dtype=torch.float32, device=dev)
+    need = pa_prefill_chunk_workspace_size(num_seqs, total_q, max_q_len, num_q_heads,
+                                           num_kv_heads, head_dim, block_size, max_context_len)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check("pa_prefill_chunk_fp8", lib().pa_prefill_chunk_fp8(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_tables), _ptr(context_lens), _ptr(cu_q_lens), num_seqs, total_q,
+        int(max_q_len), num_q_heads, num_kv_heads, head_dim, block_size, block_tables.shape[1],
+        num_blocks, int(max_context_len), float(scale), _dtype_code(query), _ptr(workspace),
         workspace.numel() if workspace is not None else 0, _stream(dev)))
     return out
 

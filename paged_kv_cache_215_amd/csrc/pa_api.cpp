@@ -243,6 +243,72 @@ pa_status_t decode_impl(float* out, const void* query, const void* key_cache,
   return from_hip(pa::launch_decode(a, kv, static_cast<hipStream_t>(stream)));
 }
 
+// Validation (NULL -> SHAPE -> UNSUPPORTED -> ALIGN -> WORKSPACE) and launch of
+// a prefill chunk over a BF16 cache, or an E4M3 one with its two scale arrays.
+pa_status_t prefill_impl(float* out, const void* query, const void* key_cache,
+                         const void* value_cache, const float* k_scale, const float* v_scale,
+                         const int32_t* block_tables, const int32_t* context_lens,
+                         const int32_t* cu_q_lens, int32_t num_seqs, int32_t total_q,
+                         int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                         int64_t num_blocks, int32_t max_context_len, float scale, bool fp8,
+                         bool type_ok, void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs < 0 || total_q < 0) return PA_ERR_SHAPE;
+  if (num_seqs == 0 || total_q == 0) return PA_OK;
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens ||
+      !cu_q_lens || (fp8 && (!k_scale || !v_scale)))
+    return PA_ERR_NULL;
+  if (max_q_len <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || max_context_len < 0 ||
+      num_q_heads % num_kv_heads != 0 || !std::isfinite(scale))
+    return PA_ERR_SHAPE;
+  if (!supported_block(block_size) || !supported_dim(head_dim) ||
+      !supported_group(num_q_heads, num_kv_heads) || !type_ok)
+    return PA_ERR_UNSUPPORTED;
+  if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) ||
+      !aligned(value_cache, 16) || !aligned(block_tables, 4) || !aligned(context_lens, 4) ||
+      !aligned(cu_q_lens, 4) || (workspace && !aligned(workspace, 16)) ||
+      (fp8 && (!aligned(k_scale, 4) || !aligned(v_scale, 4))))
+    return PA_ERR_ALIGN;
+  const size_t need = pa_prefill_chunk_workspace_size(num_seqs, total_q, max_q_len, num_q_heads,
+                                                      num_kv_heads, head_dim, block_size,
+                                                      max_context_len);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+
+  pa::PrefillArgs a;
+  a.out = out;
+  a.xcd_remap = 1;
+  a.kv_splits = pa::prefill_kv_splits(num_seqs, max_q_len, num_q_heads, num_kv_heads, head_dim,
+                                             max_context_len);
+  if (a.kv_splits < 1) a.kv_splits = 1;
+  const size_t rows = (size_t)total_q * num_q_heads * a.kv_splits;
+  a.part_o = need ? static_cast<float*>(workspace) : nullptr;
+  a.part_ml = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                              rows * head_dim * sizeof(float))
+                   : nullptr;
+  a.query = query;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.cu_q_lens = cu_q_lens;
+  a.num_seqs = num_seqs;
+  a.total_q = total_q;
+  a.max_q_len = max_q_len;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size_log2 = log2_exact(block_size);
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.ctx_limit = ctx_limit(max_context_len, max_blocks_per_seq, block_size);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.kv_fp8 = fp8;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  return from_hip(pa::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -406,56 +472,28 @@ pa_status_t pa_prefill_chunk(float* out, const void* query, const void* key_cach
                              int64_t num_blocks, int32_t max_context_len, float scale,
                              pa_dtype_t dtype, void* workspace, size_t workspace_bytes,
                              void* stream) {
-  if (num_seqs < 0 || total_q < 0) return PA_ERR_SHAPE;
-  if (num_seqs == 0 || total_q == 0) return PA_OK;
-  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens ||
-      !cu_q_lens)
-    return PA_ERR_NULL;
-  if (max_q_len <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-      block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || max_context_len < 0 ||
-      num_q_heads % num_kv_heads != 0 || !std::isfinite(scale))
-    return PA_ERR_SHAPE;
-  if (!supported_block(block_size) || !supported_dim(head_dim) ||
-      !supported_group(num_q_heads, num_kv_heads) || dtype != PA_DTYPE_BF16)
-    return PA_ERR_UNSUPPORTED;
-  if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) ||
-      !aligned(value_cache, 16) || !aligned(block_tables, 4) || !aligned(context_lens, 4) ||
-      !aligned(cu_q_lens, 4) || (workspace && !aligned(workspace, 16)))
-    return PA_ERR_ALIGN;
-  const size_t need = pa_prefill_chunk_workspace_size(num_seqs, total_q, max_q_len, num_q_heads,
-                                                      num_kv_heads, head_dim, block_size,
-                                                      max_context_len);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+  return prefill_impl(out, query, key_cache, value_cache, nullptr, nullptr, block_tables,
+                      context_lens, cu_q_lens, num_seqs, total_q, max_q_len, num_q_heads,
+                      num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                      max_context_len, scale, false, dtype == PA_DTYPE_BF16, workspace,
+                      workspace_bytes, stream);
+}
 
-  pa::PrefillArgs a;
-  a.out = out;
-  a.xcd_remap = 1;
-  a.kv_splits = pa::prefill_kv_splits(num_seqs, max_q_len, num_q_heads, num_kv_heads, head_dim,
-                                             max_context_len);
-  if (a.kv_splits < 1) a.kv_splits = 1;
-  const size_t rows = (size_t)total_q * num_q_heads * a.kv_splits;
-  a.part_o = need ? static_cast<float*>(workspace) : nullptr;
-  a.part_ml = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                              rows * head_dim * sizeof(float))
-                   : nullptr;
-  a.query = query;
-  a.key_cache = key_cache;
-  a.value_cache = value_cache;
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  a.cu_q_lens = cu_q_lens;
-  a.num_seqs = num_seqs;
-  a.total_q = total_q;
-  a.max_q_len = max_q_len;
-  a.num_q_heads = num_q_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.head_dim = head_dim;
-  a.block_size_log2 = log2_exact(block_size);
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.num_blocks = num_blocks;
-  a.ctx_limit = ctx_limit(max_context_len, max_blocks_per_seq, block_size);
-  a.scale_log2 = scale * 1.4426950408889634f;
-  return from_hip(pa::launch_prefill(a, static_cast<hipStream_t>(stream)));
+pa_status_t pa_prefill_chunk_fp8(float* out, const void* query, const void* key_cache,
+                                 const void* value_cache, const float* k_scale,
+                                 const float* v_scale, const int32_t* block_tables,
+                                 const int32_t* context_lens, const int32_t* cu_q_lens,
+                                 int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t max_blocks_per_seq,
+                                 int64_t num_blocks, int32_t max_context_len, float scale,
+                                 pa_dtype_t query_dtype, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  return prefill_impl(out, query, key_cache, value_cache, k_scale, v_scale, block_tables,
+                      context_lens, cu_q_lens, num_seqs, total_q, max_q_len, num_q_heads,
+                      num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                      max_context_len, scale, true, query_dtype == PA_DTYPE_BF16, workspace,
+                      workspace_bytes, stream);
 }
 
 pa_status_t pa_copy_blocks(void* key_cache, void* value_cache, const int64_t* pairs,

@@ -116,6 +116,9 @@ struct PrefillArgs {
   int kv_splits;         // context splits per row tile (1 = no partials)
   int xcd_remap;         // group workgroups of one (KV head, split) on one XCD
   float scale_log2;
+  bool kv_fp8;           // caches hold E4M3 codes (else BF16)
+  const float* k_scale;  // [Hkv] E4M3 cache: K = code value * k_scale (else null)
+  const float* v_scale;  // [Hkv] E4M3 cache: V = code value * v_scale (else null)
 };
 
 struct DecodeLaunch {

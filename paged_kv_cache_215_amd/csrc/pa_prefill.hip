@@ -33,6 +33,7 @@
 #include "pa_internal.hpp"
 
 #include <cstdlib>
+#include <type_traits>
 
 namespace pa {
 
@@ -101,10 +102,28 @@ struct PrefillShape {
 
 constexpr int kPfMaxBlocks = 1024;  // table entries one context split may span
 
-template <int D, int G, int HPW, int MW, int KT>
+// 8 E4M3 codes (an 8-byte cache chunk) as 8 bfloat16 (a 16-byte LDS chunk):
+// exact, every E4M3 value being a bfloat16 value.
+__device__ __forceinline__ u32x4_t fp8x8_to_bf16x8(const uint2& c) {
+  u32x4_t r;
+  r.x = fp8x2_to_bf16x2<false>(c.x);
+  r.y = fp8x2_to_bf16x2<true>(c.x);
+  r.z = fp8x2_to_bf16x2<false>(c.y);
+  r.w = fp8x2_to_bf16x2<true>(c.y);
+  return r;
+}
+
+// T: cache element type, BF16 or FP8 (E4M3 codes). An E4M3 cache is staged
+// through the same LDS layout: every 16-byte BF16 chunk of a row (8 dims)
+// corresponds to an 8-byte chunk of 8 codes at the same chunk index, which is
+// loaded and converted on its way to LDS.
+template <typename T, int D, int G, int HPW, int MW, int KT>
 __global__ __launch_bounds__((PrefillShape<D, G, HPW, MW, KT>::NT))
 __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
   using S = PrefillShape<D, G, HPW, MW, KT>;
+  constexpr bool kFp8 = std::is_same<T, FP8>::value;
+  // cache chunk: 16 bytes of 8 bfloat16, or 8 bytes of 8 codes
+  using CC = typename std::conditional<kFp8, uint2, uint4>::type;
   constexpr int DCH = S::DCH;
   constexpr int kKeyTile = KT;
   constexpr int kVtStride = S::VT_STRIDE;
@@ -150,8 +169,12 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
   // negative scale the query's sign bits are flipped instead (exact), and a
   // zero scale becomes the smallest normal float, whose products with finite
   // scores round the weights to exactly 1, as the zero scale would.
+  // (E4M3 cache: the head's positive K scale multiplies every score, so it
+  // folds into c; the V scale multiplies the output.)
   const uint32_t qflip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
-  const float c_exp = fmaxf(fabsf(a.scale_log2), 1.17549435e-38f);
+  const float k_scale = kFp8 ? a.k_scale[kvh] : 1.f;
+  const float v_scale = kFp8 ? a.v_scale[kvh] : 1.f;
+  const float c_exp = fmaxf(fabsf(a.scale_log2) * k_scale, 1.17549435e-38f);
   bf16x8_t qop[HPW][S::KSTEPS];
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
@@ -170,8 +193,9 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
   const int kt_begin = split * per_split;
   const int kt_end = min(ntiles, kt_begin + per_split);
 
-  const uint4* kcache = reinterpret_cast<const uint4*>(a.key_cache);
-  const uint4* vcache = reinterpret_cast<const uint4*>(a.value_cache);
+  // (in cache chunks: DCH per row for either element type)
+  const CC* kcache = reinterpret_cast<const CC*>(a.key_cache);
+  const CC* vcache = reinterpret_cast<const CC*>(a.value_cache);
   const int64_t block_stride = (int64_t)a.num_kv_heads * bs * DCH;
   const int64_t head_off = (int64_t)kvh * bs * DCH;
 
@@ -211,21 +235,27 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
   // (K staging uses native vectors: copied as plain structs, the registers
   // ended up in scratch memory)
   u32x4_t kreg[S::KPT];
-  uint4 vreg[S::VPT][4];
+  CC vreg[S::VPT][4];
   auto load_regs = [&](int kt) {
     const int key0 = kt * kKeyTile;
     {
-      const uint4* src = kcache + row_base(key0 + k_row_c) + k_c0;
+      const CC* src = kcache + row_base(key0 + k_row_c) + k_c0;
 #pragma unroll
-      for (int i = 0; i < S::KPT; ++i)
-        kreg[i] = *reinterpret_cast<const u32x4_t*>(src + S::TPR * i);
+      for (int i = 0; i < S::KPT; ++i) {
+        if constexpr (kFp8) {
+          const u32x2_t c = *reinterpret_cast<const u32x2_t*>(src + S::TPR * i);
+          kreg[i] = u32x4_t{c.x, c.y, 0u, 0u};  // converted when stored
+        } else {
+          kreg[i] = *reinterpret_cast<const u32x4_t*>(src + S::TPR * i);
+        }
+      }
     }
 #pragma unroll
     for (int j = 0; j < S::VPT; ++j) {
       const int job = tid + j * S::NT;
       if (job < S::VJOBS) {
         const int kg = job % (kKeyTile / 4), dg = job / (kKeyTile / 4);
-        const uint4* src = vcache + row_base(key0 + 4 * kg) + dg;
+        const CC* src = vcache + row_base(key0 + 4 * kg) + dg;
 #pragma unroll
         for (int r = 0; r < 4; ++r) vreg[j][r] = src[r * DCH];
       }
@@ -237,7 +267,7 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
         const int kg = job % (kKeyTile / 4);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (key0 + 4 * kg + r >= n) vreg[j][r] = make_uint4(0, 0, 0, 0);
+          if (key0 + 4 * kg + r >= n) zero_chunk(vreg[j][r]);
       }
     }
   };
@@ -248,7 +278,9 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int i = 0; i < S::KPT; ++i) {
         const int c = k_c0 + S::TPR * i;
-        *reinterpret_cast<u32x4_t*>(&k_lds[buf][k_row * DCH + (c ^ (k_row & S::SWZ))]) = kreg[i];
+        u32x4_t w = kreg[i];
+        if constexpr (kFp8) w = fp8x8_to_bf16x8(make_uint2(w.x, w.y));
+        *reinterpret_cast<u32x4_t*>(&k_lds[buf][k_row * DCH + (c ^ (k_row & S::SWZ))]) = w;
       }
     }
     // V^T: each job transposes 4 keys x 8 dims
@@ -258,10 +290,20 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
       if (job < S::VJOBS) {
         const int kg = job % (kKeyTile / 4), dg = job / (kKeyTile / 4);
         const int slot = vt_slot(4 * kg);
-        const uint32_t* w0 = &vreg[j][0].x;
-        const uint32_t* w1 = &vreg[j][1].x;
-        const uint32_t* w2 = &vreg[j][2].x;
-        const uint32_t* w3 = &vreg[j][3].x;
+        uint4 rows[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if constexpr (kFp8) {
+            const u32x4_t w = fp8x8_to_bf16x8(vreg[j][r]);
+            rows[r] = make_uint4(w.x, w.y, w.z, w.w);
+          } else {
+            rows[r] = vreg[j][r];
+          }
+        }
+        const uint32_t* w0 = &rows[0].x;
+        const uint32_t* w1 = &rows[1].x;
+        const uint32_t* w2 = &rows[2].x;
+        const uint32_t* w3 = &rows[3].x;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           uint2 even, odd;  // dims 8*dg + 2c and 8*dg + 2c + 1, keys 4kg..4kg+3
@@ -425,7 +467,7 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
     l_row = pair_sum<32>(l_row);
     if (my_row >= L) continue;
     const int64_t orow = (int64_t)(q0 + my_row) * a.num_q_heads + head0 + hh;
-    const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
+    const float inv = l_row > 0.f ? v_scale / l_row : 0.f;
     float* dst;
     if (a.kv_splits == 1) {
       dst = a.out + orow * D;
@@ -565,7 +607,7 @@ int prefill_kv_splits(int num_seqs, int max_q_len, int num_q_heads, int num_kv_h
   return splits;
 }
 
-template <int D, int G, int HPW, int MW, int KT>
+template <typename T, int D, int G, int HPW, int MW, int KT>
 static hipError_t launch_pf(const PrefillArgs& a_in, hipStream_t stream) {
   static const int remap = [] {
     const char* s = std::getenv("PA_PREFILL_XCD");
@@ -575,7 +617,7 @@ static hipError_t launch_pf(const PrefillArgs& a_in, hipStream_t stream) {
   a.xcd_remap = remap;
   using S = PrefillShape<D, G, HPW, MW, KT>;
   dim3 grid((a.max_q_len + S::ROWS - 1) / S::ROWS, a.num_kv_heads, a.num_seqs * a.kv_splits);
-  hipLaunchKernelGGL((prefill_kernel<D, G, HPW, MW, KT>), grid, dim3(S::NT), 0, stream, a);
+  hipLaunchKernelGGL((prefill_kernel<T, D, G, HPW, MW, KT>), grid, dim3(S::NT), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.kv_splits == 1) return err;
   hipLaunchKernelGGL((prefill_merge_kernel<D>), dim3(a.num_q_heads, a.total_q), dim3(kWave), 0,
@@ -583,50 +625,55 @@ static hipError_t launch_pf(const PrefillArgs& a_in, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, int G, int HPW, int MW>
+template <typename T, int D, int G, int HPW, int MW>
 static hipError_t launch_pk(const PrefillArgs& a, hipStream_t stream) {
   if constexpr (MW == 8 && HPW <= 2) {
-    if (prefill_key_tile(G, D) == 64) return launch_pf<D, G, HPW, MW, 64>(a, stream);
+    if (prefill_key_tile(G, D) == 64) return launch_pf<T, D, G, HPW, MW, 64>(a, stream);
   }
-  return launch_pf<D, G, HPW, MW, 32>(a, stream);
+  return launch_pf<T, D, G, HPW, MW, 32>(a, stream);
 }
 
-template <int D, int G, int MW>
+template <typename T, int D, int G, int MW>
 static hipError_t launch_ph(const PrefillArgs& a, hipStream_t stream) {
   const int hpw = prefill_group_heads_per_wave(G, D);
   if constexpr (G >= 4 && D <= 128 && (MW == 4 || 4 * D <= 256)) {
-    if (hpw == 4) return launch_pk<D, G, 4, MW>(a, stream);
+    if (hpw == 4) return launch_pk<T, D, G, 4, MW>(a, stream);
   }
   if constexpr (G >= 2 && (MW == 4 || 2 * D <= 256)) {
-    if (hpw == 2) return launch_pk<D, G, 2, MW>(a, stream);
+    if (hpw == 2) return launch_pk<T, D, G, 2, MW>(a, stream);
   }
-  return launch_pk<D, G, 1, MW>(a, stream);
+  return launch_pk<T, D, G, 1, MW>(a, stream);
 }
 
-template <int D, int G>
+template <typename T, int D, int G>
 static hipError_t launch_pw(const PrefillArgs& a, hipStream_t stream) {
-  if (prefill_min_waves(G) == 8) return launch_ph<D, G, 8>(a, stream);
-  return launch_ph<D, G, 4>(a, stream);
+  if (prefill_min_waves(G) == 8) return launch_ph<T, D, G, 8>(a, stream);
+  return launch_ph<T, D, G, 4>(a, stream);
 }
 
-template <int D>
+template <typename T, int D>
 static hipError_t launch_pg(const PrefillArgs& a, hipStream_t stream) {
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: return launch_pw<D, 1>(a, stream);
-    case 2: return launch_pw<D, 2>(a, stream);
-    case 4: return launch_pw<D, 4>(a, stream);
-    case 8: return launch_pw<D, 8>(a, stream);
+    case 1: return launch_pw<T, D, 1>(a, stream);
+    case 2: return launch_pw<T, D, 2>(a, stream);
+    case 4: return launch_pw<T, D, 4>(a, stream);
+    case 8: return launch_pw<T, D, 8>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+static hipError_t launch_pd(const PrefillArgs& a, hipStream_t stream) {
+  switch (a.head_dim) {
+    case 64: return launch_pg<T, 64>(a, stream);
+    case 128: return launch_pg<T, 128>(a, stream);
+    case 256: return launch_pg<T, 256>(a, stream);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
-  switch (a.head_dim) {
-    case 64: return launch_pg<64>(a, stream);
-    case 128: return launch_pg<128>(a, stream);
-    case 256: return launch_pg<256>(a, stream);
-  }
-  return hipErrorInvalidValue;
+  return a.kv_fp8 ? launch_pd<FP8>(a, stream) : launch_pd<BF16>(a, stream);
 }
 
 }  // namespace pa

@@ -117,6 +117,10 @@ def _oracle_written_blocks(case, blocks, key_before, value_before):
     where = {blk: i for i, blk in enumerate(blocks)}
     local = np.array([where[int(s) // bs] * bs + int(s) % bs if int(s) // bs in where else -1
                       for s in case.slot_mapping.cpu().numpy()], dtype=np.int64)
+    if case.kv_fp8:
+        return oracle.fp8.reshape_and_cache_fp8_ref(
+            to_numpy_bits(case.new_keys[0]), to_numpy_bits(case.new_values[0]), kc, vc, local,
+            case.k_scales[0].cpu().numpy(), case.v_scales[0].cpu().numpy())
     return oracle.reshape_and_cache_ref(to_numpy_bits(case.new_keys[0]),
                                         to_numpy_bits(case.new_values[0]), kc, vc, local)
 
@@ -144,3 +148,33 @@ def oracle_prefill_rows(case, seq, rows, key_before, value_before):
         out.append(oracle.prefill_chunk_ref(qh[q0 + i:q0 + i + 1], kc, vc, table,
                                             np.array([visible]), np.array([0, 1]), case.scale)[0])
     return np.stack(out)
+
+
+def oracle_prefill_all_rows(case, seq, key_before, value_before):
+    """Oracle of every row of prefill sequence `seq`'s chunk (one oracle call
+    over the blocks of its whole context), on the caches as they were before
+    the device wrote the step's tokens plus the oracle's own write."""
+    p = case.prefill
+    b = case.num_decode_seqs + seq
+    n = int(case.layout.context_lens[b])
+    L = p.q_lens[seq]
+    q0 = int(np.sum(p.q_lens[:seq]))
+    bs = case.block_size
+    blocks = [int(x) for x in case.layout.block_tables[b, : -(-n // bs)]]
+    kc, vc = _oracle_written_blocks(case, blocks, key_before, value_before)
+    table = np.arange(len(blocks), dtype=np.int32)[None, :]
+    qh = to_numpy_bits(p.query)[q0:q0 + L]
+    if case.kv_fp8:
+        return oracle.fp8.prefill_chunk_fp8_ref(qh, kc, vc, case.k_scales[0].cpu().numpy(),
+                                                case.v_scales[0].cpu().numpy(), table,
+                                                np.array([n]), np.array([0, L]), case.scale)
+    return oracle.prefill_chunk_ref(qh, kc, vc, table, np.array([n]), np.array([0, L]),
+                                    case.scale)
+
+
+def gpu_prefill_fp8(case, **kw):
+    p = case.prefill
+    return pa.pa_prefill_chunk_fp8(p.query, case.key_caches[0], case.value_caches[0],
+                                   case.k_scales[0], case.v_scales[0], p.block_tables,
+                                   p.context_lens, p.cu_q_lens, p.max_q_len, case.scale,
+                                   int(max(int(x) for x in p.context_lens.cpu())), **kw)

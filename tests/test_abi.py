@@ -146,6 +146,30 @@ def test_prefill_zero_rows_is_noop(lib):
     assert lib.pa_prefill_chunk(*prefill_args(total_q=0, out=None)) == OK
 
 
+def fp8_prefill_args(**over):
+    args = dict(out=A, query=A, key_cache=A, value_cache=A, k_scale=A, v_scale=A, block_tables=A,
+                context_lens=A, cu_q_lens=A, num_seqs=1, total_q=512, max_q_len=512,
+                num_q_heads=16, num_kv_heads=4, head_dim=256, block_size=16,
+                max_blocks_per_seq=256, num_blocks=1000, max_context_len=4096, scale=0.0625,
+                query_dtype=BF16, workspace=A, workspace_bytes=1 << 30, stream=None)
+    args.update(over)
+    return list(args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(k_scale=None), NULL), (dict(v_scale=None), NULL), (dict(cu_q_lens=None), NULL),
+    (dict(total_q=-1), SHAPE), (dict(num_kv_heads=5), SHAPE), (dict(scale=float("nan")), SHAPE),
+    (dict(query_dtype=F32), UNSUP), (dict(head_dim=32), UNSUP), (dict(block_size=8), UNSUP),
+    (dict(out=A + 4), ALIGN), (dict(k_scale=A + 2), ALIGN), (dict(workspace_bytes=16), WORKSPACE),
+])
+def test_fp8_prefill_rejects(lib, over, code):
+    assert lib.pa_prefill_chunk_fp8(*fp8_prefill_args(**over)) == code
+
+
+def test_fp8_prefill_zero_rows_is_noop(lib):
+    assert lib.pa_prefill_chunk_fp8(*fp8_prefill_args(total_q=0, k_scale=None)) == OK
+
+
 def test_binding_raises_loudly_without_library(monkeypatch, tmp_path):
     import paged_kv_cache_215_amd._lib as L
     monkeypatch.setattr(L, "_lib", None)

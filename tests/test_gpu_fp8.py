@@ -1,6 +1,7 @@
 """GPU parity of the FP8 (E4M3) cache path through the C ABI: the quantizing
-scatter bit for bit against the oracle's quantizer, and decode over FP8
-caches within 1e-3 max-abs of the fp64 oracle on the dequantized cache."""
+scatter bit for bit against the oracle's quantizer, and decode and chunked
+prefill over FP8 caches within 1e-3 max-abs of the fp64 oracle on the
+dequantized cache."""
 
 import numpy as np
 import pytest
@@ -8,8 +9,8 @@ import torch
 
 import oracle
 import paged_kv_cache_215_amd as pa
-from gpu_helpers import (ATOL, gpu_decode_fp8, max_abs_err, oracle_decode,
-                         oracle_decode_after_write, say)
+from gpu_helpers import (ATOL, gpu_decode_fp8, gpu_prefill_fp8, max_abs_err, oracle_decode,
+                         oracle_decode_after_write, oracle_prefill_all_rows, say)
 from workloads import make_case, make_config_case, to_numpy_bits
 
 pytestmark = pytest.mark.gpu
@@ -172,9 +173,10 @@ def test_c5_write_then_attend():
     assert np.all(np.isfinite(got)) and err <= ATOL
 
 
-def test_c3_full_size_sampled():
+def test_c3_full_size_all_sequences():
     # one layer of the 64 x 8192-token step at full size, FP8 cache, in the
-    # benchmark's launch configuration; sampled sequences against the oracle
+    # benchmark's launch configuration; every sequence against the oracle (in
+    # chunks of 16 sequences, to bound host memory)
     case = make_config_case("c3_full_step", device=DEV, kv_fp8=True, num_layers=1)
     kb, vb = case.key_caches[0].clone(), case.value_caches[0].clone()
     pa.pa_reshape_and_cache_fp8(case.new_keys[0], case.new_values[0], case.key_caches[0],
@@ -182,12 +184,16 @@ def test_c3_full_size_sampled():
                                 case.v_scales[0])
     out = gpu_decode_fp8(case)
     torch.cuda.synchronize()
-    seqs = [0, 31, 63]
-    got = out.cpu().numpy()[seqs]
-    want = oracle_decode_after_write(case, kb, vb, seqs=seqs)
-    err = max_abs_err(got, want)
-    say(f"[fp8 decode] c3 sampled {seqs}: max-abs err {err:.3e}")
-    assert err <= ATOL
+    got_all = out.cpu().numpy()
+    assert np.all(np.isfinite(got_all))
+    S = case.num_decode_seqs
+    worst = 0.0
+    for s0 in range(0, S, 16):
+        seqs = list(range(s0, min(S, s0 + 16)))
+        want = oracle_decode_after_write(case, kb, vb, seqs=seqs)
+        worst = max(worst, max_abs_err(got_all[seqs], want))
+    say(f"[fp8 decode] c3, all {S} sequences: max-abs err {worst:.3e}")
+    assert worst <= ATOL
 
 
 def test_fp8_matches_bf16_decode_on_dequantized_cache():
@@ -216,3 +222,82 @@ def test_run_to_run_bit_identical():
     b = gpu_decode_fp8(case)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+# ---- chunked prefill over the FP8 cache ---------------------------------------------------
+
+def _write_chunk_fp8(case):
+    """Device FP8 write of the step's tokens; returns copies of the code caches
+    taken before it, from which the oracle makes its own write."""
+    before = (case.key_caches[0].clone(), case.value_caches[0].clone())
+    pa.pa_reshape_and_cache_fp8(case.new_keys[0], case.new_values[0], case.key_caches[0],
+                                case.value_caches[0], case.slot_mapping, case.k_scales[0],
+                                case.v_scales[0])
+    return before
+
+
+def _prefill_check(case):
+    kb, vb = _write_chunk_fp8(case)
+    out = gpu_prefill_fp8(case)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    p = case.prefill
+    worst = 0.0
+    for i in range(len(p.q_lens)):
+        q0 = int(np.sum(p.q_lens[:i]))
+        want = oracle_prefill_all_rows(case, i, kb, vb)
+        worst = max(worst, max_abs_err(got[q0:q0 + p.q_lens[i]], want))
+    say(f"[fp8 prefill] {case.name}: max-abs err {worst:.3e}")
+    assert worst <= ATOL
+
+
+@pytest.mark.parametrize("head_dim", [64, 128, 256])
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+@pytest.mark.parametrize("block_size", [16, 32])
+def test_prefill_shapes(head_dim, group, block_size):
+    # unaligned prefix and chunk lengths, several row tiles and key tiles
+    case = make_case(name=f"pf8_d{head_dim}_g{group}_bs{block_size}", seed=head_dim * group + 1,
+                     context_lens=[], num_q_heads=2 * group, num_kv_heads=2, head_dim=head_dim,
+                     block_size=block_size, device=DEV, kv_fp8=True, prefill_chunks=[(45, 37)])
+    _prefill_check(case)
+
+
+@pytest.mark.parametrize("chunks", [[(0, 1)], [(0, 70)], [(31, 33)], [(700, 130)],
+                                    [(50, 20), (0, 48), (400, 100), (17, 1)]])
+def test_prefill_edges_and_several_sequences(chunks):
+    case = make_case(name=f"pf8_edge_{chunks[0][0]}_{chunks[0][1]}_{len(chunks)}", seed=91,
+                     context_lens=[], num_q_heads=16, num_kv_heads=4, head_dim=256,
+                     block_size=16, device=DEV, kv_fp8=True, prefill_chunks=chunks)
+    _prefill_check(case)
+
+
+def test_prefill_c5_chunk_all_rows():
+    # the mixed step's 512-row chunk on its 3584-token prefix, FP8 cache, after
+    # the step's 767-token FP8 scatter; every row against the oracle
+    case = make_config_case("c5_mixed_step", device=DEV, kv_fp8=True)
+    _prefill_check(case)
+
+
+def test_prefill_fp8_matches_bf16_prefill_on_dequantized_cache():
+    # power-of-two scales: the dequantized cache is exactly a BF16 cache, so
+    # the two chunk kernels see the same numbers
+    case = make_case(name="pf8_vs_bf16", seed=93, context_lens=[], num_q_heads=16,
+                     num_kv_heads=4, head_dim=256, block_size=16, device=DEV, kv_fp8=True,
+                     prefill_chunks=[(300, 77), (1000, 16)])
+    ks = torch.tensor([1 / 64, 1 / 32, 1 / 128, 1 / 16], device=DEV)
+    vs = torch.tensor([1 / 32, 1 / 64, 1 / 16, 1 / 128], device=DEV)
+    case.k_scales[0], case.v_scales[0] = ks, vs
+    _write_chunk_fp8(case)
+    out8 = gpu_prefill_fp8(case)
+    kf = case.key_caches[0].view(torch.float8_e4m3fn).float() * ks[None, :, None, None]
+    vf = case.value_caches[0].view(torch.float8_e4m3fn).float() * vs[None, :, None, None]
+    p = case.prefill
+    # NaN codes in unowned slots dequantize to NaN in both views alike
+    out16 = pa.pa_prefill_chunk(p.query, kf.to(torch.bfloat16), vf.to(torch.bfloat16),
+                                p.block_tables, p.context_lens, p.cu_q_lens, p.max_q_len,
+                                case.scale, 1016)
+    torch.cuda.synchronize()
+    diff = float((out8 - out16).abs().max())
+    say(f"[fp8 prefill] fp8 vs bf16 chunk kernel: max diff {diff:.3e}")
+    assert diff <= 1e-5

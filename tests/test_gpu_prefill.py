@@ -7,7 +7,8 @@ import torch
 
 import oracle
 import paged_kv_cache_215_amd as pa
-from gpu_helpers import ATOL, gpu_prefill, max_abs_err, oracle_prefill_rows, say
+from gpu_helpers import (ATOL, gpu_prefill, max_abs_err, oracle_prefill_all_rows,
+                         oracle_prefill_rows, say)
 from workloads import make_case, make_config_case, to_numpy_bits
 
 pytestmark = pytest.mark.gpu
@@ -86,9 +87,9 @@ def test_single_row_matches_decode():
 
 
 @pytest.mark.parametrize("prefix", [3584, 3590])
-def test_c5_chunk_sampled(prefix):
+def test_c5_chunk_all_rows(prefix):
     # the mixed step's 512-row chunk on its 3584-token prefix (and an unaligned
-    # prefix), after the step's 767-token scatter; sampled rows against the oracle
+    # prefix), after the step's 767-token scatter; every row against the oracle
     if prefix == 3584:
         case = make_config_case("c5_mixed_step", device=DEV)
     else:
@@ -98,12 +99,12 @@ def test_c5_chunk_sampled(prefix):
     kb, vb = _write_chunk(case)
     out = gpu_prefill(case)
     torch.cuda.synchronize()
-    rows = [0, 1, 15, 16, 17, 255, 256, 300, 510, 511]
-    got = out.cpu().numpy()[rows]
-    want = oracle_prefill_rows(case, 0, rows, kb, vb)
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    want = oracle_prefill_all_rows(case, 0, kb, vb)
+    assert want.shape == got.shape
     err = max_abs_err(got, want)
-    say(f"[prefill] c5 prefix {prefix}: sampled max-abs err {err:.3e}")
-    assert np.all(np.isfinite(out.cpu().numpy()))
+    say(f"[prefill] c5 prefix {prefix}: all {got.shape[0]} rows, max-abs err {err:.3e}")
     assert err <= ATOL
 
 
