@@ -217,8 +217,6 @@ def run(args):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     fp8 = args.kv == "fp8"
-    if fp8 and args.workload == "c5_mixed_step":
-        raise SystemExit("the prefill chunk reads BF16 caches only: no FP8 line for c5_mixed_step")
     log(f"[bench] generating {args.workload} (kv {args.kv}) ...")
     case = make_config_case(args.workload, device=dev, kv_fp8=fp8)
     torch.cuda.synchronize()
@@ -273,16 +271,24 @@ def run(args):
                          case.block_tables, case.context_lens, case.scale, case.max_context_len,
                          out=outs[layer], workspace=workspace)
 
+    def prefill(layer):
+        if fp8:
+            pa.pa_prefill_chunk_fp8(pf.query, case.key_caches[layer], case.value_caches[layer],
+                                    case.k_scales[layer], case.v_scales[layer], pf.block_tables,
+                                    pf.context_lens, pf.cu_q_lens, pf.max_q_len, case.scale,
+                                    pf_ctx, out=pf_out, workspace=pf_ws)
+        else:
+            pa.pa_prefill_chunk(pf.query, case.key_caches[layer], case.value_caches[layer],
+                                pf.block_tables, pf.context_lens, pf.cu_q_lens, pf.max_q_len,
+                                case.scale, pf_ctx, out=pf_out, workspace=pf_ws)
+
     def step(dec_events=None, pf_events=None):
         for layer in range(L):
             if case.slot_mapping is not None:
                 write(layer)
             timed(dec_events, lambda: attend(layer))
             if pf is not None:
-                timed(pf_events, lambda: pa.pa_prefill_chunk(
-                    pf.query, case.key_caches[layer], case.value_caches[layer], pf.block_tables,
-                    pf.context_lens, pf.cu_q_lens, pf.max_q_len, case.scale, pf_ctx,
-                    out=pf_out, workspace=pf_ws))
+                timed(pf_events, lambda: prefill(layer))
 
     for _ in range(args.warmup):
         step()
@@ -350,8 +356,10 @@ def run(args):
             "head_dim": case.head_dim,
             "block_size": case.block_size,
             "kv_cache": "fp8_e4m3 (per-head scales)" if fp8 else "bf16",
-            "step": ("per layer: pa_reshape_and_cache_fp8(new token) + pa_decode_fp8" if fp8 else
-                     "per layer: pa_reshape_and_cache(new token) + pa_decode"),
+            "step": ("per layer: pa_reshape_and_cache_fp8(new tokens) + pa_decode_fp8" if fp8 else
+                     "per layer: pa_reshape_and_cache(new tokens) + pa_decode") +
+                    ((" + pa_prefill_chunk_fp8" if fp8 else " + pa_prefill_chunk")
+                     if pf is not None else ""),
         },
         "roofline": {
             "kernel": ("pa_decode_fp8" if fp8 else "pa_decode") +
@@ -390,7 +398,8 @@ def run(args):
         for pre, ql in zip(pf.prefix_lens, pf.q_lens):
             flop += 4 * case.num_q_heads * case.head_dim * sum(pre + i + 1 for i in range(ql))
         result["prefill"] = {
-            "kernel": "pa_prefill_chunk (prefill_kernel + prefill_merge_kernel)",
+            "kernel": ("pa_prefill_chunk_fp8" if fp8 else "pa_prefill_chunk") +
+                      " (prefill_kernel + prefill_merge_kernel)",
             "bound": "mfma",
             "avg_call_us": round(pf_s * 1e6, 2),
             "algorithmic_flop_per_call": flop,
@@ -705,16 +714,19 @@ def _engine_requests(scenario):
 
 
 def run_engine(args):
-    """Continuous batching on the GPU: the native scheduler's plans executed
-    eagerly and with decode-only iterations replayed from a captured graph."""
+    """Continuous batching on the GPU: the C++ driver runs the native
+    scheduler's plans eagerly and with decode-only iterations replayed from a
+    captured graph, over a BF16 or (--kv fp8) an FP8 cache."""
     import torch
-    from paged_kv_cache_215_amd.engine import Engine, NativeEngine
+    from paged_kv_cache_215_amd.engine import Engine
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     hq, hkv, d, bs = 16, 4, 256, 16
+    fp8 = args.kv == "fp8"
     result = {"metric": "continuous-batching generated tokens/s (eager vs graph replay), "
                         "1 MI355X", "unit": "tokens/s", "n_gpus": 1, "higher_is_better": True,
-              "data": "synthetic", "dtype": "bf16", "scenarios": {}}
+              "data": "synthetic", "dtype": "fp8_e4m3 kv, bf16 q" if fp8 else "bf16",
+              "scenarios": {}}
     for scenario in ("stragglers", "mixed"):
         reqs, cfg = _engine_requests(scenario)
         L = cfg["num_layers"]
@@ -733,40 +745,23 @@ def run_engine(args):
 
         out = {"requests": len(reqs), "layers": L, "max_batch": B, "chunk_tokens": C,
                "generated_tokens": int(sum(o for _, o in reqs))}
-        for mode in ("eager", "graph", "native_eager", "native_graph"):
-            native = mode.startswith("native")
-            graph = mode.endswith("graph")
-            cls = NativeEngine if native else Engine
-            eng = cls(reqs, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=bs,
-                      device=dev, use_graph=graph, **cfg)
-            if native:
-                # inputs produced in place in the engine's buffers (once: the
-                # values do not matter for timing)
-                for name in ("q_dec", "k_dec", "v_dec", "q_pre", "k_pre", "v_pre"):
-                    for layer in range(L):
-                        eng.inputs[name][layer].copy_(bank[name][layer])
-                inputs = None
-            else:
-                if graph:
-                    static = eng.static_decode_inputs()
-                    for name in ("q_dec", "k_dec", "v_dec"):
-                        for layer in range(L):
-                            static[name][layer].copy_(bank[name][layer])
-                src_dec = static if graph else bank
-
-                def inputs(plan, src_dec=src_dec):
-                    nd, nr = len(plan["decode_seqs"]), int(plan["prefill_cu"][-1])
-                    out = {k: [t[:nd] for t in src_dec[k]] for k in ("q_dec", "k_dec", "v_dec")}
-                    out.update({k: [t[:nr] for t in bank[k]] for k in ("q_pre", "k_pre", "v_pre")})
-                    return out
+        for mode in ("eager", "graph"):
+            graph = mode == "graph"
+            eng = Engine(reqs, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=bs,
+                         device=dev, use_graph=graph, kv_fp8=fp8, **cfg)
+            # inputs produced in place in the engine's buffers (once: the
+            # values do not matter for timing)
+            for name in ("q_dec", "k_dec", "v_dec", "q_pre", "k_pre", "v_pre"):
+                for layer in range(L):
+                    eng.inputs[name][layer].copy_(bank[name][layer])
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             host = 0.0
             preempted = decode_only = 0
-            with torch.cuda.stream(eng.stream if native else torch.cuda.current_stream()):
+            with torch.cuda.stream(eng.stream):
                 while not eng.done():
                     h0 = time.perf_counter()
-                    plan, _, _ = eng.step(inputs)
+                    plan, _, _ = eng.step()
                     host += time.perf_counter() - h0
                     preempted += len(plan["preempted"])
                     decode_only += int(len(plan["prefill_seqs"]) == 0)
@@ -782,12 +777,11 @@ def run_engine(args):
             del eng
             torch.cuda.empty_cache()
         out["graph_speedup"] = round(out["graph"]["tokens_per_s"] / out["eager"]["tokens_per_s"], 3)
-        out["native_graph_speedup"] = round(out["native_graph"]["tokens_per_s"] /
-                                            out["eager"]["tokens_per_s"], 3)
         result["scenarios"][scenario] = out
-    result["value"] = result["scenarios"]["mixed"]["native_graph"]["tokens_per_s"]
+    result["value"] = result["scenarios"]["mixed"]["graph"]["tokens_per_s"]
     result["config"] = {"component": "engine", "num_q_heads": hq, "num_kv_heads": hkv,
-                        "head_dim": d, "block_size": bs}
+                        "head_dim": d, "block_size": bs,
+                        "kv_cache": "fp8_e4m3 (per-head scales)" if fp8 else "bf16"}
     print(json.dumps(result), flush=True)
 
 

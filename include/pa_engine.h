@@ -27,7 +27,13 @@
  * Ownership: the caller owns every registered buffer and keeps it alive;
  * the engine allocates its own index buffers, staging (pinned) and
  * workspaces at creation and frees them in pa_engine_destroy. All work is
- * enqueued on the stream given at creation. BF16 caches only.
+ * enqueued on the stream given at creation.
+ *
+ * Caches: BF16, or FP8 (E4M3 codes, kv_fp8 = 1) with one float32 K and one V
+ * scale per KV head and layer. The model's inputs (queries, new K/V rows) are
+ * BF16 either way; an FP8 engine quantizes the new rows as it writes them
+ * (pa_reshape_and_cache_fp8) and attends with pa_prefill_chunk_fp8 and
+ * pa_decode_fp8; the host pools then hold codes too.
  */
 #ifndef PA_ENGINE_H
 #define PA_ENGINE_H
@@ -48,13 +54,14 @@ typedef struct {
   float scale;
   int32_t use_graph;              /* replay decode-only iterations from graphs */
   pa_sched_config sched;          /* pools, block size, batch, chunk budget */
+  int32_t kv_fp8;                 /* 1: E4M3 caches with per-head scales; 0: BF16 */
 } pa_engine_config;
 
 /* Arrays of num_layers pointers each (copied at creation). */
 typedef struct {
-  void* const* key_caches;        /* device BF16 [num_blocks, Hkv, bs, d] */
+  void* const* key_caches;        /* device [num_blocks, Hkv, bs, d], BF16 or E4M3 */
   void* const* value_caches;
-  void* const* host_keys;         /* pinned BF16 [num_host_blocks, Hkv, bs, d] */
+  void* const* host_keys;         /* pinned [num_host_blocks, Hkv, bs, d], as the caches */
   void* const* host_values;
   void* const* q_dec;             /* device BF16 [max_batch, Hq, d] */
   void* const* k_dec;             /* device BF16 [max_batch, Hkv, d] */
@@ -64,11 +71,14 @@ typedef struct {
   void* const* v_pre;
   float* const* out_dec;          /* device float32 [max_batch, Hq, d] */
   float* const* out_pre;          /* device float32 [chunk_tokens, Hq, d] */
+  const float* const* k_scales;   /* kv_fp8: device float32 [Hkv] per layer (else NULL) */
+  const float* const* v_scales;
 } pa_engine_buffers;
 
 /* Creates the engine: its scheduler, index buffers, pinned staging and
  * workspaces, and (use_graph) the captured decode-only graph. Returns
- * PA_ERR_NULL for a NULL cfg, bufs, out or pointer array; PA_ERR_SHAPE for
+ * PA_ERR_NULL for a NULL cfg, bufs, out or pointer array (the scale arrays
+ * only with kv_fp8); PA_ERR_SHAPE for
  * non-positive head counts or sizes, and the scheduler's own errors
  * (pa_sched_create); PA_ERR_UNSUPPORTED when pa_decode has no kernel for the
  * head shape or block size; PA_ERR_HIP when an allocation or the capture

@@ -22,10 +22,10 @@ HIP kernels behind the C ABI in ``include/pa.h``:
 * ``pa_swap_out`` / ``pa_swap_in`` - batched block moves between the device
                              cache and a pinned host pool (preemption);
 * ``Scheduler``            - the iteration-level batching scheduler (C++);
-* ``engine.Engine`` / ``engine.NativeEngine`` - step drivers that run the
-                             scheduler's plans on the GPU (the native one is
-                             the C++ driver of ``include/pa_engine.h``), with
-                             decode-only iterations replayed from a HIP graph.
+* ``engine.Engine``        - the C++ step driver of ``include/pa_engine.h``:
+                             runs the scheduler's plans on the GPU (BF16 or
+                             FP8 caches), with decode-only iterations
+                             replayed from a HIP graph.
 
 The Python functions below only marshal torch tensors to that ABI.
 """

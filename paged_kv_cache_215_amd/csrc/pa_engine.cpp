@@ -29,6 +29,7 @@ struct pa_engine {
   pa_engine_config cfg{};
   std::vector<void*> kc, vc, hk, hv, qd, kd, vd, qp, kp, vp;
   std::vector<float*> od, op;
+  std::vector<const float*> ks, vs;   // E4M3 caches: per-layer K / V scales
   pa_scheduler* sched = nullptr;
   hipStream_t stream = nullptr;
   int32_t B = 0, MB = 0, C = 0, capacity = 0;
@@ -64,19 +65,63 @@ pa_status_t hip_ok(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; 
     if (st_ != PA_OK) return st_;        \
   } while (0)
 
+// The library calls of one layer, for the engine's cache type (BF16, or E4M3
+// codes with the layer's scales; inputs are BF16 either way).
+pa_status_t write_rows(pa_engine* e, int l, const void* k, const void* v, const int64_t* slots,
+                       int32_t rows) {
+  const auto& c = e->cfg;
+  const auto& s = c.sched;
+  if (c.kv_fp8)
+    return pa_reshape_and_cache_fp8(k, v, e->kc[l], e->vc[l], slots, e->ks[l], e->vs[l], rows,
+                                    c.num_kv_heads, c.head_dim, s.block_size, s.num_blocks,
+                                    PA_DTYPE_BF16, e->stream);
+  return pa_reshape_and_cache(k, v, e->kc[l], e->vc[l], slots, rows, c.num_kv_heads, c.head_dim,
+                              s.block_size, s.num_blocks, PA_DTYPE_BF16, e->stream);
+}
+
+pa_status_t decode_layer(pa_engine* e, int l, int32_t rows, int32_t max_ctx) {
+  const auto& c = e->cfg;
+  const auto& s = c.sched;
+  const int32_t* tab = e->d_meta + e->o_dec_tab();
+  const int32_t* len = e->d_meta + e->o_dec_len();
+  if (c.kv_fp8)
+    return pa_decode_fp8(e->od[l], e->qd[l], e->kc[l], e->vc[l], e->ks[l], e->vs[l], tab, len,
+                         rows, c.num_q_heads, c.num_kv_heads, c.head_dim, s.block_size, e->MB,
+                         s.num_blocks, max_ctx, c.scale, PA_DTYPE_BF16, e->dec_ws,
+                         e->dec_ws_bytes, e->stream);
+  return pa_decode(e->od[l], e->qd[l], e->kc[l], e->vc[l], tab, len, rows, c.num_q_heads,
+                   c.num_kv_heads, c.head_dim, s.block_size, e->MB, s.num_blocks, max_ctx,
+                   c.scale, PA_DTYPE_BF16, e->dec_ws, e->dec_ws_bytes, e->stream);
+}
+
+pa_status_t prefill_layer(pa_engine* e, int l, int32_t n_pre, int32_t rows, int32_t max_q,
+                          int32_t max_ctx) {
+  const auto& c = e->cfg;
+  const auto& s = c.sched;
+  const int32_t* tab = e->d_meta + e->o_pre_tab();
+  const int32_t* ctx = e->d_meta + e->o_pre_ctx();
+  const int32_t* cu = e->d_meta + e->o_pre_cu();
+  if (c.kv_fp8)
+    return pa_prefill_chunk_fp8(e->op[l], e->qp[l], e->kc[l], e->vc[l], e->ks[l], e->vs[l], tab,
+                                ctx, cu, n_pre, rows, max_q, c.num_q_heads, c.num_kv_heads,
+                                c.head_dim, s.block_size, e->MB, s.num_blocks, max_ctx, c.scale,
+                                PA_DTYPE_BF16, e->pf_ws, e->pf_ws_bytes, e->stream);
+  return pa_prefill_chunk(e->op[l], e->qp[l], e->kc[l], e->vc[l], tab, ctx, cu, n_pre, rows,
+                          max_q, c.num_q_heads, c.num_kv_heads, c.head_dim, s.block_size, e->MB,
+                          s.num_blocks, max_ctx, c.scale, PA_DTYPE_BF16, e->pf_ws,
+                          e->pf_ws_bytes, e->stream);
+}
+
+pa_dtype_t cache_dtype(const pa_engine* e) {
+  return e->cfg.kv_fp8 ? PA_DTYPE_FP8_E4M3 : PA_DTYPE_BF16;
+}
+
 // Decode scatter + attention of every layer for B rows, reading slots and
 // tables from the device index buffers: the body of the decode-only graph.
 pa_status_t decode_body(pa_engine* e, int32_t rows, int32_t max_ctx) {
-  const auto& c = e->cfg;
-  const auto& s = c.sched;
-  for (int l = 0; l < c.num_layers; ++l) {
-    PA_TRY(pa_reshape_and_cache(e->kd[l], e->vd[l], e->kc[l], e->vc[l], e->d_slots, rows,
-                                c.num_kv_heads, c.head_dim, s.block_size, s.num_blocks,
-                                PA_DTYPE_BF16, e->stream));
-    PA_TRY(pa_decode(e->od[l], e->qd[l], e->kc[l], e->vc[l], e->d_meta + e->o_dec_tab(),
-                     e->d_meta + e->o_dec_len(), rows, c.num_q_heads, c.num_kv_heads, c.head_dim,
-                     s.block_size, e->MB, s.num_blocks, max_ctx, c.scale, PA_DTYPE_BF16, e->dec_ws,
-                     e->dec_ws_bytes, e->stream));
+  for (int l = 0; l < e->cfg.num_layers; ++l) {
+    PA_TRY(write_rows(e, l, e->kd[l], e->vd[l], e->d_slots, rows));
+    PA_TRY(decode_layer(e, l, rows, max_ctx));
   }
   return PA_OK;
 }
@@ -126,6 +171,7 @@ pa_status_t create_impl(const pa_engine_config* cfg, const pa_engine_buffers* b,
                          b->k_dec, b->v_dec, b->q_pre, b->k_pre, b->v_pre})
     if (!a) return PA_ERR_NULL;
   if (!b->out_dec || !b->out_pre) return PA_ERR_NULL;
+  if (cfg->kv_fp8 && (!b->k_scales || !b->v_scales)) return PA_ERR_NULL;
   e->cfg = *cfg;
   e->stream = static_cast<hipStream_t>(stream);
   auto take = [L](void* const* a, std::vector<void*>& v) { v.assign(a, a + L); };
@@ -141,6 +187,10 @@ pa_status_t create_impl(const pa_engine_config* cfg, const pa_engine_buffers* b,
   take(b->v_pre, e->vp);
   e->od.assign(b->out_dec, b->out_dec + L);
   e->op.assign(b->out_pre, b->out_pre + L);
+  if (cfg->kv_fp8) {
+    e->ks.assign(b->k_scales, b->k_scales + L);
+    e->vs.assign(b->v_scales, b->v_scales + L);
+  }
   const pa_sched_config& s = cfg->sched;
   pa_status_t status = pa_sched_create(&s, prompt_lens, output_lens, num_requests, &e->sched);
   if (status != PA_OK) return status;
@@ -230,11 +280,11 @@ pa_status_t execute_impl(pa_engine* e) {
   for (int l = 0; l < c.num_layers && p.num_swap_in; ++l)
     PA_TRY(pa_swap_in(e->kc[l], e->vc[l], e->hk[l], e->hv[l], in_pairs, p.num_swap_in,
                       c.num_kv_heads, c.head_dim, s.block_size, s.num_blocks, s.num_host_blocks,
-                      PA_DTYPE_BF16, e->stream));
+                      cache_dtype(e), e->stream));
   for (int l = 0; l < c.num_layers && p.num_swap_out; ++l)
     PA_TRY(pa_swap_out(e->kc[l], e->vc[l], e->hk[l], e->hv[l], out_pairs, p.num_swap_out,
                        c.num_kv_heads, c.head_dim, s.block_size, s.num_blocks, s.num_host_blocks,
-                       PA_DTYPE_BF16, e->stream));
+                       cache_dtype(e), e->stream));
 
   if (graph) {
     PA_TRY(hip_ok(hipMemcpyAsync(e->d_slots, st.slots, e->B * sizeof(int64_t),
@@ -285,25 +335,10 @@ pa_status_t execute_impl(pa_engine* e) {
   }
 
   for (int l = 0; l < c.num_layers; ++l) {
-    if (n_dec)
-      PA_TRY(pa_reshape_and_cache(e->kd[l], e->vd[l], e->kc[l], e->vc[l], e->d_slots, n_dec,
-                                  c.num_kv_heads, c.head_dim, s.block_size, s.num_blocks,
-                                  PA_DTYPE_BF16, e->stream));
-    if (rows)
-      PA_TRY(pa_reshape_and_cache(e->kp[l], e->vp[l], e->kc[l], e->vc[l], e->d_slots + e->B,
-                                  rows, c.num_kv_heads, c.head_dim, s.block_size, s.num_blocks,
-                                  PA_DTYPE_BF16, e->stream));
-    if (n_pre)
-      PA_TRY(pa_prefill_chunk(e->op[l], e->qp[l], e->kc[l], e->vc[l], e->d_meta + e->o_pre_tab(),
-                              e->d_meta + e->o_pre_ctx(), e->d_meta + e->o_pre_cu(), n_pre, rows,
-                              max_q, c.num_q_heads, c.num_kv_heads, c.head_dim, s.block_size,
-                              e->MB, s.num_blocks, max_pre_ctx, c.scale, PA_DTYPE_BF16, e->pf_ws,
-                              e->pf_ws_bytes, e->stream));
-    if (n_dec)
-      PA_TRY(pa_decode(e->od[l], e->qd[l], e->kc[l], e->vc[l], e->d_meta + e->o_dec_tab(),
-                       e->d_meta + e->o_dec_len(), n_dec, c.num_q_heads, c.num_kv_heads,
-                       c.head_dim, s.block_size, e->MB, s.num_blocks, max_dec_ctx, c.scale,
-                       PA_DTYPE_BF16, e->dec_ws, e->dec_ws_bytes, e->stream));
+    if (n_dec) PA_TRY(write_rows(e, l, e->kd[l], e->vd[l], e->d_slots, n_dec));
+    if (rows) PA_TRY(write_rows(e, l, e->kp[l], e->vp[l], e->d_slots + e->B, rows));
+    if (n_pre) PA_TRY(prefill_layer(e, l, n_pre, rows, max_q, max_pre_ctx));
+    if (n_dec) PA_TRY(decode_layer(e, l, n_dec, max_dec_ctx));
   }
   PA_TRY(hip_ok(hipEventRecord(st.done, e->stream)));
   st.used = true;

@@ -1,9 +1,11 @@
-"""GPU parity of the continuous-batching step driver: a request set that forces
-chunked prefill and preemption (swap out / swap in) runs to completion on the
-engine (eager, and with decode-only iterations replayed from one captured
-graph); an oracle replay - its own scheduler, scatter, block moves and
-attention, starting from the same empty pools - must agree at every
-iteration: outputs within 1e-3, the device cache byte for byte."""
+"""GPU parity of the continuous-batching step driver (the C++ driver of
+include/pa_engine.h): a request set that forces chunked prefill and
+preemption (swap out / swap in) runs to completion on the engine (eager, and
+with decode-only iterations replayed from one captured graph), over BF16 and
+over FP8 caches; an oracle replay - its own scheduler, scatter (quantizing for
+FP8), block moves and attention, starting from the same empty pools - must
+agree at every iteration: outputs within 1e-3, the device cache byte for
+byte."""
 
 import numpy as np
 import pytest
@@ -13,7 +15,7 @@ import oracle
 from gpu_helpers import ATOL, max_abs_err, say
 from oracle.block_manager import move_blocks_ref
 from oracle.scheduler import SchedulerRef
-from paged_kv_cache_215_amd.engine import Engine, NativeEngine
+from paged_kv_cache_215_amd.engine import Engine
 from workloads import to_numpy_bits
 
 pytestmark = pytest.mark.gpu
@@ -58,9 +60,15 @@ class Inputs:
         return out
 
 
+# per-layer, per-head FP8 scales (any positive float32 values)
+K_SCALES = [[1 / 64, 1 / 40, 1 / 96, 0.02], [1 / 50, 1 / 64, 0.015, 1 / 32]]
+V_SCALES = [[1 / 32, 0.03, 1 / 64, 1 / 80], [0.025, 1 / 48, 1 / 64, 1 / 40]]
+
+
 class OracleReplay:
-    def __init__(self, reqs, cfg):
+    def __init__(self, reqs, cfg, kv_fp8=False):
         self.cfg = cfg
+        self.fp8 = kv_fp8
         self.sched = SchedulerRef(reqs, num_blocks=cfg["num_blocks"],
                                   num_host_blocks=cfg["num_host_blocks"],
                                   block_size=cfg["block_size"],
@@ -69,10 +77,13 @@ class OracleReplay:
         shape = (cfg["num_blocks"], cfg["num_kv_heads"], cfg["block_size"], cfg["head_dim"])
         hshape = (cfg["num_host_blocks"],) + shape[1:]
         Lc = cfg["num_layers"]
-        self.kc = [np.zeros(shape, np.uint16) for _ in range(Lc)]
-        self.vc = [np.zeros(shape, np.uint16) for _ in range(Lc)]
-        self.hk = [np.zeros(hshape, np.uint16) for _ in range(Lc)]
-        self.hv = [np.zeros(hshape, np.uint16) for _ in range(Lc)]
+        t = np.uint8 if kv_fp8 else np.uint16
+        self.kc = [np.zeros(shape, t) for _ in range(Lc)]
+        self.vc = [np.zeros(shape, t) for _ in range(Lc)]
+        self.hk = [np.zeros(hshape, t) for _ in range(Lc)]
+        self.hv = [np.zeros(hshape, t) for _ in range(Lc)]
+        self.ks = [np.asarray(x, dtype=np.float32) for x in K_SCALES[:Lc]]
+        self.vs = [np.asarray(x, dtype=np.float32) for x in V_SCALES[:Lc]]
 
     def step(self, inputs):
         plan = self.sched.step()
@@ -95,8 +106,13 @@ class OracleReplay:
                                         to_numpy_bits(inputs["k_dec"][layer])])
                 v_new = np.concatenate([to_numpy_bits(inputs["v_pre"][layer]),
                                         to_numpy_bits(inputs["v_dec"][layer])])
-                self.kc[layer], self.vc[layer] = oracle.reshape_and_cache_ref(
-                    k_new, v_new, self.kc[layer], self.vc[layer], slots)
+                if self.fp8:
+                    self.kc[layer], self.vc[layer] = oracle.fp8.reshape_and_cache_fp8_ref(
+                        k_new, v_new, self.kc[layer], self.vc[layer], slots, self.ks[layer],
+                        self.vs[layer])
+                else:
+                    self.kc[layer], self.vc[layer] = oracle.reshape_and_cache_ref(
+                        k_new, v_new, self.kc[layer], self.vc[layer], slots)
             cap = cfg["max_blocks_per_seq"]
 
             def tables(seqs):
@@ -106,25 +122,36 @@ class OracleReplay:
                 seqs = [c["seq"] for c in plan["prefill"]]
                 ctx = np.array([c["start"] + c["rows"] for c in plan["prefill"]])
                 cu = np.concatenate([[0], np.cumsum([c["rows"] for c in plan["prefill"]])])
-                pre_out.append(oracle.prefill_chunk_ref(
-                    to_numpy_bits(inputs["q_pre"][layer]), self.kc[layer], self.vc[layer],
-                    tables(seqs), ctx, cu, scale))
+                q = to_numpy_bits(inputs["q_pre"][layer])
+                if self.fp8:
+                    pre_out.append(oracle.fp8.prefill_chunk_fp8_ref(
+                        q, self.kc[layer], self.vc[layer], self.ks[layer], self.vs[layer],
+                        tables(seqs), ctx, cu, scale))
+                else:
+                    pre_out.append(oracle.prefill_chunk_ref(
+                        q, self.kc[layer], self.vc[layer], tables(seqs), ctx, cu, scale))
             if plan["decode"]:
                 seqs = [d["seq"] for d in plan["decode"]]
                 ctx = np.array([d["context"] for d in plan["decode"]])
-                dec_out.append(oracle.decode_ref(
-                    to_numpy_bits(inputs["q_dec"][layer]), self.kc[layer], self.vc[layer],
-                    tables(seqs), ctx, scale))
+                q = to_numpy_bits(inputs["q_dec"][layer])
+                if self.fp8:
+                    dec_out.append(oracle.fp8.decode_fp8_ref(
+                        q, self.kc[layer], self.vc[layer], self.ks[layer], self.vs[layer],
+                        tables(seqs), ctx, scale))
+                else:
+                    dec_out.append(oracle.decode_ref(q, self.kc[layer], self.vc[layer],
+                                                     tables(seqs), ctx, scale))
         return plan, dec_out, pre_out
 
 
-@pytest.mark.parametrize("kind", ["python", "native"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
 @pytest.mark.parametrize("use_graph", [False, True])
-def test_engine_matches_oracle_replay(use_graph, kind):
+def test_engine_matches_oracle_replay(use_graph, kv):
     reqs = _requests()
-    cls = NativeEngine if kind == "native" else Engine
-    eng = cls(reqs, device=DEV, use_graph=use_graph, **CFG)
-    ref = OracleReplay(reqs, CFG)
+    fp8 = kv == "fp8"
+    scales = dict(kv_fp8=True, k_scales=K_SCALES, v_scales=V_SCALES) if fp8 else {}
+    eng = Engine(reqs, device=DEV, use_graph=use_graph, **scales, **CFG)
+    ref = OracleReplay(reqs, CFG, kv_fp8=fp8)
     inputs = Inputs(CFG)
     it = preempted = replays = worst = 0
     while not eng.done():
@@ -147,14 +174,13 @@ def test_engine_matches_oracle_replay(use_graph, kind):
     for layer in range(CFG["num_layers"]):
         assert np.array_equal(to_numpy_bits(eng.host_keys[layer]), ref.hk[layer])
         assert np.array_equal(to_numpy_bits(eng.host_values[layer]), ref.hv[layer])
-    say(f"[engine {kind} graph={use_graph}] {it} iterations, {preempted} preemptions, "
+    say(f"[engine {kv} graph={use_graph}] {it} iterations, {preempted} preemptions, "
         f"{replays} graph replays, worst max-abs err {worst:.3e}")
     assert preempted > 0
     if use_graph:
         assert replays > 0
-    if kind == "native":
-        assert eng.iterations == it
-        assert eng.graph_launches == (replays if use_graph else 0)
+    assert eng.iterations == it
+    assert eng.graph_launches == (replays if use_graph else 0)
     eng.close()
 
 
