@@ -15,6 +15,12 @@ definitions state:
 * ``paged_ref.decode_ref``            - one-query-per-sequence attention walked
                                         through a block table, two-pass softmax.
 * ``paged_ref.prefill_chunk_ref``     - causal query chunk against the cache.
+* ``paged_ref.attention_partial_ref`` / ``merge_partials_ref`` - the partial
+                                        result of one context split and the
+                                        log-sum-exp merge of partials.
+* ``paged_ref.decode_shared_prefix_ref`` - decode of copy-on-write groups as a
+                                        shared-prefix partial (first member's
+                                        table) merged with each tail.
 * ``dense_ref.dense_attention_ref``   - the same attention as a matrix formula
                                         on contiguous K/V (no block table).
 * ``accounting``                      - KV footprint closed form and slot
@@ -48,4 +54,11 @@ from .accounting import (  # noqa: F401
 from . import block_manager, fp8, scheduler  # noqa: F401
 from .dense_ref import dense_attention_ref  # noqa: F401
 from .numerics import bf16_bits_to_f64, to_f64  # noqa: F401
-from .paged_ref import decode_ref, prefill_chunk_ref, reshape_and_cache_ref  # noqa: F401
+from .paged_ref import (  # noqa: F401
+    attention_partial_ref,
+    decode_ref,
+    decode_shared_prefix_ref,
+    merge_partials_ref,
+    prefill_chunk_ref,
+    reshape_and_cache_ref,
+)

@@ -155,3 +155,73 @@ def prefill_chunk_ref(query, key_cache, value_cache, block_tables, context_lens,
                     scores = scale * (keys[:visible] @ q_all[cu[b] + i, h])
                     out[cu[b] + i, h] = _softmax_weighted_sum(scores, vals[:visible])
     return out
+
+
+def attention_partial_ref(query_row, keys, values, scale):
+    """One partial result of attention over a subset of a row's keys, the
+    quantity a context split produces: with s_j = scale * q . k_j,
+    m = max_j s_j, l = sum_j exp(s_j - m), o = sum_j exp(s_j - m) v_j / l.
+    An empty subset gives (o = 0, m = -inf, l = 0).
+
+    query_row: [d] float64; keys, values: [n, d] float64. Returns (o, m, l)."""
+    if keys.shape[0] == 0:
+        return np.zeros(values.shape[1]), -np.inf, 0.0
+    s = scale * (keys @ query_row)
+    m = np.max(s)
+    p = np.exp(s - m)
+    return (p @ values) / np.sum(p), m, float(np.sum(p))
+
+
+def merge_partials_ref(partials):
+    """Attention over the union of disjoint key subsets from their partials
+    (o_i, m_i, l_i): with M = max_i m_i and w_i = l_i exp(m_i - M),
+    out = sum_i w_i o_i / sum_i w_i. Empty partials (l_i = 0) contribute
+    nothing; if every partial is empty the result is 0 (an empty context)."""
+    live = [(o, m, l) for o, m, l in partials if l > 0]
+    if not live:
+        return np.zeros_like(partials[0][0])
+    big_m = max(m for _, m, _ in live)
+    w = [l * np.exp(m - big_m) for _, m, l in live]
+    return sum(wi * o for wi, (o, _, _) in zip(w, live)) / sum(w)
+
+
+def decode_shared_prefix_ref(query, key_cache, value_cache, block_tables, context_lens,
+                             cu_groups, prefix_lens, scale):
+    """Decode for sequences grouped by a shared prompt, evaluated the way the
+    sharing allows: group g is sequences cu_groups[g] .. cu_groups[g+1] - 1,
+    whose first P_g = prefix_lens[g] positions hold the same K/V (forked
+    rollouts of one prompt point at the prompt's physical blocks: How vLLM
+    gets real throughput on H100s, "PagedAttention borrows from operating
+    systems"; Dissecting vLLM, "PagedAttention: Virtual Memory for KV
+    Cache"). For a member b with n_b tokens, one partial covers positions
+    0 .. min(P_g, n_b) - 1, read through the group's FIRST member's table, and
+    one covers P_g .. n_b - 1 through b's own table; the two are merged with
+    merge_partials_ref. Sequences in no group are attended as in decode_ref.
+    When the prefix really is shared this equals decode_ref up to rounding
+    order (the merge is exact); it is the definition the grouped device path
+    follows, checked against decode_ref by the pins."""
+    q_all = to_f64(query)
+    num_seqs, num_q_heads, head_dim = q_all.shape
+    num_kv_heads = key_cache.shape[1]
+    group = num_q_heads // num_kv_heads
+    out = np.zeros((num_seqs, num_q_heads, head_dim), dtype=np.float64)
+    cu = np.asarray(cu_groups).astype(np.int64)
+    owner = {}  # sequence -> (first member, prefix length)
+    for g in range(len(cu) - 1):
+        for b in range(int(cu[g]), int(cu[g + 1])):
+            owner[b] = (int(cu[g]), int(prefix_lens[g]))
+    for b in range(num_seqs):
+        n = int(context_lens[b])
+        first, p_len = owner.get(b, (b, 0))
+        shared = min(p_len, n)
+        for kv in range(num_kv_heads):
+            k_pre = _gather_sequence(key_cache, block_tables[first], shared, kv)
+            v_pre = _gather_sequence(value_cache, block_tables[first], shared, kv)
+            k_all = _gather_sequence(key_cache, block_tables[b], n, kv)
+            v_all = _gather_sequence(value_cache, block_tables[b], n, kv)
+            k_tail, v_tail = k_all[shared:], v_all[shared:]
+            for h in range(kv * group, (kv + 1) * group):
+                parts = [attention_partial_ref(q_all[b, h], k_pre, v_pre, scale),
+                         attention_partial_ref(q_all[b, h], k_tail, v_tail, scale)]
+                out[b, h] = merge_partials_ref(parts)
+    return out
