@@ -260,7 +260,29 @@ def run(args):
                                     case.key_caches[layer], case.value_caches[layer],
                                     case.slot_mapping)
 
+    # Copy-on-write groups (the shared prompts of forked rollouts), found from
+    # the block tables on the host before timing: such a batch is decoded
+    # with pa_decode_shared, which reads each group's shared blocks once.
+    groups = None
+    if not args.no_shared_prefix:
+        cu, pl, mg, mp = pa.find_shared_prefixes(case.layout.block_tables[:S],
+                                                 case.layout.context_lens[:S], case.block_size)
+        if len(pl):
+            groups = (torch.as_tensor(cu, device=dev), torch.as_tensor(pl, device=dev), mg, mp)
+            workspace = pa.decode_shared_workspace(S, case.num_q_heads, case.num_kv_heads,
+                                                   case.head_dim, case.block_size,
+                                                   case.max_context_len, len(pl), mg, mp, dev)
+            log(f"[bench] {len(pl)} copy-on-write groups (largest {mg}, prefix {mp}): "
+                f"pa_decode_shared")
+
     def attend(layer):
+        if groups is not None:
+            kw = dict(k_scale=case.k_scales[layer], v_scale=case.v_scales[layer]) if fp8 else {}
+            pa.pa_decode_shared(case.queries[layer], case.key_caches[layer],
+                                case.value_caches[layer], case.block_tables, case.context_lens,
+                                groups[0], groups[1], groups[2], groups[3], case.scale,
+                                case.max_context_len, out=outs[layer], workspace=workspace, **kw)
+            return
         if fp8:
             pa.pa_decode_fp8(case.queries[layer], case.key_caches[layer], case.value_caches[layer],
                              case.k_scales[layer], case.v_scales[layer], case.block_tables,
@@ -356,15 +378,19 @@ def run(args):
             "head_dim": case.head_dim,
             "block_size": case.block_size,
             "kv_cache": "fp8_e4m3 (per-head scales)" if fp8 else "bf16",
-            "step": ("per layer: pa_reshape_and_cache_fp8(new tokens) + pa_decode_fp8" if fp8 else
-                     "per layer: pa_reshape_and_cache(new tokens) + pa_decode") +
+            "step": ("per layer: " +
+                     ("pa_reshape_and_cache_fp8(new tokens) + " if fp8 and case.slot_mapping is not None else
+                      "pa_reshape_and_cache(new tokens) + " if case.slot_mapping is not None else "") +
+                     ("pa_decode_shared" if groups is not None else
+                      "pa_decode_fp8" if fp8 else "pa_decode")) +
                     ((" + pa_prefill_chunk_fp8" if fp8 else " + pa_prefill_chunk")
                      if pf is not None else ""),
         },
         "roofline": {
-            "kernel": ("pa_decode_fp8" if fp8 else "pa_decode") +
-                      f" ({decode_kernel_name(fp8, case.num_q_heads // case.num_kv_heads, case.head_dim, elem == 4)}"
-                      " + decode_merge_kernel)",
+            "kernel": (("pa_decode_shared (prefill_kernel prefix pass + " if groups is not None else
+                        ("pa_decode_fp8 (" if fp8 else "pa_decode (")) +
+                       f"{decode_kernel_name(fp8, case.num_q_heads // case.num_kv_heads, case.head_dim, elem == 4)}"
+                       " + decode_merge_kernel)"),
             "bound": "hbm",
             "achieved": round(achieved_gbs, 1),
             "peak": HBM_PEAK_GBS,
@@ -800,6 +826,9 @@ def main():
                          "batching engine, or block copies and swaps")
     ap.add_argument("--kv", choices=["bf16", "fp8"], default="bf16",
                     help="KV cache element type (fp8: E4M3 codes with per-head scales)")
+    ap.add_argument("--no-shared-prefix", action="store_true",
+                    help="decode copy-on-write batches with plain pa_decode (every member "
+                         "reads the shared prompt) instead of pa_decode_shared")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-layers", type=int, default=4)
     ap.add_argument("--copy-calib", action="store_true",

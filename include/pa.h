@@ -195,6 +195,62 @@ pa_status_t pa_decode_noalloc(float* out, const void* query,
 size_t pa_decode_noalloc_max_bytes(void);
 
 /*
+ * Decode of a batch that holds copy-on-write groups: sequences forked from
+ * one prompt point at the prompt's physical blocks (How vLLM gets real
+ * throughput on H100s, "PagedAttention borrows from operating systems";
+ * Dissecting vLLM, "PagedAttention: Virtual Memory for KV Cache"), so the
+ * shared blocks need to be read once per group, not once per member. The
+ * result is pa_decode's (pa_decode_fp8's for an E4M3 cache); only the order
+ * of the arithmetic differs:
+ *   1. a shared-prefix pass on the matrix cores: for each group, its members'
+ *      queries (G heads each) are the rows of one product over the group's
+ *      shared blocks, read through the FIRST member's table; member b sees
+ *      positions below min(prefix, n_b);
+ *   2. the decode kernels over each member's private tail (positions from
+ *      the prefix on), and over every ungrouped sequence in full;
+ *   3. the merge of both partial results by log-sum-exp.
+ * Groups (device int32 arrays):
+ *   cu_groups    [num_groups + 1], non-decreasing, within [0, num_seqs]:
+ *                group g is sequences cu_groups[g] .. cu_groups[g+1] - 1
+ *                (sequences outside [cu_groups[0], cu_groups[num_groups])
+ *                are in no group); bounds outside the batch are clamped;
+ *   prefix_lens  [num_groups]: positions 0 .. prefix_lens[g] - 1 hold the same
+ *                K/V in every member (their blocks are shared). Only whole
+ *                blocks count: the prefix is rounded down to a multiple of
+ *                block_size (a partly filled last prompt block is attended
+ *                with each tail). 0 = nothing shared.
+ *   max_group_size  upper bound of the members of any group whose prefix is
+ *                at least one block; max_prefix_len upper bound of
+ *                prefix_lens. Both size the launch (host values).
+ * Other arguments as pa_decode / pa_decode_fp8: cache_dtype is
+ * PA_DTYPE_BF16 (k_scale, v_scale ignored) or PA_DTYPE_FP8_E4M3 (scales
+ * required); the query is BF16. At most 4096 sequences per call. num_groups
+ * = 0 is a plain decode. The workspace is pa_decode_shared_workspace_size
+ * bytes (a decode workspace, initialised once as with pa_decode_workspace_init,
+ * followed by the prefix pass's partials).
+ */
+size_t pa_decode_shared_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t block_size, int32_t max_context_len,
+                                       int32_t num_groups, int32_t max_group_size,
+                                       int32_t max_prefix_len);
+
+pa_status_t pa_decode_shared(float* out, const void* query,
+                             const void* key_cache, const void* value_cache,
+                             const float* k_scale, const float* v_scale,
+                             const int32_t* block_tables,
+                             const int32_t* context_lens,
+                             const int32_t* cu_groups, const int32_t* prefix_lens,
+                             int32_t num_groups, int32_t max_group_size,
+                             int32_t max_prefix_len, int32_t num_seqs,
+                             int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size,
+                             int32_t max_blocks_per_seq, int64_t num_blocks,
+                             int32_t max_context_len, float scale,
+                             pa_dtype_t cache_dtype, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
  * FP8 KV cache. Quantizing the cache to FP8 halves the bytes every decode
  * step re-reads, which the pages count as doubling the effective memory
  * bandwidth (vLLM architecture, memory and benchmarks deep dive,

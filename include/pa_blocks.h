@@ -94,6 +94,26 @@ pa_status_t pa_bm_tables(const pa_block_manager* bm, const int64_t* seqs, int32_
 int64_t pa_bm_take_copies(pa_block_manager* bm, int64_t* pairs, int64_t max_pairs);
 
 /*
+ * Copy-on-write groups of a decode batch, for pa_decode_shared, from its block
+ * tables and lengths (host arrays; the block manager hands forked sequences
+ * the same physical blocks for their shared prompt): maximal runs of
+ * consecutive sequences whose tables start with the same blocks as the run's
+ * first sequence, for at least min_blocks blocks within every member's
+ * context. A run's prefix is the number of leading blocks every member shares
+ * with the first, times block_size. Runs of one sequence are not groups;
+ * sequences between two runs become one group with prefix 0. Writes
+ * cu_groups[0 .. G] (capacity num_seqs + 1), prefix_lens[0 .. G - 1]
+ * (capacity num_seqs), and the largest member count and prefix of the groups
+ * with a non-zero prefix; returns G (0: nothing shared), or -1 for invalid
+ * arguments.
+ */
+int32_t pa_find_shared_prefixes(const int32_t* block_tables, const int32_t* context_lens,
+                                int32_t num_seqs, int32_t max_blocks_per_seq,
+                                int32_t block_size, int32_t min_blocks, int32_t* cu_groups,
+                                int32_t* prefix_lens, int32_t* max_group_size,
+                                int32_t* max_prefix_len);
+
+/*
  * Device copy of whole blocks, K and V: for each pair (src, dst) of
  * pairs[num_pairs][2] (int64, device), block dst of both caches (all heads,
  * all rows) receives block src's bytes. A pair with an index outside

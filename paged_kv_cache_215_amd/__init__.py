@@ -10,6 +10,12 @@ HIP kernels behind the C ABI in ``include/pa.h``:
                              separate merge kernel;
 * ``pa_prefill_chunk``     - a causal query chunk against the paged cache on
                              the matrix cores;
+* ``pa_decode_shared``     - decode of a batch with copy-on-write groups: each
+                             group's shared prompt blocks read once for all
+                             its members (a matrix-core pass), each member's
+                             tail by the decode kernels, merged by
+                             log-sum-exp; ``find_shared_prefixes`` finds the
+                             groups from the block tables;
 * ``pa_decode_noalloc``    - ``pa_decode`` on a static scratch inside the
                              library, for callers that cannot allocate;
 * ``pa_reshape_and_cache_fp8`` / ``pa_decode_fp8`` / ``pa_prefill_chunk_fp8``
@@ -47,6 +53,10 @@ from ._lib import (  # noqa: F401
     pa_decode,
     pa_decode_fp8,
     pa_decode_noalloc,
+    pa_decode_shared,
+    pa_decode_shared_workspace_size,
+    decode_shared_workspace,
+    find_shared_prefixes,
     pa_decode_workspace_init,
     pa_decode_workspace_size,
     pa_prefill_chunk,

@@ -38,6 +38,12 @@ SIGNATURES = {
     "pa_decode_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                  _i32, _i64, _i32, _f32, _i32, _vp]),
     "pa_decode_noalloc_max_bytes": (_sz, []),
+    "pa_decode_shared_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                              _i32]),
+    "pa_decode_shared": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                _i32, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _f32, _i32, _vp,
+                                _sz, _vp]),
+    "pa_find_shared_prefixes": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
     "pa_reshape_and_cache_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                         _i64, _i32, _vp]),
     "pa_decode_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
@@ -222,6 +228,82 @@ def pa_decode_noalloc(query, key_cache, value_cache, block_tables, context_lens,
         _ptr(context_lens), num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
         block_tables.shape[1], num_blocks, int(max_context_len), float(scale),
         _dtype_code(query), _stream(dev)))
+    return out
+
+
+def find_shared_prefixes(block_tables, context_lens, block_size, min_blocks=1):
+    """Copy-on-write groups of a decode batch from its host block tables and
+    lengths (numpy int32 arrays): (cu_groups, prefix_lens, max_group_size,
+    max_prefix_len) as numpy int32 arrays and ints; no groups -> empty arrays."""
+    import numpy as np
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
+    S = int(ctx.size)
+    cu = np.zeros(S + 1, dtype=np.int32)
+    pl = np.zeros(max(S, 1), dtype=np.int32)
+    mg, mp = ctypes.c_int32(0), ctypes.c_int32(0)
+    g = lib().pa_find_shared_prefixes(bt.ctypes.data_as(_vp), ctx.ctypes.data_as(_vp), S,
+                                      bt.shape[1], block_size, min_blocks,
+                                      cu.ctypes.data_as(_vp), pl.ctypes.data_as(_vp),
+                                      ctypes.byref(mg), ctypes.byref(mp))
+    if g < 0:
+        raise ValueError("pa_find_shared_prefixes: invalid arguments")
+    if g == 0:
+        return cu[:0], pl[:0], 0, 0
+    return cu[:g + 1].copy(), pl[:g].copy(), int(mg.value), int(mp.value)
+
+
+def pa_decode_shared_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                    max_context_len, num_groups, max_group_size, max_prefix_len):
+    return int(lib().pa_decode_shared_workspace_size(num_seqs, num_q_heads, num_kv_heads,
+                                                     head_dim, block_size, max_context_len,
+                                                     num_groups, max_group_size, max_prefix_len))
+
+
+def decode_shared_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                            max_context_len, num_groups, max_group_size, max_prefix_len, device):
+    """An initialised workspace for pa_decode_shared, reusable across calls."""
+    need = pa_decode_shared_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                           block_size, max_context_len, num_groups,
+                                           max_group_size, max_prefix_len)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    pa_decode_workspace_init(ws)
+    return ws
+
+
+def pa_decode_shared(query, key_cache, value_cache, block_tables, context_lens, cu_groups,
+                     prefix_lens, max_group_size, max_prefix_len, scale, max_context_len,
+                     k_scale=None, v_scale=None, out=None, workspace=None):
+    """Decode over a batch with copy-on-write groups (cu_groups, prefix_lens:
+    int32 device tensors); an FP8 cache (uint8 codes) takes k_scale / v_scale.
+    Returns float32 [S, Hq, d]."""
+    fp8 = key_cache.dtype in (torch.uint8, torch.float8_e4m3fn)
+    tensors = [query, key_cache, value_cache, block_tables, context_lens, cu_groups, prefix_lens]
+    if fp8:
+        _scales(k_scale, v_scale)
+        tensors += [k_scale, v_scale]
+    dev = _dev(*tensors)
+    for t in (block_tables, context_lens, cu_groups, prefix_lens):
+        if t.dtype != torch.int32:
+            raise TypeError("tables, lengths and group arrays must be int32")
+    num_seqs, num_q_heads, head_dim = query.shape
+    num_blocks, num_kv_heads, block_size, _ = key_cache.shape
+    num_groups = prefix_lens.numel()
+    if out is None:
+        out = torch.empty((num_seqs, num_q_heads, head_dim), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = decode_shared_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                            block_size, max_context_len, num_groups,
+                                            max_group_size, max_prefix_len, dev)
+    _dev(out, workspace)
+    _check("pa_decode_shared", lib().pa_decode_shared(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
+        _ptr(k_scale if fp8 else None), _ptr(v_scale if fp8 else None), _ptr(block_tables),
+        _ptr(context_lens), _ptr(cu_groups), _ptr(prefix_lens), num_groups, int(max_group_size),
+        int(max_prefix_len), num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+        block_tables.shape[1], num_blocks, int(max_context_len), float(scale),
+        PA_DTYPE_FP8_E4M3 if fp8 else _dtype_code(key_cache), _ptr(workspace), workspace.numel(),
+        _stream(dev)))
     return out
 
 

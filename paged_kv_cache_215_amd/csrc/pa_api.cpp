@@ -166,6 +166,42 @@ void* scratch_on_current_device() {
   return p;
 }
 
+// Copy-on-write groups of a grouped decode (pa_decode_shared).
+struct GroupSpec {
+  const int32_t* cu_groups;
+  const int32_t* prefix_lens;
+  int32_t num_groups;
+  int32_t max_group_size;
+  int32_t max_prefix_len;
+};
+
+// Workspace of a grouped decode: the decode workspace, then each sequence's
+// tail start, then the prefix pass's partials [S, Hq, splits, D] and
+// [S, Hq, splits, 2].
+struct SharedGeometry {
+  DecodeGeometry dec;
+  int splits;
+  size_t seq_start_off;
+  size_t pre_o_off;
+  size_t pre_ml_off;
+  size_t bytes;
+};
+
+SharedGeometry shared_geometry(int32_t num_seqs, int32_t hq, int32_t hkv, int32_t d, int32_t bs,
+                               int32_t max_ctx, const GroupSpec& gs) {
+  SharedGeometry g;
+  g.dec = decode_geometry(num_seqs, hq, hkv, d, bs, max_ctx);
+  g.splits = gs.num_groups > 0 ? pa::prefix_pass_splits(gs.num_groups, gs.max_group_size, hq, hkv,
+                                                        gs.max_prefix_len)
+                               : 0;
+  const size_t rows = (size_t)num_seqs * hq * g.splits;
+  g.seq_start_off = round_up(g.dec.bytes, 256);
+  g.pre_o_off = round_up(g.seq_start_off + (size_t)num_seqs * sizeof(int32_t), 256);
+  g.pre_ml_off = round_up(g.pre_o_off + rows * d * sizeof(float), 256);
+  g.bytes = round_up(g.pre_ml_off + rows * 2 * sizeof(float), 256);
+  return g;
+}
+
 // Validation (NULL -> SHAPE -> UNSUPPORTED -> ALIGN -> WORKSPACE) and launch of
 // a decode over a cache of type kv. type_ok is the caller's check of its
 // element types (reported as UNSUPPORTED); an FP8 cache also needs its two
@@ -180,28 +216,36 @@ pa_status_t decode_impl(float* out, const void* query, const void* key_cache,
                         int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                         int64_t num_blocks, int32_t max_context_len, float scale, pa::KvType kv,
                         bool type_ok, void* workspace, size_t workspace_bytes, void* stream,
-                        bool use_scratch = false) {
+                        bool use_scratch = false, const GroupSpec* groups = nullptr) {
   const bool scaled = kv == pa::KvType::FP8;
-  if (num_seqs < 0) return PA_ERR_SHAPE;
+  const bool grouped = groups && groups->num_groups > 0;
+  if (num_seqs < 0 || (groups && groups->num_groups < 0)) return PA_ERR_SHAPE;
   if (num_seqs == 0) return PA_OK;
   if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens ||
-      (!workspace && !use_scratch) || (scaled && (!k_scale || !v_scale)))
+      (!workspace && !use_scratch) || (scaled && (!k_scale || !v_scale)) ||
+      (grouped && (!groups->cu_groups || !groups->prefix_lens)))
     return PA_ERR_NULL;
   if (num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
       max_blocks_per_seq <= 0 || num_blocks <= 0 || max_context_len < 0 ||
-      num_q_heads % num_kv_heads != 0 || !std::isfinite(scale))
+      num_q_heads % num_kv_heads != 0 || !std::isfinite(scale) ||
+      (grouped && (groups->max_group_size <= 0 || groups->max_prefix_len < 0)))
     return PA_ERR_SHAPE;
   if (!supported_block(block_size) || !supported_dim(head_dim) ||
-      !supported_group(num_q_heads, num_kv_heads) || !type_ok)
+      !supported_group(num_q_heads, num_kv_heads) || !type_ok || (groups && num_seqs > 4096))
     return PA_ERR_UNSUPPORTED;
   if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) ||
       !aligned(value_cache, 16) || (!use_scratch && !aligned(workspace, 16)) ||
       !aligned(block_tables, 4) ||
-      !aligned(context_lens, 4) || (scaled && (!aligned(k_scale, 4) || !aligned(v_scale, 4))))
+      !aligned(context_lens, 4) || (scaled && (!aligned(k_scale, 4) || !aligned(v_scale, 4))) ||
+      (grouped && (!aligned(groups->cu_groups, 4) || !aligned(groups->prefix_lens, 4))))
     return PA_ERR_ALIGN;
-  const DecodeGeometry geo = decode_geometry(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                             block_size, max_context_len);
-  if ((use_scratch ? kScratchBytes : workspace_bytes) < geo.bytes) return PA_ERR_WORKSPACE;
+  const GroupSpec none{nullptr, nullptr, 0, 0, 0};
+  const SharedGeometry sgeo = shared_geometry(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                              block_size, max_context_len,
+                                              grouped ? *groups : none);
+  const DecodeGeometry& geo = sgeo.dec;
+  const size_t need = groups ? sgeo.bytes : geo.bytes;
+  if ((use_scratch ? kScratchBytes : workspace_bytes) < need) return PA_ERR_WORKSPACE;
   if (use_scratch) {
     workspace = scratch_on_current_device();
     if (!workspace) return PA_ERR_HIP;
@@ -240,7 +284,59 @@ pa_status_t decode_impl(float* out, const void* query, const void* key_cache,
   a.scale_log2 = scale * 1.4426950408889634f;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
-  return from_hip(pa::launch_decode(a, kv, static_cast<hipStream_t>(stream)));
+  a.cu_groups = nullptr;
+  a.prefix_lens = nullptr;
+  a.num_groups = 0;
+  a.pre_splits = 0;
+  a.pre_o = nullptr;
+  a.pre_ml = nullptr;
+  a.seq_start = nullptr;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (grouped) {
+    a.cu_groups = groups->cu_groups;
+    a.prefix_lens = groups->prefix_lens;
+    a.num_groups = groups->num_groups;
+    a.pre_splits = sgeo.splits;
+    a.pre_o = reinterpret_cast<float*>(ws + sgeo.pre_o_off);
+    a.pre_ml = reinterpret_cast<float*>(ws + sgeo.pre_ml_off);
+    a.seq_start = reinterpret_cast<int*>(ws + sgeo.seq_start_off);
+    // The shared-prefix pass on the matrix cores: each group's members are
+    // the query rows of one causal-free chunk over the group's whole shared
+    // blocks; its partials go to pre_o / pre_ml for the merge.
+    pa::PrefillArgs p;
+    p.out = nullptr;
+    p.part_o = a.pre_o;
+    p.part_ml = a.pre_ml;
+    p.query = query;
+    p.key_cache = key_cache;
+    p.value_cache = value_cache;
+    p.block_tables = block_tables;
+    p.context_lens = groups->prefix_lens;
+    p.cu_q_lens = groups->cu_groups;
+    p.num_seqs = groups->num_groups;
+    p.total_q = num_seqs;
+    p.max_q_len = groups->max_group_size;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.head_dim = head_dim;
+    p.block_size_log2 = a.block_size_log2;
+    p.max_blocks_per_seq = max_blocks_per_seq;
+    p.num_blocks = num_blocks;
+    p.ctx_limit = a.ctx_limit;
+    p.kv_splits = sgeo.splits;
+    p.xcd_remap = 1;
+    p.scale_log2 = a.scale_log2;
+    p.kv_fp8 = scaled;
+    p.k_scale = k_scale;
+    p.v_scale = v_scale;
+    p.prefix_mode = 1;
+    p.member_lens = context_lens;
+    p.seq_start = a.seq_start;
+    p.min_waves = 4;
+    const hipError_t err = pa::launch_prefill(p, st);
+    if (err != hipSuccess) return PA_ERR_HIP;
+  }
+  return from_hip(pa::launch_decode(a, kv, st));
 }
 
 // Validation (NULL -> SHAPE -> UNSUPPORTED -> ALIGN -> WORKSPACE) and launch of
@@ -306,6 +402,10 @@ pa_status_t prefill_impl(float* out, const void* query, const void* key_cache,
   a.kv_fp8 = fp8;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
+  a.prefix_mode = 0;
+  a.member_lens = nullptr;
+  a.seq_start = nullptr;
+  a.min_waves = 0;
   return from_hip(pa::launch_prefill(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -432,6 +532,41 @@ pa_status_t pa_decode_noalloc(float* out, const void* query, const void* key_cac
 }
 
 size_t pa_decode_noalloc_max_bytes(void) { return kScratchBytes; }
+
+size_t pa_decode_shared_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                       int32_t max_context_len, int32_t num_groups,
+                                       int32_t max_group_size, int32_t max_prefix_len) {
+  if (num_seqs <= 0 || num_seqs > 4096 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      max_context_len < 0 || num_q_heads % num_kv_heads || !supported_block(block_size) ||
+      !supported_dim(head_dim) || !supported_group(num_q_heads, num_kv_heads) ||
+      num_groups < 0 || (num_groups > 0 && (max_group_size <= 0 || max_prefix_len < 0)))
+    return 0;
+  const GroupSpec gs{nullptr, nullptr, num_groups, max_group_size, max_prefix_len};
+  return shared_geometry(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                         max_context_len, gs)
+      .bytes;
+}
+
+pa_status_t pa_decode_shared(float* out, const void* query, const void* key_cache,
+                             const void* value_cache, const float* k_scale, const float* v_scale,
+                             const int32_t* block_tables, const int32_t* context_lens,
+                             const int32_t* cu_groups, const int32_t* prefix_lens,
+                             int32_t num_groups, int32_t max_group_size, int32_t max_prefix_len,
+                             int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                             int64_t num_blocks, int32_t max_context_len, float scale,
+                             pa_dtype_t cache_dtype, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  const bool fp8 = cache_dtype == PA_DTYPE_FP8_E4M3;
+  const bool type_ok = fp8 || cache_dtype == PA_DTYPE_BF16;
+  const GroupSpec gs{cu_groups, prefix_lens, num_groups, max_group_size, max_prefix_len};
+  return decode_impl(out, query, key_cache, value_cache, fp8 ? k_scale : nullptr,
+                     fp8 ? v_scale : nullptr, block_tables, context_lens, num_seqs, num_q_heads,
+                     num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                     max_context_len, scale, fp8 ? pa::KvType::FP8 : pa::KvType::BF16, type_ok,
+                     workspace, workspace_bytes, stream, false, &gs);
+}
 
 pa_status_t pa_decode_fp8(float* out, const void* query, const void* key_cache,
                           const void* value_cache, const float* k_scale, const float* v_scale,

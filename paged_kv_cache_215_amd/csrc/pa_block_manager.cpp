@@ -266,4 +266,61 @@ int64_t pa_bm_take_copies(pa_block_manager* bm, int64_t* pairs, int64_t max_pair
   return taken;
 }
 
+int32_t pa_find_shared_prefixes(const int32_t* block_tables, const int32_t* context_lens,
+                                int32_t num_seqs, int32_t max_blocks_per_seq,
+                                int32_t block_size, int32_t min_blocks, int32_t* cu_groups,
+                                int32_t* prefix_lens, int32_t* max_group_size,
+                                int32_t* max_prefix_len) {
+  if (!block_tables || !context_lens || !cu_groups || !prefix_lens || !max_group_size ||
+      !max_prefix_len || num_seqs < 0 || max_blocks_per_seq <= 0 || block_size <= 0 ||
+      min_blocks < 1)
+    return -1;
+  *max_group_size = 0;
+  *max_prefix_len = 0;
+  auto blocks_of = [&](int32_t b) -> int64_t {  // table entries within the context
+    const int64_t n = context_lens[b] < 0 ? 0 : context_lens[b];
+    const int64_t nb = (n + block_size - 1) / block_size;
+    return nb < max_blocks_per_seq ? nb : max_blocks_per_seq;
+  };
+  auto common = [&](int32_t a, int32_t b) -> int64_t {  // leading blocks a and b share
+    const int32_t* ta = block_tables + (int64_t)a * max_blocks_per_seq;
+    const int32_t* tb = block_tables + (int64_t)b * max_blocks_per_seq;
+    const int64_t lim = std::min(blocks_of(a), blocks_of(b));
+    int64_t k = 0;
+    while (k < lim && ta[k] >= 0 && ta[k] == tb[k]) ++k;
+    return k;
+  };
+  // group g spans cu_groups[g] .. cu_groups[g + 1] - 1
+  int32_t groups = 0, last_end = -1;
+  for (int32_t b = 0; b < num_seqs;) {
+    int64_t shared = blocks_of(b);
+    int32_t end = b + 1;
+    while (end < num_seqs) {
+      const int64_t k = common(b, end);
+      if (k < min_blocks) break;
+      shared = std::min(shared, k);
+      ++end;
+    }
+    if (end - b < 2 || shared < min_blocks) {
+      ++b;
+      continue;
+    }
+    if (groups == 0) {
+      cu_groups[0] = b;
+    } else if (last_end < b) {  // the unshared sequences since the last run
+      prefix_lens[groups] = 0;
+      cu_groups[groups + 1] = b;
+      ++groups;
+    }
+    prefix_lens[groups] = (int32_t)std::min<int64_t>(shared * block_size, INT32_MAX);
+    cu_groups[groups + 1] = end;
+    ++groups;
+    *max_group_size = std::max(*max_group_size, end - b);
+    *max_prefix_len = std::max(*max_prefix_len, prefix_lens[groups - 1]);
+    last_end = end;
+    b = end;
+  }
+  return groups;
+}
+
 }  // extern "C"

@@ -261,7 +261,9 @@ __device__ __forceinline__ int wave_scan(int x) {
 constexpr int kTailClasses = 16;  // size classes of the last partitions (P / 16 tokens each)
 
 struct PlanLds {
-  int lens[kPlanSeqs];        // clamped context lengths
+  int lens[kPlanSeqs];        // tokens to attend: clamped context lengths, less a
+                              // copy-on-write group member's shared prefix
+  int starts[kPlanSeqs];      // first position attended (the shared prefix's end)
   int full_pre[kPlanSeqs];    // exclusive prefix of full-partition counts
   unsigned short tail_order[kPlanSeqs];  // sequences by the size of their last partition
   int cls_cnt[8][kTailClasses];          // per wave: last partitions of each size class
@@ -298,11 +300,20 @@ __device__ void build_plan(const DecodeArgs& a, PlanLds& pl) {
     const int e = a.block_tables[(int64_t)(b0 - 1) * a.max_blocks_per_seq];
     if (n > 0 && a.ctx_limit > 0) prev_first = e;
   }
+  const int grouped_lo = a.num_groups > 0 ? max(a.cu_groups[0], 0) : 0;
+  const int grouped_hi = a.num_groups > 0 ? min(a.cu_groups[a.num_groups], S) : 0;
   for (int b = b0; b < b1; ++b) {
     int n = a.context_lens[b];
     const int e = a.block_tables[(int64_t)b * a.max_blocks_per_seq];
     n = n < 0 ? 0 : n;
     n = n > a.ctx_limit ? a.ctx_limit : n;
+    // copy-on-write group member: its shared prefix was attended by the
+    // prefix pass, which recorded where its tail starts; this launch takes
+    // the tail (sequences outside [cu_groups[0], cu_groups[num_groups]) are
+    // in no group)
+    const int start = (b >= grouped_lo && b < grouped_hi) ? a.seq_start[b] : 0;
+    pl.starts[b] = start;
+    n = n > start ? n - start : 0;
     pl.lens[b] = n;
     sum += n;
     mn = min(mn, n);
@@ -336,7 +347,8 @@ __device__ void build_plan(const DecodeArgs& a, PlanLds& pl) {
     mx = wave_max(mx);
     shared = (int)wave_sum_ll(shared);
     live = (int)wave_sum_ll(live);
-    shared = live > 0 && 2 * shared >= live;
+    // (members of copy-on-write groups attend only their private tails here)
+    shared = a.num_groups == 0 && live > 0 && 2 * shared >= live;
     if (lane == 0) {
       int P = a.part_floor;
       if (mx > 0 && mn == mx) {
@@ -557,10 +569,22 @@ __global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(DecodeArgs
   // One work unit: (sequence, KV head, partition) of the plan.
   auto unit = [&](const int seq, const int kvh, const int part, auto keep_tag) {
   constexpr bool kKeep = decltype(keep_tag)::value;
+  // n: tokens this launch attends (a copy-on-write group member's tail, from
+  // position pos0 on; the whole context otherwise)
   const int n = s_plan.lens[seq];
+  const int pos0 = s_plan.starts[seq];
+  const bool has_prefix = pos0 > 0;
   const int start = part * P;
-  if (n == 0) {  // empty context: a zero row
-    for (int idx = tid; idx < G * D / 4; idx += kThreads)
+  if (n == 0) {
+    if (has_prefix) {  // empty tail: an empty partial for the merge
+      if (tid < G) {
+        const int64_t slot = partial_slot(a, s_plan, seq, 0, 1, kvh * G + tid);
+        a.part_ml[2 * slot] = -INFINITY;
+        a.part_ml[2 * slot + 1] = 0.f;
+      }
+      return;
+    }
+    for (int idx = tid; idx < G * D / 4; idx += kThreads)  // empty context: a zero row
       reinterpret_cast<float4*>(a.out)[((int64_t)seq * a.num_q_heads + (int64_t)kvh * G) * (D / 4) + idx] =
           make_float4(0.f, 0.f, 0.f, 0.f);
     return;
@@ -597,7 +621,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(DecodeArgs
   // Block-table entries of this partition, staged in LDS (at most
   // kMaxPartBlocks by construction of part_tokens); -1 marks an entry outside
   // the pool.
-  const int blk0 = start >> bs_log2;
+  const int blk0 = (pos0 + start) >> bs_log2;  // pos0 is a whole number of blocks
   const int nblk = ((end - start) + bs - 1) >> bs_log2;
   for (int i = tid; i < nblk; i += kThreads) {
     const int e = a.block_tables[(int64_t)seq * a.max_blocks_per_seq + blk0 + i];
@@ -864,7 +888,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(DecodeArgs
     const float inv = out_scale / L;
     o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
     const int64_t head = (int64_t)seq * a.num_q_heads + (int64_t)kvh * G + g;
-    if (nparts == 1) {
+    if (nparts == 1 && !has_prefix) {
       reinterpret_cast<float4*>(a.out)[head * (D / 4) + d4] = o;
     } else {
       const int64_t slot = partial_slot(a, s_plan, seq, part, nparts, kvh * G + g);
@@ -947,10 +971,22 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeArgs a) {
 
   auto unit = [&](const int seq, const int kvh, const int part, auto keep_tag) {
   constexpr bool kKeep = decltype(keep_tag)::value;
+  // n: tokens this launch attends (a copy-on-write group member's tail, from
+  // position pos0 on; the whole context otherwise)
   const int n = s_plan.lens[seq];
+  const int pos0 = s_plan.starts[seq];
+  const bool has_prefix = pos0 > 0;
   const int start = part * P;
-  if (n == 0) {  // empty context: a zero row
-    for (int idx = tid; idx < G * D / 4; idx += kThreads)
+  if (n == 0) {
+    if (has_prefix) {  // empty tail: an empty partial for the merge
+      if (tid < G) {
+        const int64_t slot = partial_slot(a, s_plan, seq, 0, 1, kvh * G + tid);
+        a.part_ml[2 * slot] = -INFINITY;
+        a.part_ml[2 * slot + 1] = 0.f;
+      }
+      return;
+    }
+    for (int idx = tid; idx < G * D / 4; idx += kThreads)  // empty context: a zero row
       reinterpret_cast<float4*>(a.out)[((int64_t)seq * a.num_q_heads + (int64_t)kvh * G) * (D / 4) + idx] =
           make_float4(0.f, 0.f, 0.f, 0.f);
     return;
@@ -983,7 +1019,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeArgs a) {
   const float score_scale = kFp8 ? a.scale_log2 * a.k_scale[kvh] : a.scale_log2;
   const float out_scale = kFp8 ? a.v_scale[kvh] : 1.f;
 
-  const int blk0 = start >> bs_log2;
+  const int blk0 = (pos0 + start) >> bs_log2;  // pos0 is a whole number of blocks
   const int nblk = ((end - start) + bs - 1) >> bs_log2;
   for (int i = tid; i < nblk; i += kThreads) {
     const int e = a.block_tables[(int64_t)seq * a.max_blocks_per_seq + blk0 + i];
@@ -1168,7 +1204,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeArgs a) {
     const float inv = out_scale / L;
     o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
     const int64_t head = (int64_t)seq * a.num_q_heads + (int64_t)kvh * G + g;
-    if (nparts == 1) {
+    if (nparts == 1 && !has_prefix) {
       reinterpret_cast<float4*>(a.out)[head * (D / 4) + d4] = o;
     } else {
       const int64_t slot = partial_slot(a, s_plan, seq, part, nparts, kvh * G + g);
@@ -1185,14 +1221,18 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeArgs a) {
 }
 
 // Merge of the per-partition partials of one (sequence, query head):
-// out = sum_p w_p o_p / sum_p w_p with w_p = l_p * 2^(m_p - max_p m_p).
-// Persistent over rows; when the plan gave every sequence one partition the
-// partition kernel already wrote every row and the launch ends at once.
+// out = sum_p w_p o_p / sum_p w_p with w_p = l_p * 2^(m_p - max_p m_p), over
+// partials with l_p > 0 (a partial that saw no key adds nothing; if none saw
+// one the row is zero). A copy-on-write group member's partials are its
+// shared-prefix splits (from the prefix pass) followed by its tail's
+// partitions. Persistent over rows; when the plan gave every sequence one
+// partition and there are no groups, the partition kernel already wrote every
+// row and the launch ends at once.
 template <int D>
 __global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeArgs a) {
   constexpr int PER = D / kWave;  // 1, 2 or 4 floats per lane
   const int P = a.plan->part_tokens;
-  if (a.plan->max_nparts <= 1) return;
+  if (a.plan->max_nparts <= 1 && a.num_groups == 0) return;
   const int full_total = a.plan->full_total;
   const int rows = a.num_seqs * a.num_q_heads;
   const int lane = threadIdx.x;
@@ -1201,37 +1241,57 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeArgs a) {
     int n = a.context_lens[seq];
     n = n < 0 ? 0 : n;
     n = n > a.ctx_limit ? a.ctx_limit : n;
-    const int nparts = (n + P - 1) / P;
-    if (nparts <= 1) continue;  // written by the partition kernel (zeros if empty)
-    const int first = a.full_pre[seq];
-    // slot of partition p (rows of Hq query heads per slot)
-    auto slot = [&](int p) -> int64_t {
+    const bool grouped = a.num_groups > 0 && seq >= a.cu_groups[0] &&
+                         seq < a.cu_groups[a.num_groups];
+    const int pos0 = grouped ? a.seq_start[seq] : 0;
+    n = n > pos0 ? n - pos0 : 0;
+    const int nparts = (n + P - 1) / P;          // tail partitions (0 for an empty tail)
+    const int npre = pos0 > 0 ? a.pre_splits : 0;  // shared-prefix splits
+    if (npre == 0 && nparts <= 1) continue;  // written by the partition kernel
+    const int total = npre + (nparts > 0 ? nparts : 1);
+    const int first = nparts > 1 ? a.full_pre[seq] : 0;
+    // (m, l) and partial output of entry k: prefix splits, then tail partitions
+    auto ml_of = [&](int k) -> const float* {
+      if (k < npre) return a.pre_ml + 2 * (((int64_t)seq * a.num_q_heads + h) * npre + k);
+      const int p = k - npre;
       const int e = p < nparts - 1 ? first + p : full_total + seq;
-      return (int64_t)e * a.num_q_heads + h;
+      return a.part_ml + 2 * ((int64_t)e * a.num_q_heads + h);
     };
-    // lane p holds partition p's (m, l), 64 partitions per pass
+    auto o_of = [&](int k) -> const float* {
+      if (k < npre) return a.pre_o + (((int64_t)seq * a.num_q_heads + h) * npre + k) * D;
+      const int p = k - npre;
+      const int e = p < nparts - 1 ? first + p : full_total + seq;
+      return a.part_o + ((int64_t)e * a.num_q_heads + h) * D;
+    };
+    // lane k holds entry k's (m, l), 64 entries per pass
     float M = -INFINITY;
-    for (int p = lane; p < nparts; p += kWave) M = fmaxf(M, a.part_ml[2 * slot(p)]);
+    for (int k = lane; k < total; k += kWave) {
+      const float* ml = ml_of(k);
+      if (ml[1] > 0.f) M = fmaxf(M, ml[0]);
+    }
 #pragma unroll
     for (int m = 1; m < kWave; m <<= 1) M = fmaxf(M, __shfl_xor(M, m));
     float o[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) o[e] = 0.f;
     float L = 0.f;
-    for (int p0 = 0; p0 < nparts; p0 += kWave) {
-      const int p = p0 + lane;
-      const float w_lane =
-          p < nparts ? a.part_ml[2 * slot(p) + 1] * fast_exp2(a.part_ml[2 * slot(p)] - M) : 0.f;
+    for (int k0 = 0; k0 < total; k0 += kWave) {
+      const int k = k0 + lane;
+      float w_lane = 0.f;
+      if (k < total) {
+        const float* ml = ml_of(k);
+        w_lane = ml[1] > 0.f ? ml[1] * fast_exp2(ml[0] - M) : 0.f;
+      }
       L += w_lane;
-      const int cnt = nparts - p0 < kWave ? nparts - p0 : kWave;
-      // four partitions per step, so that their loads are in flight together
+      const int cnt = total - k0 < kWave ? total - k0 : kWave;
+      // four entries per step, so that their loads are in flight together
       for (int j0 = 0; j0 < cnt; j0 += 4) {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int j = j0 + jj;
           const float w = __shfl(w_lane, j < cnt ? j : 0);
-          if (j < cnt) {
-            const float* po = a.part_o + slot(p0 + j) * D + lane * PER;
+          if (j < cnt && w > 0.f) {
+            const float* po = o_of(k0 + j) + lane * PER;
 #pragma unroll
             for (int e = 0; e < PER; ++e) o[e] = __builtin_fmaf(w, po[e], o[e]);
           }
@@ -1240,7 +1300,7 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeArgs a) {
     }
 #pragma unroll
     for (int m = 1; m < kWave; m <<= 1) L += __shfl_xor(L, m);
-    const float inv = 1.f / L;
+    const float inv = L > 0.f ? 1.f / L : 0.f;
     float* out = a.out + (int64_t)row * D + lane * PER;
 #pragma unroll
     for (int e = 0; e < PER; ++e) out[e] = o[e] * inv;

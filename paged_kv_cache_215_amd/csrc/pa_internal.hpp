@@ -20,6 +20,20 @@ struct DecodePlan {
 
 struct DecodeArgs {
   float* out;            // [S, Hq, D] float32
+  // Copy-on-write groups (num_groups > 0): group g is sequences
+  // cu_groups[g] .. cu_groups[g+1] - 1 sharing their first prefix_lens[g]
+  // tokens (rounded down to whole blocks). Their shared part was attended by
+  // the prefix pass (partials pre_o / pre_ml, [S, Hq, pre_splits]); this
+  // launch attends each member's tail from that position on and the merge
+  // combines both.
+  const int32_t* cu_groups;
+  const int32_t* prefix_lens;
+  int num_groups;
+  int pre_splits;
+  float* pre_o;          // [S, Hq, pre_splits, D]
+  float* pre_ml;         // [S, Hq, pre_splits, 2]
+  int* seq_start;        // [S] first tail position of each group member (written by
+                         // the prefix pass; sequences outside every group start at 0)
   float* part_o;         // [unit_slots, Hq, D] normalised partial outputs
   float* part_ml;        // [unit_slots, Hq, 2] (max in log2 units, sum)
   int* full_pre;         // [S] first slot of each sequence's full partitions
@@ -119,6 +133,17 @@ struct PrefillArgs {
   bool kv_fp8;           // caches hold E4M3 codes (else BF16)
   const float* k_scale;  // [Hkv] E4M3 cache: K = code value * k_scale (else null)
   const float* v_scale;  // [Hkv] E4M3 cache: V = code value * v_scale (else null)
+  // Prefix mode (the shared-prefix pass of a grouped decode): "sequence" g is
+  // a copy-on-write group whose rows are its members' decode queries
+  // (cu_q_lens = group bounds over the decode batch), context_lens holds the
+  // groups' shared prefix lengths, the blocks are read through the first
+  // member's table, no causal mask applies, row r sees keys below its own
+  // member_lens entry, and partials are always written (part_o / part_ml
+  // indexed by (member, query head, split)) for the decode merge.
+  int prefix_mode;
+  const int32_t* member_lens;   // [S] decode context lengths (prefix mode)
+  int* seq_start;        // [S] prefix mode: written with each member's tail start
+  int min_waves;         // waves per workgroup at least (0: the default for the group)
 };
 
 struct DecodeLaunch {
@@ -143,5 +168,7 @@ hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
 int prefill_kv_splits(int num_seqs, int max_q_len, int num_q_heads, int num_kv_heads,
                       int head_dim, int max_context_len);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+int prefix_pass_splits(int num_groups, int max_group_size, int num_q_heads, int num_kv_heads,
+                       int max_prefix_len);
 
 }  // namespace pa

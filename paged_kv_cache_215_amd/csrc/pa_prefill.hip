@@ -142,16 +142,30 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
   const int kvh = (lin / n_rt) % gridDim.y;
   const int zz = lin / (n_rt * gridDim.y);
   const int seq = zz / a.kv_splits, split = zz % a.kv_splits;
-  const int q0 = a.cu_q_lens[seq];
-  const int L = a.cu_q_lens[seq + 1] - q0;
+  int q0 = a.cu_q_lens[seq];
+  int L = a.cu_q_lens[seq + 1] - q0;
+  if (a.prefix_mode) {  // group bounds kept within the decode batch
+    const int q1 = min(max(q0 + L, 0), a.total_q);
+    q0 = min(max(q0, 0), a.total_q);
+    L = max(q1 - q0, 0);
+  }
   const int r0 = row_tile * S::ROWS;
-  if (r0 >= L) return;
-  int n = a.context_lens[seq];
-  n = n > a.ctx_limit ? a.ctx_limit : n;
-  if (L > n) return;  // malformed chunk (longer than its context): nothing defined to compute
   const int bs_log2 = a.block_size_log2;
   const int bs = 1 << bs_log2;
-  const int base_pos = n - L;  // position of chunk row 0
+  int n = a.context_lens[seq];
+  n = n > a.ctx_limit ? a.ctx_limit : n;
+  if (a.prefix_mode) {
+    // shared prefix of a copy-on-write group: its whole blocks only. One
+    // workgroup per group records where each member's tail starts, for the
+    // decode of the tails and the merge that follow in stream order.
+    n = n < 0 ? 0 : n & ~(bs - 1);
+    if (row_tile == 0 && kvh == 0 && split == 0)
+      for (int r = threadIdx.x; r < L; r += S::NT) a.seq_start[q0 + r] = n;
+  } else if (L > n) {
+    return;  // malformed chunk (longer than its context): nothing defined to compute
+  }
+  if (r0 >= L) return;
+  const int base_pos = n - L;  // position of chunk row 0 (causal chunks)
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -187,7 +201,18 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
 
   // Key range of this split: keys visible to some row of the workgroup.
   const int last_row = min(r0 + S::ROWS, L) - 1;
-  const int kmax = base_pos + last_row + 1;
+  const int kmax = a.prefix_mode ? n : base_pos + last_row + 1;
+  // Prefix mode: row my_row (member q0 + my_row) sees keys below both the
+  // shared prefix and its own context; a wave with a row that stops short of
+  // the prefix masks every tile.
+  int member_limit = n - 1;
+  if (a.prefix_mode) {
+    int nm = a.member_lens[q0 + qrow];
+    nm = nm < 0 ? 0 : (nm > a.ctx_limit ? a.ctx_limit : nm);
+    member_limit = min(n, nm) - 1;
+  }
+  const bool wave_short =
+      a.prefix_mode && __builtin_amdgcn_ballot_w64(member_limit < n - 1) != 0;
   const int ntiles = (kmax + kKeyTile - 1) / kKeyTile;
   const int per_split = (ntiles + a.kv_splits - 1) / a.kv_splits;
   const int kt_begin = split * per_split;
@@ -204,7 +229,9 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
   {
     const int key_end = min(kt_end * kKeyTile, n);
     const int nblk = key_end > kt_begin * kKeyTile ? ((key_end + bs - 1) >> bs_log2) - blk_first : 0;
-    const int32_t* bt = a.block_tables + (int64_t)seq * a.max_blocks_per_seq + blk_first;
+    // (prefix mode: the group's first member holds the shared blocks)
+    const int32_t* bt =
+        a.block_tables + (int64_t)(a.prefix_mode ? q0 : seq) * a.max_blocks_per_seq + blk_first;
     for (int i = tid; i < nblk && i < kPfMaxBlocks; i += S::NT) {
       const int e = bt[i];
       s_bt[i] = (e >= 0 && (int64_t)e < a.num_blocks) ? e : -1;
@@ -370,8 +397,11 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
     // the loads.
     if (has_next) load_regs(kt + 1);
 
-    const int limit = base_pos + my_row;  // last key this row may see
-    const bool diag = key0 + kKeyTile - 1 > base_pos + r0 || key0 + kKeyTile > n;
+    // last key this row may see; tiles that need the mask
+    const int limit = a.prefix_mode ? member_limit : base_pos + my_row;
+    const bool diag = a.prefix_mode
+                          ? (wave_short || key0 + kKeyTile > n)
+                          : (key0 + kKeyTile - 1 > base_pos + r0 || key0 + kKeyTile > n);
     bf16x8_t pop_hi[HPW][S::PSTEPS], pop_lo[HPW][S::PSTEPS];
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
@@ -469,7 +499,7 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
     const int64_t orow = (int64_t)(q0 + my_row) * a.num_q_heads + head0 + hh;
     const float inv = l_row > 0.f ? v_scale / l_row : 0.f;
     float* dst;
-    if (a.kv_splits == 1) {
+    if (a.kv_splits == 1 && !a.prefix_mode) {
       dst = a.out + orow * D;
     } else {
       const int64_t slot = orow * a.kv_splits + split;
@@ -607,6 +637,33 @@ int prefill_kv_splits(int num_seqs, int max_q_len, int num_q_heads, int num_kv_h
   return splits;
 }
 
+// Context splits of the shared-prefix pass of a grouped decode. Its
+// workgroups are 4-wave ones (rows per workgroup: 16 per wave and head of the
+// group, 64 / G rows when G <= 4) over whole 32-key tiles; the prefix of each
+// group is split until the launch has about kPrefixTargetWgs workgroups,
+// keeping at least 256 keys per split, then further if a split's keys would
+// not fit the staged table. Fewer splits mean fewer partials for the merge to
+// read; the environment override exists for tuning sweeps only.
+int prefix_pass_splits(int num_groups, int max_group_size, int num_q_heads, int num_kv_heads,
+                       int max_prefix_len) {
+  static const int target = [] {
+    const char* s = std::getenv("PA_PREFIX_TARGET_WGS");
+    const int v = s ? std::atoi(s) : 0;
+    return v > 0 ? v : 256;
+  }();
+  const int group = num_q_heads / num_kv_heads;
+  const int nw = group > 4 ? group : 4;
+  const int rows = 16 * (nw / group);
+  const int64_t wgs =
+      (int64_t)num_groups * num_kv_heads * ((max_group_size + rows - 1) / rows);
+  int splits = 1;
+  while (splits < 32 && wgs * splits < target && max_prefix_len / (2 * splits) >= 256)
+    splits *= 2;
+  const int64_t span = (int64_t)(kPfMaxBlocks - 6) * 16;
+  while ((int64_t)splits * span < max_prefix_len) ++splits;
+  return splits;
+}
+
 template <typename T, int D, int G, int HPW, int MW, int KT>
 static hipError_t launch_pf(const PrefillArgs& a_in, hipStream_t stream) {
   static const int remap = [] {
@@ -619,7 +676,8 @@ static hipError_t launch_pf(const PrefillArgs& a_in, hipStream_t stream) {
   dim3 grid((a.max_q_len + S::ROWS - 1) / S::ROWS, a.num_kv_heads, a.num_seqs * a.kv_splits);
   hipLaunchKernelGGL((prefill_kernel<T, D, G, HPW, MW, KT>), grid, dim3(S::NT), 0, stream, a);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || a.kv_splits == 1) return err;
+  // (prefix mode: the decode merge combines these partials with the tails')
+  if (err != hipSuccess || a.kv_splits == 1 || a.prefix_mode) return err;
   hipLaunchKernelGGL((prefill_merge_kernel<D>), dim3(a.num_q_heads, a.total_q), dim3(kWave), 0,
                      stream, a);
   return hipGetLastError();
@@ -647,7 +705,8 @@ static hipError_t launch_ph(const PrefillArgs& a, hipStream_t stream) {
 
 template <typename T, int D, int G>
 static hipError_t launch_pw(const PrefillArgs& a, hipStream_t stream) {
-  if (prefill_min_waves(G) == 8) return launch_ph<T, D, G, 8>(a, stream);
+  const int mw = a.min_waves ? a.min_waves : prefill_min_waves(G);
+  if (mw == 8) return launch_ph<T, D, G, 8>(a, stream);
   return launch_ph<T, D, G, 4>(a, stream);
 }
 

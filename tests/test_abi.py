@@ -170,6 +170,41 @@ def test_fp8_prefill_zero_rows_is_noop(lib):
     assert lib.pa_prefill_chunk_fp8(*fp8_prefill_args(total_q=0, k_scale=None)) == OK
 
 
+def shared_args(**over):
+    args = dict(out=A, query=A, key_cache=A, value_cache=A, k_scale=None, v_scale=None,
+                block_tables=A, context_lens=A, cu_groups=A, prefix_lens=A, num_groups=8,
+                max_group_size=16, max_prefix_len=4096, num_seqs=128, num_q_heads=16,
+                num_kv_heads=4, head_dim=256, block_size=16, max_blocks_per_seq=320,
+                num_blocks=7000, max_context_len=5120, scale=0.0625, cache_dtype=BF16,
+                workspace=A, workspace_bytes=1 << 34, stream=None)
+    args.update(over)
+    return list(args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(out=None), NULL), (dict(cu_groups=None), NULL), (dict(prefix_lens=None), NULL),
+    (dict(cache_dtype=2), NULL),  # an FP8 cache needs its scales
+    (dict(num_groups=-1), SHAPE), (dict(max_group_size=0), SHAPE), (dict(max_prefix_len=-5), SHAPE),
+    (dict(num_kv_heads=3), SHAPE), (dict(cache_dtype=F32), UNSUP), (dict(num_seqs=4097), UNSUP),
+    (dict(head_dim=80), UNSUP), (dict(cu_groups=A + 2), ALIGN), (dict(prefix_lens=A + 1), ALIGN),
+    (dict(workspace_bytes=1 << 20), WORKSPACE),
+])
+def test_shared_decode_rejects(lib, over, code):
+    assert lib.pa_decode_shared(*shared_args(**over)) == code
+
+
+def test_shared_decode_zero_sequences_and_no_groups(lib):
+    assert lib.pa_decode_shared(*shared_args(num_seqs=0, out=None)) == OK
+    # without groups the group arrays are not needed
+    none = lib.pa_decode_shared_workspace_size(128, 16, 4, 256, 16, 5120, 0, 0, 0)
+    assert none >= lib.pa_decode_workspace_size(128, 16, 4, 256, 16, 5120)
+    some = lib.pa_decode_shared_workspace_size(128, 16, 4, 256, 16, 5120, 8, 16, 4096)
+    # the prefix pass's partials: 128 sequences x 16 heads x splits x (256 + 2) floats
+    assert some - none >= 128 * 16 * 258 * 4
+    assert lib.pa_decode_shared_workspace_size(4097, 16, 4, 256, 16, 5120, 8, 16, 4096) == 0
+    assert lib.pa_decode_shared_workspace_size(128, 16, 4, 256, 16, 5120, 8, 0, 4096) == 0
+
+
 def test_binding_raises_loudly_without_library(monkeypatch, tmp_path):
     import paged_kv_cache_215_amd._lib as L
     monkeypatch.setattr(L, "_lib", None)

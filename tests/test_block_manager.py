@@ -147,3 +147,71 @@ def test_mixed_step_population_matches_closed_form():
         st, slots = bm.append(s, int(n))
         assert st == 0 and len(slots) == n
     assert 200_000 - bm.num_free() == int(sum(-(-int(n) // 16) for n in lens))
+
+
+# ---- copy-on-write groups of a decode batch ------------------------------------------------
+
+def _groups_brute_force(bt, ctx, bs, min_blocks=1):
+    """The definition of pa_find_shared_prefixes, written out: greedy maximal
+    runs of consecutive sequences sharing >= min_blocks leading table entries
+    (within each member's context) with the run's first sequence."""
+    nb = [min(-(-max(int(n), 0) // bs), bt.shape[1]) for n in ctx]
+
+    def common(a, b):
+        k = 0
+        while k < min(nb[a], nb[b]) and bt[a, k] >= 0 and bt[a, k] == bt[b, k]:
+            k += 1
+        return k
+    runs, b, S = [], 0, len(ctx)
+    while b < S:
+        shared, end = nb[b], b + 1
+        while end < S and common(b, end) >= min_blocks:
+            shared = min(shared, common(b, end))
+            end += 1
+        if end - b >= 2 and shared >= min_blocks:
+            runs.append((b, end, shared * bs))
+            b = end
+        else:
+            b += 1
+    cu, pl = [], []
+    for i, (s0, e0, p) in enumerate(runs):
+        if i == 0:
+            cu.append(s0)
+        elif cu[-1] < s0:
+            pl.append(0)
+            cu.append(s0)
+        pl.append(p)
+        cu.append(e0)
+    return cu, pl
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_find_shared_prefixes_matches_its_definition(seed):
+    rng = np.random.default_rng(seed)
+    S, bs, mb = int(rng.integers(1, 40)), int(rng.choice([4, 16])), 12
+    ctx = rng.integers(0, mb * bs + 1, size=S).astype(np.int32)
+    bt = rng.integers(0, 10_000, size=(S, mb)).astype(np.int32)
+    # plant forks: runs that copy a random number of their first member's entries
+    b = 0
+    while b < S:
+        run = int(rng.integers(1, 6))
+        k = int(rng.integers(0, mb))
+        for c in range(b + 1, min(S, b + run)):
+            bt[c, :k] = bt[b, :k]
+        b += run
+    bt[rng.random(bt.shape) < 0.05] = -1
+    for min_blocks in (1, 2):
+        cu, pl, mg, mp = pa.find_shared_prefixes(bt, ctx, bs, min_blocks)
+        want_cu, want_pl = _groups_brute_force(bt, ctx, bs, min_blocks)
+        assert cu.tolist() == want_cu and pl.tolist() == want_pl
+        sizes = [cu[i + 1] - cu[i] for i in range(len(pl)) if pl[i] > 0]
+        assert mg == (max(sizes) if sizes else 0) and mp == (max(pl) if len(pl) else 0)
+
+
+def test_find_shared_prefixes_c4_structure():
+    from workloads import make_config_case
+    case = make_config_case("c4_grpo_cow", structure_only=True)
+    lay = case.layout
+    cu, pl, mg, mp = pa.find_shared_prefixes(lay.block_tables, lay.context_lens, 16)
+    assert cu.tolist() == list(range(0, 129, 16)) and pl.tolist() == [4096] * 8
+    assert (mg, mp) == (16, 4096)
