@@ -39,7 +39,8 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense BF16 matrix-core peak, TFLOP/s
 DECODE_SOURCES = ["paged_kv_cache_215_amd/csrc/pa_decode.hip",
                   "paged_kv_cache_215_amd/csrc/pa_device.hpp"]
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_c3_hbm_counters.json")
+# the grouped decode's prefix pass is the chunk kernel in prefix mode
+SHARED_SOURCES = DECODE_SOURCES + ["paged_kv_cache_215_amd/csrc/pa_prefill.hip"]
 
 
 def log(msg):
@@ -97,15 +98,31 @@ def source_hash(paths):
     return h.hexdigest()[:16]
 
 
-def load_traffic():
-    """HBM traffic per pa_decode call from the committed rocprofv3 counter
-    summary, only if it was taken on the current decode kernel source."""
+# HBM counter summaries under profiles/: (workload, FP8 cache) -> file stem.
+COUNTER_SETS = {
+    ("c3_full_step", False): "decode_c3_hbm_counters",
+    ("c3_full_step", True): "decode_fp8_c3_hbm_counters",
+    ("c4_grpo_cow", False): "decode_c4_hbm_counters",
+}
+
+
+def _sources_for(workload):
+    return SHARED_SOURCES if workload == "c4_grpo_cow" else DECODE_SOURCES
+
+
+def load_traffic(workload="c3_full_step", fp8=False):
+    """HBM traffic per decode call from the committed rocprofv3 counter
+    summary of this workload, only if it was taken on the current kernel
+    source."""
+    stem = COUNTER_SETS.get((workload, fp8))
+    if stem is None:
+        return None
     try:
-        with open(COUNTERS_FILE) as f:
+        with open(os.path.join(ROOT, "profiles", stem + ".json")) as f:
             c = json.load(f)
     except (OSError, ValueError):
         return None
-    if c.get("source_hash") != source_hash(DECODE_SOURCES):
+    if c.get("source_hash") != source_hash(_sources_for(workload)):
         return None
     return c.get("hbm_bytes_per_call")
 
@@ -137,6 +154,11 @@ def _cpu_worker(args):
         return oracle.fp8.decode_fp8_ref(q[b:b + 1], kc, vc, _cpu_arr(f"ks{layer}"),
                                          _cpu_arr(f"vs{layer}"), bt[b:b + 1], lens[b:b + 1], scale)
     return oracle.decode_ref(q[b:b + 1], kc, vc, bt[b:b + 1], lens[b:b + 1], scale)
+
+
+# Worker processes of the CPU baseline at most: a one-GPU job's CPU share on
+# the GPU hosts (the oracle runs one single-threaded process per core).
+CPU_SHARE_CORES = 16
 
 
 def cpu_model():
@@ -173,10 +195,13 @@ def cpu_baseline(case, layers, seq_layers_per_step):
                 np.save(os.path.join(folder, f"ks{layer}.npy"), case.k_scales[layer].cpu().numpy())
                 np.save(os.path.join(folder, f"vs{layer}.npy"), case.v_scales[layer].cpu().numpy())
         try:
-            cores = len(os.sched_getaffinity(0))
+            host_cores = len(os.sched_getaffinity(0))
         except AttributeError:
-            cores = os.cpu_count() or 1
-        workers = max(1, min(16, cores))
+            host_cores = os.cpu_count() or 1
+        # one worker per core this process may run on, capped at the 16-core
+        # CPU share a one-GPU job gets on these hosts (the affinity mask can
+        # list every core of the machine)
+        workers = max(1, min(CPU_SHARE_CORES, host_cores))
         saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
                                                 "MKL_NUM_THREADS")}
         for k in saved:
@@ -200,7 +225,7 @@ def cpu_baseline(case, layers, seq_layers_per_step):
     finally:
         shutil.rmtree(folder, ignore_errors=True)
     n_tasks = len(layers) * S
-    return {"wall_s": wall, "workers": workers, "tasks": n_tasks,
+    return {"wall_s": wall, "workers": workers, "host_cores": host_cores, "tasks": n_tasks,
             "step_seconds": wall * seq_layers_per_step / n_tasks}
 
 
@@ -324,6 +349,36 @@ def run(args):
     decode_ms = [a.elapsed_time(b) for a, b in dec_events]
     avg_decode_s = float(np.mean(decode_ms)) / 1e3
 
+    # The same step replayed from one captured HIP graph (a second, labelled
+    # line: the headline value stays the eager step). Every replay rewrites
+    # the same new tokens and recomputes the same outputs, so the outputs of
+    # the first and of the last replay must equal the eager step's bit for bit.
+    graph_line = None
+    if args.graph_steps > 0:
+        eager_out = [o.clone() for o in outs]
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for o in outs:
+            o.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        first_ok = all(torch.equal(a, b) for a, b in zip(outs, eager_out))
+        g0 = time.perf_counter()
+        for _ in range(args.graph_steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        g_elapsed = time.perf_counter() - g0
+        last_ok = all(torch.equal(a, b) for a, b in zip(outs, eager_out))
+        if not (first_ok and last_ok):
+            raise SystemExit("graph replay differs from the eager step")
+        graph_line = {"steps": args.graph_steps,
+                      "ms_per_step": round(g_elapsed / args.graph_steps * 1e3, 4),
+                      "tokens_per_s": round(S * args.graph_steps / g_elapsed, 2),
+                      "outputs_equal_eager": True}
+        log(f"[bench] graph replay: {graph_line}")
+        del graph, eager_out
+
     # Cold-cache decode calls (one-layer workloads): a 1 GiB write, more than
     # the 256 MB last-level cache holds, goes between calls, outside the events,
     # so every call reads its K/V from HBM. The full 16-layer step needs none:
@@ -353,7 +408,8 @@ def run(args):
         f"{tokens_per_s:.1f} tok/s; pa_decode avg {avg_decode_s * 1e6:.1f} us "
         f"(min {min(decode_ms) * 1e3:.1f}, max {max(decode_ms) * 1e3:.1f}), "
         f"{achieved_gbs:.1f} GB/s = {achieved_gbs / HBM_PEAK_GBS:.3f} of HBM peak")
-    traffic = load_traffic() if args.workload == "c3_full_step" and not fp8 else None
+    traffic = (load_traffic(args.workload, fp8)
+               if groups is not None or args.workload != "c4_grpo_cow" else None)
 
     result = {
         "metric": "paged-attn decode tokens/s & achieved HBM GB/s (% of 8 TB/s), 1 MI355X",
@@ -410,6 +466,8 @@ def run(args):
                                elem, unique_blocks=False, kv_bytes=1 if fp8 else None)
         result["roofline"]["logical_bytes_per_call"] = logical
         result["roofline"]["effective_logical_gbs"] = round(logical / avg_decode_s / 1e9, 1)
+    if graph_line is not None:
+        result["graph_replay"] = graph_line
     if cold_ms:
         cold_s = float(np.median(cold_ms)) / 1e3
         result["roofline"]["cold_cache"] = {
@@ -444,6 +502,8 @@ def run(args):
             "value": round(S / cb["step_seconds"], 4),
             "unit": "tokens/s",
             "cores": cb["workers"],
+            "workers": cb["workers"],
+            "host_cores": cb["host_cores"],
             "cpu": cpu_model(),
             "effective_gbs": round(bytes_call * L / cb["step_seconds"] / 1e9, 3),
             "kind": "oracle",
@@ -472,29 +532,81 @@ def copy_calibration(nbytes=1 << 30, reps=5):
 
 # ------------------------------------------------------- profile summaries ---
 
-PROFILE_COMMANDS = {
-    "kt_c3": "cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats --output-format csv "
-             "-d <out>/kt_c3 -o kt -- python3 <repo>/bench.py --steps 5 --warmup 1 --no-cpu-baseline",
-    "kt_c5": "cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats --output-format csv "
-             "-d <out>/kt_c5 -o kt -- python3 <repo>/bench.py --workload c5_mixed_step "
-             "--steps 5 --warmup 1 --cold-calls 0 --no-cpu-baseline",
-    "kt_c3_fp8": "cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats --output-format csv "
-                 "-d <out>/kt_c3_fp8 -o kt -- python3 <repo>/bench.py --kv fp8 --steps 5 "
-                 "--warmup 1 --no-cpu-baseline",
+_KT = ("cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats --output-format csv "
+       "-d <out>/{tag} -o kt -- python3 <repo>/bench.py {args} --no-cpu-baseline")
+_PMC = ("rocprofv3 --pmc {counter} --output-format csv -d <out>/{tag} -o p -- "
+        "python3 <repo>/bench.py {args} --no-cpu-baseline")
+
+# Kernel traces: tag -> (bench arguments, title, summary file).
+TRACES = {
+    "kt_c3": ("--steps 5 --warmup 1",
+              "pa kernels, 64 seqs x 8192 ctx x 16 layers (bs 32)", "decode_c3_kernel_trace.md"),
+    "kt_c3_fp8": ("--kv fp8 --steps 5 --warmup 1",
+                  "pa kernels, FP8 E4M3 cache, 64 seqs x 8192 ctx x 16 layers (bs 32)",
+                  "decode_fp8_c3_kernel_trace.md"),
+    "kt_c5": ("--workload c5_mixed_step --steps 5 --warmup 1 --cold-calls 0",
+              "pa kernels, mixed step: 255 decode seqs + 512-row prefill chunk",
+              "mixed_c5_kernel_trace.md"),
+    "kt_c5_fp8": ("--workload c5_mixed_step --kv fp8 --steps 5 --warmup 1 --cold-calls 0",
+                  "pa kernels, mixed step over an FP8 cache: 255 decode seqs + 512-row "
+                  "prefill chunk", "mixed_fp8_c5_kernel_trace.md"),
+    "kt_c2": ("--workload c2_layer_decode --steps 10 --warmup 2 --cold-calls 10",
+              "pa kernels, one ragged layer: 32 seqs, contexts U[512, 8192], bs 16",
+              "decode_c2_kernel_trace.md"),
+    "kt_c2_fp8": ("--workload c2_layer_decode --kv fp8 --steps 10 --warmup 2 --cold-calls 10",
+                  "pa kernels, one ragged layer over an FP8 cache: 32 seqs, contexts "
+                  "U[512, 8192], bs 16", "decode_fp8_c2_kernel_trace.md"),
+    "kt_c4": ("--workload c4_grpo_cow --steps 10 --warmup 2 --cold-calls 10",
+              "pa kernels, copy-on-write batch (8 prompts x 16 rollouts, 4096-token shared "
+              "prompt, tails U[0, 1024], bs 16) through pa_decode_shared",
+              "decode_c4_kernel_trace.md"),
+    "kt_c4_fp8": ("--workload c4_grpo_cow --kv fp8 --steps 10 --warmup 2 --cold-calls 10",
+                  "pa kernels, the copy-on-write batch over an FP8 cache through "
+                  "pa_decode_shared", "decode_fp8_c4_kernel_trace.md"),
+}
+
+# HBM counter passes: (workload, FP8 cache) -> (bench arguments, description,
+# kernel-name filters of the decode call's kernels).
+COUNTER_RUNS = {
+    ("c3_full_step", False): ("--steps 2 --warmup 1",
+                              "64 seqs x 8192 ctx, bs 32, 4 KV / 16 query heads, d 256, BF16",
+                              ("decode_partition_kernel", "decode_mfma_kernel",
+                               "decode_merge_kernel")),
+    ("c3_full_step", True): ("--kv fp8 --steps 2 --warmup 1",
+                             "64 seqs x 8192 ctx, bs 32, 4 KV / 16 query heads, d 256, FP8 E4M3",
+                             ("decode_partition_kernel", "decode_mfma_kernel",
+                              "decode_merge_kernel")),
+    ("c4_grpo_cow", False): ("--workload c4_grpo_cow --steps 2 --warmup 1 --cold-calls 0",
+                             "copy-on-write batch, 8 x 16 rollouts of a 4096-token prompt, "
+                             "tails U[0, 1024], bs 16, BF16, pa_decode_shared",
+                             ("prefill_kernel", "decode_partition_kernel", "decode_mfma_kernel",
+                              "decode_merge_kernel")),
+}
+
+
+def _counter_tags(key):
+    stem = "c3" if key[0] == "c3_full_step" else "c4"
+    return (f"pmc_fetch_{stem}{'_fp8' if key[1] else ''}",
+            f"pmc_write_{stem}{'_fp8' if key[1] else ''}")
+
+
+PROFILE_COMMANDS = {tag: _KT.format(tag=tag, args=a) for tag, (a, _, _) in TRACES.items()}
+for _key, (_args, _, _) in COUNTER_RUNS.items():
+    _f, _w = _counter_tags(_key)
+    PROFILE_COMMANDS[_f] = _PMC.format(counter="FETCH_SIZE", tag=_f, args=_args)
+    PROFILE_COMMANDS[_w] = _PMC.format(counter="WRITE_SIZE", tag=_w, args=_args)
+PROFILE_COMMANDS.update({
     "pmc_prefill_c5": "rocprofv3 --pmc SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU "
                       "SQ_ACTIVE_INST_VALU SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_ACTIVE_INST_LDS "
                       "SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE --output-format csv -d <out>/pmc_prefill_c5 "
                       "-o p -- python3 <repo>/bench.py --workload c5_mixed_step --steps 2 --warmup 1 "
                       "--cold-calls 0 --no-cpu-baseline",
-    "pmc_fetch_c3": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/pmc_fetch_c3 -o p -- "
-                    "python3 <repo>/bench.py --steps 2 --warmup 1 --no-cpu-baseline",
-    "pmc_write_c3": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/pmc_write_c3 -o p -- "
-                    "python3 <repo>/bench.py --steps 2 --warmup 1 --no-cpu-baseline",
     "pmc_fetch_copy": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/pmc_fetch_copy -o p -- "
                       "python3 <repo>/bench.py --copy-calib",
     "pmc_write_copy": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/pmc_write_copy -o p -- "
                       "python3 <repo>/bench.py --copy-calib",
-}
+})
+
 
 
 def _csv(path):
@@ -573,16 +685,74 @@ def _summarize_prefill_counters(folder, kt_folder, dst):
     log("wrote prefill_c5_counters.md")
 
 
+def _algorithmic_decode_bytes(workload, fp8):
+    """Algorithmic bytes of one decode call of a workload (its structure only:
+    no value tensors are drawn)."""
+    from workloads import make_config_case
+    case = make_config_case(workload, structure_only=True)
+    S = case.num_decode_seqs
+    return decode_bytes(case.layout, S, case.num_q_heads, case.num_kv_heads, case.head_dim, 2,
+                        unique_blocks=workload == "c4_grpo_cow", kv_bytes=1 if fp8 else None)
+
+
+def _summarize_traffic(src, dst, key, calib):
+    """FETCH_SIZE / WRITE_SIZE per decode call of one workload, scaled by the
+    plain-copy calibration, into profiles/<stem>.{json,md}."""
+    f_tag, w_tag = _counter_tags(key)
+    if not all(os.path.isdir(os.path.join(src, t)) for t in (f_tag, w_tag)):
+        return
+    args, desc, filters = COUNTER_RUNS[key]
+    fetch = _counter_means(os.path.join(src, f_tag), "FETCH_SIZE")
+    write = _counter_means(os.path.join(src, w_tag), "WRITE_SIZE")
+    parts = [k for k in fetch if any(f in k for f in filters)]
+    copy_name, f_factor, w_factor, cf, cw = calib
+    per_call_read = sum(fetch[k][1] for k in parts) * 1024 * f_factor
+    per_call_write = sum(write.get(k, (0, 0.0))[1] for k in parts) * 1024 * w_factor
+    algo = _algorithmic_decode_bytes(*key)
+    stem = COUNTER_SETS[key]
+    need = [f_tag, w_tag, "pmc_fetch_copy", "pmc_write_copy"]
+    summary = {
+        "workload": f"{key[0]} ({desc})",
+        "source_hash": source_hash(_sources_for(key[0])),
+        "copy_calibration": {"kernel": copy_name, "bytes_each_way": 1 << 30,
+                             "fetch_size_kib": cf, "write_size_kib": cw,
+                             "fetch_scale": f_factor, "write_scale": w_factor},
+        "per_kernel_kib_per_dispatch": {
+            _short(k): {"FETCH_SIZE": fetch[k][1], "WRITE_SIZE": write.get(k, (0, 0.0))[1],
+                        "dispatches": fetch[k][0]} for k in parts},
+        "hbm_read_bytes_per_call": per_call_read,
+        "hbm_write_bytes_per_call": per_call_write,
+        "hbm_bytes_per_call": per_call_read + per_call_write,
+        "algorithmic_bytes_per_call": algo,
+        "commands": {t: PROFILE_COMMANDS[t] for t in need},
+    }
+    with open(os.path.join(dst, stem + ".json"), "w") as f:
+        json.dump(summary, f, indent=1)
+    lines = [f"# HBM traffic of one decode call: {key[0]} ({desc})", "",
+             "Per dispatch, averaged over the profiled steps; FETCH_SIZE and WRITE_SIZE are "
+             "in KiB. Each counter ran in a pass of its own.", "",
+             "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB |", "|---|---|---|"]
+    for k in parts:
+        lines.append(f"| `{_short(k)}` | {fetch[k][1]:.1f} | {write.get(k, (0, 0.0))[1]:.1f} |")
+    lines += ["", f"Calibration: a plain 1 GiB device copy (`{_short(copy_name)}`, "
+                  f"`bench.py --copy-calib`) reads as FETCH_SIZE {cf:.1f} KiB and "
+                  f"WRITE_SIZE {cw:.1f} KiB, so fetch counts are scaled by "
+                  f"{f_factor:.4f} and write counts by {w_factor:.4f}.", "",
+              f"Traffic per call: read {per_call_read / 1e9:.4f} GB, write "
+              f"{per_call_write / 1e9:.4f} GB, total {(per_call_read + per_call_write) / 1e9:.4f} GB "
+              f"(algorithmic bytes: {algo / 1e9:.4f} GB, ratio "
+              f"{(per_call_read + per_call_write) / algo:.3f}).", "", "Commands:", ""]
+    lines += [f"    {PROFILE_COMMANDS[t]}" for t in need]
+    with open(os.path.join(dst, stem + ".md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    log(f"wrote {stem}.{{json,md}}")
+
+
 def summarize_profiles(src, dst):
     """Turn rocprofv3 CSV output (folders named as in PROFILE_COMMANDS) into
     the short text summaries kept under profiles/."""
     os.makedirs(dst, exist_ok=True)
-    names = {"kt_c3": "decode_c3_kernel_trace.md", "kt_c5": "mixed_c5_kernel_trace.md",
-             "kt_c3_fp8": "decode_fp8_c3_kernel_trace.md"}
-    for tag, title in (("kt_c3", "pa kernels, 64 seqs x 8192 ctx x 16 layers (bs 32)"),
-                       ("kt_c5", "pa kernels, mixed step: 255 decode seqs + 512-row prefill chunk"),
-                       ("kt_c3_fp8", "pa kernels, FP8 E4M3 cache, 64 seqs x 8192 ctx x 16 layers "
-                                     "(bs 32)")):
+    for tag, (_, title, name) in TRACES.items():
         folder = os.path.join(src, tag)
         if not os.path.isdir(folder):
             continue
@@ -597,8 +767,8 @@ def summarize_profiles(src, dst):
             lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                          f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
         lines.append("")
-        lines.append("Kernels not listed are torch's input generation (outside the timed steps).")
-        name = names[tag]
+        lines.append("Kernels not listed are torch's input generation and the cache flushes "
+                     "between cold calls (outside the timed calls).")
         with open(os.path.join(dst, name), "w") as f:
             f.write("\n".join(lines) + "\n")
         log(f"wrote {name}")
@@ -607,54 +777,16 @@ def summarize_profiles(src, dst):
         _summarize_prefill_counters(os.path.join(src, "pmc_prefill_c5"),
                                     os.path.join(src, "kt_c5"), dst)
 
-    need = ["pmc_fetch_c3", "pmc_write_c3", "pmc_fetch_copy", "pmc_write_copy"]
-    if not all(os.path.isdir(os.path.join(src, t)) for t in need):
+    if not all(os.path.isdir(os.path.join(src, t)) for t in ("pmc_fetch_copy", "pmc_write_copy")):
         return
-    fetch = _counter_means(os.path.join(src, "pmc_fetch_c3"), "FETCH_SIZE")
-    write = _counter_means(os.path.join(src, "pmc_write_c3"), "WRITE_SIZE")
     cf = _counter_means(os.path.join(src, "pmc_fetch_copy"), "FETCH_SIZE")
     cw = _counter_means(os.path.join(src, "pmc_write_copy"), "WRITE_SIZE")
     copy_name = [k for k in cf if "copyBuffer" in k][0]
     calib = 1 << 30                                   # bench.py --copy-calib moves 1 GiB each way
-    f_factor = calib / (cf[copy_name][1] * 1024)
-    w_factor = calib / (cw[copy_name][1] * 1024)
-    parts = [k for k in fetch if "decode_partition_kernel" in k] + \
-            [k for k in fetch if "decode_merge_kernel" in k]
-    per_call_read = sum(fetch[k][1] for k in parts) * 1024 * f_factor
-    per_call_write = sum(write[k][1] for k in parts) * 1024 * w_factor
-    summary = {
-        "workload": "c3_full_step (64 seqs x 8192 ctx, bs 32, 4 KV / 16 query heads, d 256, BF16)",
-        "source_hash": source_hash(DECODE_SOURCES),
-        "copy_calibration": {"kernel": copy_name, "bytes_each_way": calib,
-                             "fetch_size_kib": cf[copy_name][1], "write_size_kib": cw[copy_name][1],
-                             "fetch_scale": f_factor, "write_scale": w_factor},
-        "per_kernel_kib_per_dispatch": {
-            _short(k): {"FETCH_SIZE": fetch[k][1], "WRITE_SIZE": write.get(k, (0, 0.0))[1],
-                        "dispatches": fetch[k][0]} for k in parts},
-        "hbm_read_bytes_per_call": per_call_read,
-        "hbm_write_bytes_per_call": per_call_write,
-        "hbm_bytes_per_call": per_call_read + per_call_write,
-        "commands": {t: PROFILE_COMMANDS[t] for t in need},
-    }
-    with open(os.path.join(dst, "decode_c3_hbm_counters.json"), "w") as f:
-        json.dump(summary, f, indent=1)
-    lines = ["# HBM traffic of pa_decode, 64 seqs x 8192 ctx (bs 32, BF16)", "",
-             "Per dispatch, averaged over the profiled steps; FETCH_SIZE and WRITE_SIZE are "
-             "in KiB. Each counter ran in a pass of its own.", "",
-             "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB |", "|---|---|---|"]
-    for k in parts:
-        lines.append(f"| `{_short(k)}` | {fetch[k][1]:.1f} | {write.get(k, (0, 0.0))[1]:.1f} |")
-    lines += ["", f"Calibration: a plain 1 GiB device copy (`{_short(copy_name)}`, "
-                  f"`bench.py --copy-calib`) reads as FETCH_SIZE {cf[copy_name][1]:.1f} KiB and "
-                  f"WRITE_SIZE {cw[copy_name][1]:.1f} KiB, so fetch counts are scaled by "
-                  f"{f_factor:.4f} and write counts by {w_factor:.4f}.", "",
-              f"Traffic per pa_decode call: read {per_call_read / 1e9:.4f} GB, write "
-              f"{per_call_write / 1e9:.4f} GB, total {(per_call_read + per_call_write) / 1e9:.4f} GB "
-              f"(algorithmic bytes: 2.1491 GB).", "", "Commands:", ""]
-    lines += [f"    {PROFILE_COMMANDS[t]}" for t in need]
-    with open(os.path.join(dst, "decode_c3_hbm_counters.md"), "w") as f:
-        f.write("\n".join(lines) + "\n")
-    log("wrote decode_c3_hbm_counters.{json,md}")
+    cal = (copy_name, calib / (cf[copy_name][1] * 1024), calib / (cw[copy_name][1] * 1024),
+           cf[copy_name][1], cw[copy_name][1])
+    for key in COUNTER_RUNS:
+        _summarize_traffic(src, dst, key, cal)
 
 
 # ------------------------------------------------------------ components ---
@@ -826,6 +958,9 @@ def main():
                          "batching engine, or block copies and swaps")
     ap.add_argument("--kv", choices=["bf16", "fp8"], default="bf16",
                     help="KV cache element type (fp8: E4M3 codes with per-head scales)")
+    ap.add_argument("--graph-steps", type=int, default=20,
+                    help="also time this many steps replayed from one captured HIP graph "
+                         "(reported beside the eager line; 0 = skip)")
     ap.add_argument("--no-shared-prefix", action="store_true",
                     help="decode copy-on-write batches with plain pa_decode (every member "
                          "reads the shared prompt) instead of pa_decode_shared")

@@ -533,8 +533,11 @@ __device__ __forceinline__ void run_units(const DecodeArgs& a, PlanLds& pl, bool
     else unit(e.x, u % a.num_kv_heads, e.y, std::false_type{});
     __syncthreads();
   }
+  // (No fence before the count: each workgroup consumed the value its last
+  // ticket fetch returned before it got here, so that fetch has been
+  // performed. A device-scope fence would also write this XCD's L2 back,
+  // which cost the C2-shaped ragged layer about 10 %.)
   if (tid == 0) {
-    __threadfence();  // this workgroup's last ticket is taken before it counts itself out
     if (atomicAdd(&a.plan->done, 1) == (int)gridDim.x - 1) {
       atomicExch(&a.plan->ticket, 0);
       atomicExch(&a.plan->done, 0);
