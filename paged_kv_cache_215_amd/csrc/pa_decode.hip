@@ -1234,6 +1234,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeArgs a) {
 template <int D>
 __global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeArgs a) {
   constexpr int PER = D / kWave;  // 1, 2 or 4 floats per lane
+  constexpr int kBatch = 8;       // entries whose outputs are loaded together
   const int P = a.plan->part_tokens;
   if (a.plan->max_nparts <= 1 && a.num_groups == 0) return;
   const int full_total = a.plan->full_total;
@@ -1241,7 +1242,11 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeArgs a) {
   const int lane = threadIdx.x;
   for (int row = blockIdx.x; row < rows; row += gridDim.x) {
     const int seq = row / a.num_q_heads, h = row % a.num_q_heads;
+    // (the first slot is read whatever the partition count turns out to be,
+    // so that its load does not wait on the length's; it is used only for
+    // a sequence of several partitions, for which the plan wrote it)
     int n = a.context_lens[seq];
+    const int first_slot = a.full_pre[seq];
     n = n < 0 ? 0 : n;
     n = n > a.ctx_limit ? a.ctx_limit : n;
     const bool grouped = a.num_groups > 0 && seq >= a.cu_groups[0] &&
@@ -1252,7 +1257,7 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeArgs a) {
     const int npre = pos0 > 0 ? a.pre_splits : 0;  // shared-prefix splits
     if (npre == 0 && nparts <= 1) continue;  // written by the partition kernel
     const int total = npre + (nparts > 0 ? nparts : 1);
-    const int first = nparts > 1 ? a.full_pre[seq] : 0;
+    const int first = nparts > 1 ? first_slot : 0;
     // (m, l) and partial output of entry k: prefix splits, then tail partitions
     auto ml_of = [&](int k) -> const float* {
       if (k < npre) return a.pre_ml + 2 * (((int64_t)seq * a.num_q_heads + h) * npre + k);
@@ -1266,7 +1271,17 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeArgs a) {
       const int e = p < nparts - 1 ? first + p : full_total + seq;
       return a.part_o + ((int64_t)e * a.num_q_heads + h) * D;
     };
-    // lane k holds entry k's (m, l), 64 entries per pass
+    // The first kBatch entries' outputs go out together with the (m, l)
+    // loads (lane k: entry k), so that the row costs two dependent loads.
+    // An empty partial (l = 0) may leave its output unwritten: it enters by
+    // a select, never as a product with zero.
+    float ob[kBatch][PER];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const float* po = o_of(j < total ? j : 0) + lane * PER;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) ob[j][e] = po[e];
+    }
     float M = -INFINITY;
     for (int k = lane; k < total; k += kWave) {
       const float* ml = ml_of(k);
@@ -1287,17 +1302,21 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeArgs a) {
       }
       L += w_lane;
       const int cnt = total - k0 < kWave ? total - k0 : kWave;
-      // four entries per step, so that their loads are in flight together
-      for (int j0 = 0; j0 < cnt; j0 += 4) {
+      for (int j0 = 0; j0 < cnt; j0 += kBatch) {
+        if (k0 + j0 > 0) {  // later batches: their outputs, loaded together
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int j = j0 + jj;
-          const float w = __shfl(w_lane, j < cnt ? j : 0);
-          if (j < cnt && w > 0.f) {
-            const float* po = o_of(k0 + j) + lane * PER;
+          for (int j = 0; j < kBatch; ++j) {
+            const float* po = o_of(j0 + j < cnt ? k0 + j0 + j : k0) + lane * PER;
 #pragma unroll
-            for (int e = 0; e < PER; ++e) o[e] = __builtin_fmaf(w, po[e], o[e]);
+            for (int e = 0; e < PER; ++e) ob[j][e] = po[e];
           }
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const float w = __shfl(w_lane, j0 + j < cnt ? j0 + j : 0);
+          const bool use = j0 + j < cnt && w > 0.f;
+#pragma unroll
+          for (int e = 0; e < PER; ++e) o[e] = use ? __builtin_fmaf(w, ob[j][e], o[e]) : o[e];
         }
       }
     }
