@@ -147,3 +147,42 @@ def test_long_prefix_and_large_groups():
     assert cu.tolist() == [0, 3, 43] and pl.tolist() == [prefix_blocks * bs, 2 * bs]
     assert mg == 40
     _check(case, cu, pl, mg, mp)
+
+
+@pytest.mark.parametrize("kv_fp8", [False, True])
+def test_poisoned_workspace(kv_fp8):
+    # Past its 256-byte head a workspace may hold anything between calls;
+    # here every byte of it is 0xFF (a NaN in every float32 slot, -1 in every
+    # index) before the call. Each partial the merge reads must then have been
+    # written by this call, and the empty tails (a member whose context ends
+    # inside the shared prefix, one whose context is the prefix itself), whose
+    # output rows are never written, must not reach the merged rows.
+    bs = 16
+    lens = [20, 200, 150, 37, 90, 90, 300, 5, 3 * bs, 3 * bs + 70, 3 * bs + 400]
+    case = make_case(name="sh_poison", seed=83, context_lens=lens, num_q_heads=16,
+                     num_kv_heads=4, head_dim=256, block_size=bs, device=DEV, kv_fp8=kv_fp8)
+    _share(case, [(1, 3, 9), (4, 2, 5), (8, 3, 3)])
+    cu = np.array([1, 4, 6, 7, 8, 11], dtype=np.int32)
+    pl = np.array([150, 0, 70, 0, 3 * bs], dtype=np.int32)
+    S, Hq, d = case.queries[0].shape
+    ws = pa.decode_shared_workspace(S, Hq, case.num_kv_heads, d, bs, case.max_context_len,
+                                    len(pl), 3, 150, DEV)
+    ws[256:].fill_(0xFF)
+    kw = dict(k_scale=case.k_scales[0], v_scale=case.v_scales[0]) if kv_fp8 else {}
+    say(f"[shared] poisoned workspace, fp8={kv_fp8}: {ws.numel()} bytes")
+    got = pa.pa_decode_shared(case.queries[0], case.key_caches[0], case.value_caches[0],
+                              case.block_tables, case.context_lens,
+                              torch.as_tensor(cu, device=DEV), torch.as_tensor(pl, device=DEV),
+                              3, 150, case.scale, case.max_context_len, workspace=ws, **kw)
+    # the plain decode over a poisoned workspace of its own
+    wsp = pa.decode_workspace(S, Hq, case.num_kv_heads, d, bs, case.max_context_len, DEV)
+    wsp[256:].fill_(0xFF)
+    plain = (gpu_decode_fp8(case, workspace=wsp) if kv_fp8 else gpu_decode(case, workspace=wsp))
+    torch.cuda.synchronize()
+    ref = oracle_decode(case)
+    for name, t in (("shared", got), ("plain", plain)):
+        g = t.cpu().numpy()
+        assert np.all(np.isfinite(g)), name
+        err = max_abs_err(g, ref)
+        say(f"    {name}: max-abs err vs oracle {err:.3e}")
+        assert err <= ATOL, name
