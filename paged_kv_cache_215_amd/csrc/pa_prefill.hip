@@ -35,6 +35,10 @@
 #include <cstdlib>
 #include <type_traits>
 
+#ifndef PA_PF_DEEP
+#define PA_PF_DEEP 1
+#endif
+
 namespace pa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -98,9 +102,23 @@ struct PrefillShape {
   static constexpr int TPR = (NT / KT) < DCH ? (NT / KT) : DCH;
   static constexpr int KPT = DCH / TPR;
   static constexpr int VPT = (VJOBS + NT - 1) / NT;       // V jobs per thread
+  // Two register stages of staged tiles, for one head per wave at d <= 128
+  // and for 4-wave workgroups (at d = 256 the 8-wave shape ran slower with
+  // the second set: 248 VGPRs)
+  static constexpr bool kDeep = PA_PF_DEEP && HPW == 1 && (D <= 128 || NW == 4);
+  static constexpr bool kAllV = VJOBS % NT == 0;  // every thread has VPT jobs
 };
 
 constexpr int kPfMaxBlocks = 1024;  // table entries one context split may span
+
+// Workgroup barrier that orders LDS only: global loads in flight (the
+// prefetch of later tiles) stay in flight across it, where __syncthreads()
+// would wait for them.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // 8 E4M3 codes (an 8-byte cache chunk) as 8 bfloat16 (a 16-byte LDS chunk):
 // exact, every E4M3 value being a bfloat16 value.
@@ -248,9 +266,10 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
     return (int64_t)(e < 0 ? 0 : e) * block_stride + head_off + (int64_t)(k & (bs - 1)) * DCH;
   };
 
-  // Tile staging, split in two so that the next tile's global loads are in
-  // flight while the current tile's products run: load_regs issues them,
-  // store_lds writes them (K swizzled, V transposed) into the other buffer.
+  // Tile staging, split in two so that later tiles' global loads are in
+  // flight while the current tile's products run: load_into issues them into
+  // a register set, store_from writes a set (K swizzled, V transposed) into
+  // an LDS buffer.
   // K: thread t stages chunks (t % TPR) + TPR * i of key row t / TPR.
   // V: a job stages 4 consecutive keys (one block) x 8 dims.
   // (threads beyond the tile's rows, which only some shapes have, load a
@@ -261,9 +280,11 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
   const int k_row_c = k_active ? k_row : kKeyTile - 1;
   // (K staging uses native vectors: copied as plain structs, the registers
   // ended up in scratch memory)
-  u32x4_t kreg[S::KPT];
-  CC vreg[S::VPT][4];
-  auto load_regs = [&](int kt) {
+  using KRegs = u32x4_t[S::KPT];
+  using VRegs = CC[S::VPT][4];
+  KRegs kreg;
+  VRegs vreg;
+  auto load_into = [&](int kt, KRegs& kr, VRegs& vr) {
     const int key0 = kt * kKeyTile;
     {
       const CC* src = kcache + row_base(key0 + k_row_c) + k_c0;
@@ -271,41 +292,42 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
       for (int i = 0; i < S::KPT; ++i) {
         if constexpr (kFp8) {
           const u32x2_t c = *reinterpret_cast<const u32x2_t*>(src + S::TPR * i);
-          kreg[i] = u32x4_t{c.x, c.y, 0u, 0u};  // converted when stored
+          kr[i] = u32x4_t{c.x, c.y, 0u, 0u};  // converted when stored
         } else {
-          kreg[i] = *reinterpret_cast<const u32x4_t*>(src + S::TPR * i);
+          kr[i] = *reinterpret_cast<const u32x4_t*>(src + S::TPR * i);
         }
       }
     }
 #pragma unroll
     for (int j = 0; j < S::VPT; ++j) {
       const int job = tid + j * S::NT;
-      if (job < S::VJOBS) {
+      if (S::kAllV || job < S::VJOBS) {
         const int kg = job % (kKeyTile / 4), dg = job / (kKeyTile / 4);
         const CC* src = vcache + row_base(key0 + 4 * kg) + dg;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) vreg[j][r] = src[r * DCH];
+        for (int r = 0; r < 4; ++r) vr[j][r] = src[r * DCH];
       }
     }
-    if (key0 + kKeyTile > n) {  // tail tile: rows past the context may hold NaN
+  };
+  auto store_from = [&](int buf, int kt, KRegs& kr, VRegs& vr) {
+    const int key0 = kt * kKeyTile;
+    if (key0 + kKeyTile > n) {  // tail tile: V rows past the context may hold NaN
 #pragma unroll
       for (int j = 0; j < S::VPT; ++j) {
         const int job = tid + j * S::NT;
         const int kg = job % (kKeyTile / 4);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (key0 + 4 * kg + r >= n) zero_chunk(vreg[j][r]);
+          if (key0 + 4 * kg + r >= n) zero_chunk(vr[j][r]);
       }
     }
-  };
-  auto store_lds = [&](int buf) {
     // K: chunk c of row r lives at c ^ (r & SWZ), so the 16 rows one MFMA
     // operand read touches fall in distinct banks
     if (k_active) {
 #pragma unroll
       for (int i = 0; i < S::KPT; ++i) {
         const int c = k_c0 + S::TPR * i;
-        u32x4_t w = kreg[i];
+        u32x4_t w = kr[i];
         if constexpr (kFp8) w = fp8x8_to_bf16x8(make_uint2(w.x, w.y));
         *reinterpret_cast<u32x4_t*>(&k_lds[buf][k_row * DCH + (c ^ (k_row & S::SWZ))]) = w;
       }
@@ -314,17 +336,17 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int j = 0; j < S::VPT; ++j) {
       const int job = tid + j * S::NT;
-      if (job < S::VJOBS) {
+      if (S::kAllV || job < S::VJOBS) {
         const int kg = job % (kKeyTile / 4), dg = job / (kKeyTile / 4);
         const int slot = vt_slot(4 * kg);
         uint4 rows[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           if constexpr (kFp8) {
-            const u32x4_t w = fp8x8_to_bf16x8(vreg[j][r]);
+            const u32x4_t w = fp8x8_to_bf16x8(vr[j][r]);
             rows[r] = make_uint4(w.x, w.y, w.z, w.w);
           } else {
-            rows[r] = vreg[j][r];
+            rows[r] = vr[j][r];
           }
         }
         const uint32_t* w0 = &rows[0].x;
@@ -357,15 +379,11 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
     l_part[hh] = 0.f;
   }
 
-  if (kt_begin < kt_end) {
-    load_regs(kt_begin);
-    store_lds(0);
-  }
-  __syncthreads();
-  for (int kt = kt_begin; kt < kt_end; ++kt) {
+  // One key tile in LDS buffer buf: S^T products, then after_scores() (where
+  // the caller issues later tiles' loads), the masked online softmax and the
+  // PV products.
+  auto attend_tile = [&](int kt, int buf, auto&& after_scores) {
     const int key0 = kt * kKeyTile;
-    const int buf = (kt - kt_begin) & 1;
-    const bool has_next = kt + 1 < kt_end;
 
     // ---- S^T = K Q^T for keys key0..key0+KT-1 (16-key row blocks), per head
     f32x4_t sc[HPW][S::QB];
@@ -392,10 +410,10 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
     interleave_reads<S::KSTEPS * S::QB, HPW>();
 
     __builtin_amdgcn_s_setprio(0);
-    // The next tile's global loads go out once the score products have been
+    // Later tiles' global loads go out once the score products have been
     // issued: issued before them, the compiler made those products wait for
     // the loads.
-    if (has_next) load_regs(kt + 1);
+    after_scores();
 
     // last key this row may see; tiles that need the mask
     const int limit = a.prefix_mode ? member_limit : base_pos + my_row;
@@ -486,8 +504,54 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillArgs a) {
     }
     interleave_reads<S::DTILES * S::PSTEPS, 2 * HPW>();
     __builtin_amdgcn_s_setprio(0);
-    if (has_next) store_lds(buf ^ 1);
-    __syncthreads();  // next buffer complete; this one free for reuse
+  };
+
+  if constexpr (S::kDeep) {
+    // Two register stages, so that two tiles are in flight behind the one
+    // being attended: step i attends tile i, writes tile i + 1 (set c, loaded
+    // one step earlier) into the other buffer and loads tile i + 2 into set
+    // n; the sets swap roles every step. The per-step barrier orders LDS only
+    // (lds_barrier), so set n's loads stay in flight across it.
+    KRegs kreg2;
+    VRegs vreg2;
+    const int ntl = kt_end - kt_begin;
+    if (ntl > 0) {
+      load_into(kt_begin, kreg, vreg);
+      store_from(0, kt_begin, kreg, vreg);
+    }
+    if (ntl > 1) load_into(kt_begin + 1, kreg, vreg);
+    lds_barrier();
+    auto step = [&](int i, KRegs& kc, VRegs& vc, KRegs& kn, VRegs& vn) {
+      // (the last two steps load the split's last tile again into a set
+      // that is never stored: issued unconditionally, the loads keep the
+      // wait counts static, so waiting for set c never waits for set n)
+      attend_tile(kt_begin + i, i & 1, [&] {
+        load_into(kt_begin + min(i + 2, ntl - 1), kn, vn);
+      });
+      if (i + 1 < ntl) store_from((i & 1) ^ 1, kt_begin + i + 1, kc, vc);
+      lds_barrier();  // next buffer complete; this one free for reuse
+    };
+    int i = 0;
+    for (; i + 1 < ntl; i += 2) {
+      step(i, kreg, vreg, kreg2, vreg2);
+      step(i + 1, kreg2, vreg2, kreg, vreg);
+    }
+    if (i < ntl) step(i, kreg, vreg, kreg2, vreg2);
+  } else {
+    if (kt_begin < kt_end) {
+      load_into(kt_begin, kreg, vreg);
+      store_from(0, kt_begin, kreg, vreg);
+    }
+    __syncthreads();
+    for (int kt = kt_begin; kt < kt_end; ++kt) {
+      const int buf = (kt - kt_begin) & 1;
+      const bool has_next = kt + 1 < kt_end;
+      attend_tile(kt, buf, [&] {
+        if (has_next) load_into(kt + 1, kreg, vreg);
+      });
+      if (has_next) store_from(buf ^ 1, kt + 1, kreg, vreg);
+      __syncthreads();  // next buffer complete; this one free for reuse
+    }
   }
 
   // ---- row totals and output, per head
