@@ -35,10 +35,6 @@
 #include <cstdlib>
 #include <type_traits>
 
-#ifndef PA_PF_DEEP
-#define PA_PF_DEEP 1
-#endif
-
 namespace pa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -105,7 +101,7 @@ struct PrefillShape {
   // Two register stages of staged tiles, for one head per wave at d <= 128
   // and for 4-wave workgroups (at d = 256 the 8-wave shape ran slower with
   // the second set: 248 VGPRs)
-  static constexpr bool kDeep = PA_PF_DEEP && HPW == 1 && (D <= 128 || NW == 4);
+  static constexpr bool kDeep = HPW == 1 && (D <= 128 || NW == 4);
   static constexpr bool kAllV = VJOBS % NT == 0;  // every thread has VPT jobs
 };
 
