@@ -981,6 +981,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint4 s_region[kWaves][kTile * DCH];
   __shared__ float s_m[kWaves][G];
   __shared__ float s_l[kWaves][G];
+  __shared__ int s_prog[kWaves];  // tiles each wave has finished in this unit
 
   const int bs_log2 = a.block_size_log2;
   const int bs = 1 << bs_log2;
@@ -1047,6 +1048,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeArgs a) {
     const int e = a.block_tables[(int64_t)seq * a.max_blocks_per_seq + blk0 + i];
     s_bt[i] = (e >= 0 && (int64_t)e < a.num_blocks) ? e : -1;
   }
+  if (lane == 0) s_prog[wave] = 0;
   __syncthreads();
 
   const uint4* kcache = reinterpret_cast<const uint4*>(a.key_cache);
@@ -1186,11 +1188,21 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeArgs a) {
     load_k(tile_offset(t, blk));
     load_v(tile_offset(t, blk));
     for (; t + kWaves < ntiles; t += kWaves) {
+      if constexpr (kWaves == 8) {  // the priority rule of the VALU kernel
+        __builtin_amdgcn_sched_barrier(0);
+        const int done = (t - wave) / kWaves;
+        if (lane == 0) s_prog[wave] = done;
+        const int partner = __builtin_amdgcn_readfirstlane(s_prog[wave ^ 4]);
+        if (done > partner) __builtin_amdgcn_s_setprio(0);
+        else __builtin_amdgcn_s_setprio(1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       const int blk_next = tile_block(t + kWaves);
       process(t, blk, tile_offset(t + kWaves, blk_next), std::true_type{});
       blk = blk_next;
     }
     process(t, blk, 0, std::false_type{});
+    if constexpr (kWaves == 8) __builtin_amdgcn_s_setprio(0);
   }
 
   // ---- wave totals per head, into this wave's region (its V rows are done)
