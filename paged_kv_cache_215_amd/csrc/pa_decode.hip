@@ -355,11 +355,19 @@ __device__ void build_plan(const DecodeArgs& a, PlanLds& pl) {
         for (int p = a.part_floor; p <= a.part_cap; p *= 2)
           if ((long long)S * a.num_kv_heads * ((mx + p - 1) / p) >= a.plan_cus) P = p;
       } else if (mx > 0) {
+        // Ragged lengths: each CU's share of the tokens, rounded up to a
+        // multiple of 128 (whole 16-token tiles for every wave, whole
+        // blocks), within [part_floor, part_cap]. Rounded down to a power
+        // of two instead, a CU's share was one full partition plus scraps
+        // for the ticketed tails to fill: ragged 32-sequence layer 106.5 ->
+        // 101.7 us, over FP8 67.8 -> 62.7 us, mixed step 303.5 -> 298.4 us.
         const int units = shared ? a.plan_units_per_cu : a.plan_units_unshared;
         const long long budget =
             sum * a.num_kv_heads / ((long long)a.plan_cus * units);
-        for (int p = a.part_floor; p <= a.part_cap; p *= 2)
-          if (p <= budget) P = p;
+        long long p = (budget + 127) / 128 * 128;
+        p = p < a.part_floor ? a.part_floor : p;
+        p = p > a.part_cap ? a.part_cap : p;
+        P = (int)p;
       }
       pl.part_tokens = P;
       pl.ranked = mn != mx;  // equal lengths: equal last partitions, already in order
