@@ -105,18 +105,29 @@ def kernel_resources(lib_path=LIB):
             if "amdgcn" not in fn:
                 continue
             notes = _run([os.path.join(llvm, "llvm-readelf"), "--notes", os.path.join(tmp, fn)])
-            name = None
+            # Each kernel is one list item of amdhsa.kernels ("  - .field: ..."
+            # opens it); its fields are sorted by name, so some come before
+            # its .name and the item is stored when the next one opens.
+            fields, name = None, None
+            def flush():
+                if fields is not None and name:
+                    out[name] = dict(fields)
             for line in notes.splitlines():
-                m = re.match(r"\s+\.name:\s+(\S+)", line)
+                if re.match(r"  - \.", line):
+                    flush()
+                    fields, name = {}, None
+                if fields is None:
+                    continue
+                m = re.match(r"\s+(?:- )?\.name:\s+(\S+)", line)
                 if m:
                     name = m.group(1)
-                    out.setdefault(name, {})
                     continue
-                m = re.match(r"\s+\.(private_segment_fixed_size|vgpr_count|agpr_count|sgpr_count|"
-                             r"vgpr_spill_count|sgpr_spill_count|group_segment_fixed_size):\s+(\d+)",
-                             line)
-                if m and name:
-                    out[name][m.group(1)] = int(m.group(2))
+                m = re.match(r"\s+(?:- )?\.(private_segment_fixed_size|vgpr_count|agpr_count|"
+                             r"sgpr_count|vgpr_spill_count|sgpr_spill_count|"
+                             r"group_segment_fixed_size):\s+(\d+)", line)
+                if m:
+                    fields[m.group(1)] = int(m.group(2))
+            flush()
     return out
 
 
