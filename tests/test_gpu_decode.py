@@ -252,3 +252,25 @@ def test_very_long_contexts(kv_fp8):
     err = max_abs_err(out.cpu().numpy(), oracle_decode(case))
     say(f"[decode] contexts {lens} (fp8={kv_fp8}): max-abs err {err:.3e}")
     assert np.all(np.isfinite(out.cpu().numpy())) and err <= ATOL
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_ragged_partition_sizes_sweep(seed):
+    # Ragged batches whose per-CU share of the tokens lands on many different
+    # multiples of 128 (the plan's partition size for ragged lengths), with
+    # sequences shorter than, equal to and several times that size, at both
+    # block sizes and several head shapes: every sequence against the oracle.
+    rng = np.random.default_rng(1000 + seed)
+    num_seqs = int(rng.choice([12, 24, 40, 64]))
+    group = int(rng.choice([1, 2, 4, 8]))
+    num_kv = int(rng.choice([2, 4]))
+    head_dim = int(rng.choice([64, 128]))
+    block_size = int(rng.choice([16, 32]))
+    lens = rng.integers(1, 9000, size=num_seqs)
+    lens[: num_seqs // 4] = rng.integers(1, 300, size=num_seqs // 4)  # short ones too
+    case = make_case(name=f"plan_sweep_{seed}", seed=seed, context_lens=lens,
+                     num_q_heads=group * num_kv, num_kv_heads=num_kv, head_dim=head_dim,
+                     block_size=block_size, device=DEV)
+    share = int(lens.sum()) * num_kv / 256
+    _check(case, tag=f"S={num_seqs} G={group} Hkv={num_kv} d={head_dim} bs={block_size} "
+                     f"share~{share:.0f} tokens/CU")
