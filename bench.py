@@ -103,6 +103,9 @@ COUNTER_SETS = {
     ("c3_full_step", False): "decode_c3_hbm_counters",
     ("c3_full_step", True): "decode_fp8_c3_hbm_counters",
     ("c4_grpo_cow", False): "decode_c4_hbm_counters",
+    ("c2_layer_decode", False): "decode_c2_hbm_counters",
+    ("c2_layer_decode", True): "decode_fp8_c2_hbm_counters",
+    ("c5_mixed_step", False): "decode_c5_hbm_counters",
 }
 
 
@@ -581,11 +584,30 @@ COUNTER_RUNS = {
                              "tails U[0, 1024], bs 16, BF16, pa_decode_shared",
                              ("prefill_kernel", "decode_partition_kernel", "decode_mfma_kernel",
                               "decode_merge_kernel")),
+    ("c2_layer_decode", False): ("--workload c2_layer_decode --steps 2 --warmup 1 --cold-calls 0",
+                                 "32 seqs, contexts U[512, 8192], bs 16, 4 KV / 16 query heads, "
+                                 "d 256, BF16",
+                                 ("decode_partition_kernel", "decode_mfma_kernel",
+                                  "decode_merge_kernel")),
+    ("c2_layer_decode", True): ("--workload c2_layer_decode --kv fp8 --steps 2 --warmup 1 "
+                                "--cold-calls 0",
+                                "32 seqs, contexts U[512, 8192], bs 16, 4 KV / 16 query heads, "
+                                "d 256, FP8 E4M3",
+                                ("decode_partition_kernel", "decode_mfma_kernel",
+                                 "decode_merge_kernel")),
+    ("c5_mixed_step", False): ("--workload c5_mixed_step --steps 2 --warmup 1 --cold-calls 0",
+                               "the mixed step's decode of 255 seqs (prefill chunk not "
+                               "counted), bs 16, BF16",
+                               ("decode_partition_kernel", "decode_mfma_kernel",
+                                "decode_merge_kernel")),
 }
+
+_COUNTER_STEMS = {"c2_layer_decode": "c2", "c3_full_step": "c3", "c4_grpo_cow": "c4",
+                  "c5_mixed_step": "c5"}
 
 
 def _counter_tags(key):
-    stem = "c3" if key[0] == "c3_full_step" else "c4"
+    stem = _COUNTER_STEMS[key[0]]
     return (f"pmc_fetch_{stem}{'_fp8' if key[1] else ''}",
             f"pmc_write_{stem}{'_fp8' if key[1] else ''}")
 
