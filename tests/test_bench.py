@@ -2,6 +2,7 @@
 roofline divides by, the one-GPU guard, and the source hash that ties the
 committed HBM counters to the kernel they were taken on."""
 
+import json
 import os
 import subprocess
 import sys
@@ -99,3 +100,17 @@ def test_prefill_counter_summary(tmp_path):
     assert "16.0 busy cycles per matrix instruction" in text
     assert "Waves waiting: 30.0 %" in text and "VALU issue: 20.0 %" in text
     assert f"Kernel length: {cycles:,} cycles" in text
+
+
+def test_committed_counter_summaries_are_consistent():
+    # every HBM counter summary under profiles/ was taken with a command the
+    # bench still defines, on the workload whose algorithmic bytes the bench
+    # computes today, and reads no more than a quarter above them
+    for key, stem in bench.COUNTER_SETS.items():
+        with open(os.path.join(ROOT, "profiles", stem + ".json")) as f:
+            c = json.load(f)
+        assert c["algorithmic_bytes_per_call"] == bench._algorithmic_decode_bytes(*key), stem
+        for tag, cmd in c["commands"].items():
+            assert bench.PROFILE_COMMANDS[tag] == cmd, (stem, tag)
+        ratio = c["hbm_bytes_per_call"] / c["algorithmic_bytes_per_call"]
+        assert 0.95 <= ratio <= 1.25, (stem, ratio)
