@@ -301,3 +301,21 @@ def test_prefill_fp8_matches_bf16_prefill_on_dequantized_cache():
     diff = float((out8 - out16).abs().max())
     say(f"[fp8 prefill] fp8 vs bf16 chunk kernel: max diff {diff:.3e}")
     assert diff <= 1e-5
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_prefill_random_shapes_sweep(seed):
+    # seeded draws as in the BF16 prefill sweep, over an E4M3 cache
+    rng = np.random.default_rng(3000 + seed)
+    group = int(rng.choice([1, 2, 4, 8]))
+    head_dim = int(rng.choice([64, 128, 256]))
+    block_size = int(rng.choice([16, 32]))
+    n = int(rng.integers(1, 5))
+    chunks = [(int(rng.choice([0, rng.integers(1, 601)])), int(rng.choice([1, rng.integers(2, 201)])))
+              for _ in range(n)]
+    hkv = int(rng.choice([1, 2, 4]))
+    case = make_case(name=f"pf8_sweep{seed}", seed=4000 + seed, context_lens=[],
+                     num_q_heads=group * hkv, num_kv_heads=hkv, head_dim=head_dim,
+                     block_size=block_size, device=DEV, kv_fp8=True, prefill_chunks=chunks)
+    say(f"[fp8 prefill sweep] G {group} Hkv {hkv} d {head_dim} bs {block_size} chunks {chunks}")
+    _prefill_check(case)

@@ -147,3 +147,23 @@ def test_scale_sign_and_zero(scale, group, head_dim):
                      device=DEV, prefill_chunks=[(90, 70)])
     case.scale = scale
     _full_check(case, tag=f"scale {scale}")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_shapes_sweep(seed):
+    # seeded draws of group, head size, block size and one to four chunks with
+    # prefixes in [0, 600] and lengths in [1, 200] (prefix 0 and length 1
+    # included), block tables a random permutation of the pool; every row of
+    # every chunk against the oracle
+    rng = np.random.default_rng(1000 + seed)
+    group = int(rng.choice([1, 2, 4, 8]))
+    head_dim = int(rng.choice([64, 128, 256]))
+    block_size = int(rng.choice([16, 32]))
+    n = int(rng.integers(1, 5))
+    chunks = [(int(rng.choice([0, rng.integers(1, 601)])), int(rng.choice([1, rng.integers(2, 201)])))
+              for _ in range(n)]
+    hkv = int(rng.choice([1, 2, 4]))
+    case = make_case(name=f"pf_sweep{seed}", seed=2000 + seed, context_lens=[],
+                     num_q_heads=group * hkv, num_kv_heads=hkv, head_dim=head_dim,
+                     block_size=block_size, device=DEV, prefill_chunks=chunks)
+    _full_check(case, tag=f"G {group} Hkv {hkv} d {head_dim} bs {block_size} chunks {chunks}")
