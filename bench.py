@@ -106,6 +106,8 @@ COUNTER_SETS = {
     ("c2_layer_decode", False): "decode_c2_hbm_counters",
     ("c2_layer_decode", True): "decode_fp8_c2_hbm_counters",
     ("c5_mixed_step", False): "decode_c5_hbm_counters",
+    ("c5_mixed_step", True): "decode_fp8_c5_hbm_counters",
+    ("c4_grpo_cow", True): "decode_fp8_c4_hbm_counters",
 }
 
 
@@ -600,6 +602,17 @@ COUNTER_RUNS = {
                                "counted), bs 16, BF16",
                                ("decode_partition_kernel", "decode_mfma_kernel",
                                 "decode_merge_kernel")),
+    ("c5_mixed_step", True): ("--workload c5_mixed_step --kv fp8 --steps 2 --warmup 1 "
+                              "--cold-calls 0",
+                              "the mixed step's decode of 255 seqs (prefill chunk not "
+                              "counted), bs 16, FP8 E4M3",
+                              ("decode_partition_kernel", "decode_mfma_kernel",
+                               "decode_merge_kernel")),
+    ("c4_grpo_cow", True): ("--workload c4_grpo_cow --kv fp8 --steps 2 --warmup 1 --cold-calls 0",
+                            "copy-on-write batch, 8 x 16 rollouts of a 4096-token prompt, "
+                            "tails U[0, 1024], bs 16, FP8 E4M3, pa_decode_shared",
+                            ("prefill_kernel", "decode_partition_kernel", "decode_mfma_kernel",
+                             "decode_merge_kernel")),
 }
 
 _COUNTER_STEMS = {"c2_layer_decode": "c2", "c3_full_step": "c3", "c4_grpo_cow": "c4",
