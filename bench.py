@@ -21,6 +21,7 @@ same workload (one layer's sequences), in worker processes on the host cores.
 """
 
 import argparse
+import gc
 import hashlib
 import json
 import math
@@ -268,12 +269,17 @@ def run(args):
             len(pf.q_lens), pf.query.shape[0], pf.max_q_len, case.num_q_heads, case.num_kv_heads,
             case.head_dim, case.block_size, pf_ctx)), dtype=torch.uint8, device=dev)
 
+    # Event pairs for the timed calls are created before the timed region, so
+    # that no allocation (and no garbage collection it might start) falls
+    # inside it.
+    spare_events = []
+
     def timed(events, fn):
         if events is None:
             fn()
             return
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
+        e0, e1 = (spare_events.pop() if spare_events else
+                  (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
         e0.record(stream)
         fn()
         e1.record(stream)
@@ -346,11 +352,19 @@ def run(args):
         step()
     torch.cuda.synchronize()
     dec_events, pf_events = [], []
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(dec_events, pf_events)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    calls = args.steps * L * (2 if pf is not None else 1)
+    spare_events.extend((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                        for _ in range(calls))
+    gc.collect()
+    gc.disable()  # (the interpreter's collector stays out of the timed region)
+    try:
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step(dec_events, pf_events)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    finally:
+        gc.enable()
     decode_ms = [a.elapsed_time(b) for a, b in dec_events]
     avg_decode_s = float(np.mean(decode_ms)) / 1e3
 
